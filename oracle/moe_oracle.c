@@ -1,0 +1,347 @@
+/*
+ * moe_oracle.c -- plain, slow, single-threaded fp64 CPU oracle for the forward
+ * pass of one sparse Mixture-of-Experts FFN layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this library.  The GPU product
+ * path never links, loads or falls back to it, and this file shares no code,
+ * header, table or constant generator with the HIP kernels.
+ *
+ * Sources (the five web pages that define the method; cited by page and section):
+ *   P1  "这不是参数堆砌，而是动态稀疏激活的工程革命"
+ *       devpress.csdn.net/awstech/6a46250010ee7a33f285d330
+ *   P2  "项目概述：参数规模与稀疏激活的真相拆解"
+ *       devpress.csdn.net/awstech/6a919c0d2b83d06f0ec6f601
+ *   P3  "项目概述：参数规模与稀疏激活的真相拆解" (second article, same heading)
+ *       devpress.csdn.net/awstech/6a46202710ee7a33f285c5a4
+ *   P4  hotelren.com/news/2927663 (MoE gating article under an unrelated headline)
+ *   P5  "这句话到底在说什么？" aicoding.csdn.net/6a320eef10ee7a33f27e52b3
+ *
+ * What is computed, per token t (all arithmetic in IEEE binary64):
+ *   1. logits  l[e] = sum_i x[t,i] * Wg[i,e]  (+ b[e])        P2 §2.2 steps 1-2; P5 §3.2 "处理"
+ *      Wg is d x E row-major (P5 §3.2 gives W_router as a d x 128 matrix).
+ *      The sum runs over ascending i.  bf16 and fp32 inputs widen exactly and
+ *      their pairwise products are exact in binary64.
+ *   2. noise   g[e] = -ln(-ln u),  u in (0,1) from Philox4x64-10   P1 §3.1 steps 2-3
+ *      (counter-based generator of Salmon et al., SC'11, keyed on
+ *      (seed, token, expert); g = 0 when noise is off)
+ *   3. z[e] = (l[e] + g[e]) / tau                                   P1 §3.1 step 3
+ *   4. ids  = the k experts with the largest z, ordered by z descending;
+ *      exact ties go to the lower expert index; NaN ranks below every number.
+ *      Selecting on z equals selecting on softmax(z) (softmax is monotone). P1 §3.1 step 4; P2 §2.2 step 3
+ *   5. p = softmax(z) over all E, max-subtracted; gate[j] = p[ids[j]] (not
+ *      renormalised over the k chosen).                              P2 §2.2 step 4; P5 §3.1 worked example
+ *   6. expert FFN  o = W2_e * GeLU(W1_e * x),  GeLU(h) = h * Phi(h)
+ *                  = 0.5 h (1 + erf(h / sqrt 2)), no bias.           P3 §3.2 (d -> 4d -> d MLP, GELU)
+ *      W1_e is d_ff x d, W2_e is d x d_ff (out x in, input dim contiguous).
+ *      INT4 experts: w[n,c] = q[n,c] * s[n, c/128] exactly, q in [-8,7]
+ *      (symmetric group-128 codes with bf16 scales).                 P1 §5.4; P2 §2.3 (dequantize step)
+ *   7. y[t] = sum_j p[ids[j]] * o_{ids[j]}                           P2 §2.2 step 4; P5 §3.2 "合并"
+ * Dispatch bookkeeping (per-expert counts, exclusive offsets, a stable
+ * counting sort of the (token, slot) assignments) follows P3 §4.2's per-expert
+ * load vector and its note that tokens are scattered to experts.
+ *
+ * Nothing is blocked, fused or reordered beyond the definitions above.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+#define ORACLE_INT4_G128 2
+
+/* ---------------------------------------------------------------- decoding */
+
+static double bf16_to_double(uint16_t bits)
+{
+    uint32_t w = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
+/* Element idx of an activation-typed array (x, Wg). */
+static double load_act(const void *base, int32_t dtype, int64_t idx)
+{
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)base)[idx];
+    return bf16_to_double(((const uint16_t *)base)[idx]);
+}
+
+/* One signed 4-bit code: two's complement nibble, even column in the low nibble. */
+static int int4_code(const uint8_t *codes, int64_t K, int64_t n, int64_t c)
+{
+    uint8_t byte = codes[n * (K / 2) + c / 2];
+    int nib = (c % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+    return nib >= 8 ? nib - 16 : nib;
+}
+
+/* Weight element [n][c] of one expert's N x K matrix. */
+static double load_w(const void *w, const void *scales, int32_t dtype, int64_t K, int64_t n, int64_t c)
+{
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)w)[n * K + c];
+    if (dtype == ORACLE_BF16)
+        return bf16_to_double(((const uint16_t *)w)[n * K + c]);
+    {
+        int q = int4_code((const uint8_t *)w, K, n, c);
+        double s = bf16_to_double(((const uint16_t *)scales)[n * (K / 128) + c / 128]);
+        return (double)q * s;
+    }
+}
+
+/* ------------------------------------------------------ Philox4x64-10 (SC'11) */
+
+/* One Philox4x64 block with 10 rounds.  Round function: two 64x64->128
+ * multiplies of words 0 and 2, outputs (hi1^x1^k0, lo1, hi0^x3^k1, lo0); the
+ * key is bumped by the two Weyl constants between rounds. */
+void oracle_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4])
+{
+    const uint64_t M0 = 0xD2E7470EE14C6C93ULL, M1 = 0xCA5A826395121157ULL;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ULL, W1 = 0xBB67AE8584CAA73BULL;
+    uint64_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+    uint64_t k0 = key[0], k1 = key[1];
+    for (int r = 0; r < 10; ++r) {
+        unsigned __int128 p0 = (unsigned __int128)M0 * x0;
+        unsigned __int128 p1 = (unsigned __int128)M1 * x2;
+        uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+        uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+        uint64_t y0 = hi1 ^ x1 ^ k0, y1 = lo1, y2 = hi0 ^ x3 ^ k1, y3 = lo0;
+        x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+        k0 += W0;
+        k1 += W1;
+    }
+    out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+}
+
+/* Uniform u strictly inside (0,1) for (seed, token, expert): the top 53 bits of
+ * the block's first word, offset by half an ulp. */
+double oracle_uniform(uint64_t seed, uint64_t token, uint64_t expert)
+{
+    uint64_t ctr[4] = {token, expert, 0, 0}, key[2] = {seed, 0}, r[4];
+    oracle_philox4x64_10(ctr, key, r);
+    return ((double)(r[0] >> 11) + 0.5) * (1.0 / 9007199254740992.0); /* 2^-53 */
+}
+
+/* Standard Gumbel draw g = -ln(-ln u)   (P1 §3.1 step 2). */
+double oracle_gumbel(uint64_t seed, uint64_t token, uint64_t expert)
+{
+    double u = oracle_uniform(seed, token, expert);
+    return -log(-log(u));
+}
+
+/* GeLU in its exact form h * Phi(h). */
+double oracle_gelu(double h)
+{
+    return 0.5 * h * (1.0 + erf(h / sqrt(2.0)));
+}
+
+/* ------------------------------------------------------------------ routing */
+
+/* Is expert a ranked before expert b?  Larger z first, NaN last, ties to the
+ * lower index. */
+static int ranks_before(const double *z, int32_t a, int32_t b)
+{
+    int na = isnan(z[a]), nb = isnan(z[b]);
+    if (na != nb)
+        return nb; /* the non-NaN one wins */
+    if (!na && z[a] != z[b])
+        return z[a] > z[b];
+    return a < b;
+}
+
+/*
+ * Router for all T tokens.  Writes ids[T][k] (best first), gates[T][k] =
+ * (float) p[ids], and optionally gate_p[T][k] (the same probabilities in
+ * binary64), z_out[T][E] and p_out[T][E].  bias may be NULL.
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_route(int64_t T, int64_t d, int32_t E, int32_t k, int32_t act_dtype,
+                 const void *x, const void *Wg, const float *bias,
+                 double tau, int32_t use_gumbel, uint64_t seed, uint64_t token_offset,
+                 int32_t *ids, float *gates, double *gate_p, double *z_out, double *p_out)
+{
+    if (T < 0 || d < 1 || E < 1 || k < 1 || k > E || !(tau > 0.0))
+        return -1;
+    if (act_dtype != ORACLE_F32 && act_dtype != ORACLE_BF16)
+        return -1;
+    double *l = (double *)malloc(sizeof(double) * (size_t)E);
+    double *z = (double *)malloc(sizeof(double) * (size_t)E);
+    double *p = (double *)malloc(sizeof(double) * (size_t)E);
+    int32_t *taken = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    if (!l || !z || !p || !taken) {
+        free(l); free(z); free(p); free(taken);
+        return -1;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        /* 1. logits: each l[e] accumulates over ascending i. */
+        for (int32_t e = 0; e < E; ++e)
+            l[e] = 0.0;
+        for (int64_t i = 0; i < d; ++i) {
+            double xi = load_act(x, act_dtype, t * d + i);
+            for (int32_t e = 0; e < E; ++e)
+                l[e] += xi * load_act(Wg, act_dtype, i * (int64_t)E + e);
+        }
+        if (bias)
+            for (int32_t e = 0; e < E; ++e)
+                l[e] += (double)bias[e];
+        /* 2-3. noise and temperature. */
+        for (int32_t e = 0; e < E; ++e) {
+            double g = use_gumbel ? oracle_gumbel(seed, token_offset + (uint64_t)t, (uint64_t)e) : 0.0;
+            z[e] = (l[e] + g) / tau;
+        }
+        /* 5. softmax over all experts. */
+        double m = z[0];
+        for (int32_t e = 1; e < E; ++e)
+            if (z[e] > m)
+                m = z[e];
+        double s = 0.0;
+        for (int32_t e = 0; e < E; ++e) {
+            p[e] = exp(z[e] - m);
+            s += p[e];
+        }
+        for (int32_t e = 0; e < E; ++e)
+            p[e] /= s;
+        /* 4. top-k by repeated selection of the best expert not yet taken. */
+        for (int32_t e = 0; e < E; ++e)
+            taken[e] = 0;
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t best = -1;
+            for (int32_t e = 0; e < E; ++e)
+                if (!taken[e] && (best < 0 || ranks_before(z, e, best)))
+                    best = e;
+            taken[best] = 1;
+            ids[t * k + j] = best;
+            gates[t * k + j] = (float)p[best];
+            if (gate_p)
+                gate_p[t * k + j] = p[best];
+        }
+        if (z_out)
+            memcpy(z_out + t * E, z, sizeof(double) * (size_t)E);
+        if (p_out)
+            memcpy(p_out + t * E, p, sizeof(double) * (size_t)E);
+    }
+    free(l); free(z); free(p); free(taken);
+    return 0;
+}
+
+/* ----------------------------------------------------------------- dispatch */
+
+/*
+ * Per-expert counts, exclusive offsets[E+1], and the stable counting sort of
+ * the T*k assignments taken in row-major (token, slot) order:
+ *   sorted_token[offsets[e] + r] = token of the r-th assignment to e,
+ *   pos[t*k + j] = the position of assignment (t, j) in that order.
+ * Returns 0, or -1 if an id is out of range.
+ */
+int oracle_permute(int64_t T, int32_t E, int32_t k, const int32_t *ids,
+                   int32_t *counts, int32_t *offsets, int32_t *sorted_token, int32_t *pos)
+{
+    for (int32_t e = 0; e < E; ++e)
+        counts[e] = 0;
+    for (int64_t a = 0; a < T * k; ++a) {
+        if (ids[a] < 0 || ids[a] >= E)
+            return -1;
+        counts[ids[a]] += 1;
+    }
+    offsets[0] = 0;
+    for (int32_t e = 0; e < E; ++e)
+        offsets[e + 1] = offsets[e] + counts[e];
+    int32_t *fill = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    if (!fill)
+        return -1;
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t e = ids[t * k + j];
+            int32_t slot = offsets[e] + fill[e];
+            fill[e] += 1;
+            sorted_token[slot] = (int32_t)t;
+            pos[t * k + j] = slot;
+        }
+    free(fill);
+    return 0;
+}
+
+/* --------------------------------------------------------------- expert FFN */
+
+/*
+ * o[0..d) = W2_e * GeLU(W1_e * xr) for one token row xr (binary64, length d).
+ * W1e is d_ff x d, W2e is d x d_ff, both in w_dtype; S1e/S2e are the bf16 group
+ * scales for INT4 (ignored otherwise).  Returns 0, or -1 on a bad argument.
+ */
+int oracle_expert_ffn(int64_t d, int64_t d_ff, int32_t w_dtype,
+                      const double *xr, const void *W1e, const void *S1e,
+                      const void *W2e, const void *S2e, double *o)
+{
+    if (w_dtype == ORACLE_INT4_G128 && (d % 128 != 0 || d_ff % 128 != 0 || !S1e || !S2e))
+        return -1;
+    double *a = (double *)malloc(sizeof(double) * (size_t)d_ff);
+    if (!a)
+        return -1;
+    for (int64_t n = 0; n < d_ff; ++n) {
+        double h = 0.0;
+        for (int64_t i = 0; i < d; ++i)
+            h += load_w(W1e, S1e, w_dtype, d, n, i) * xr[i];
+        a[n] = oracle_gelu(h);
+    }
+    for (int64_t c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int64_t n = 0; n < d_ff; ++n)
+            acc += load_w(W2e, S2e, w_dtype, d_ff, c, n) * a[n];
+        o[c] = acc;
+    }
+    free(a);
+    return 0;
+}
+
+/*
+ * Layer output for the listed tokens: y[r][c] = sum_j gate_p[t][j] * o_j[c],
+ * t = tokens[r], o_j the FFN of expert ids[t][j].  W1/S1/W2/S2 are arrays of E
+ * per-expert pointers (an expert no listed token routes to may be NULL).
+ * Returns 0, or -1 on a bad argument or a missing expert.
+ */
+int oracle_forward_tokens(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k,
+                          int32_t act_dtype, int32_t w_dtype, const void *x,
+                          const int32_t *ids, const double *gate_p,
+                          const void *const *W1, const void *const *S1,
+                          const void *const *W2, const void *const *S2,
+                          int64_t ntok, const int64_t *tokens, double *y)
+{
+    double *xr = (double *)malloc(sizeof(double) * (size_t)d);
+    double *o = (double *)malloc(sizeof(double) * (size_t)d);
+    if (!xr || !o) {
+        free(xr); free(o);
+        return -1;
+    }
+    int rc = 0;
+    for (int64_t r = 0; r < ntok && rc == 0; ++r) {
+        int64_t t = tokens[r];
+        if (t < 0 || t >= T) {
+            rc = -1;
+            break;
+        }
+        for (int64_t i = 0; i < d; ++i)
+            xr[i] = load_act(x, act_dtype, t * d + i);
+        for (int64_t c = 0; c < d; ++c)
+            y[r * d + c] = 0.0;
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t e = ids[t * k + j];
+            if (e < 0 || e >= E || !W1[e] || !W2[e]) {
+                rc = -1;
+                break;
+            }
+            rc = oracle_expert_ffn(d, d_ff, w_dtype, xr, W1[e], S1 ? S1[e] : NULL,
+                                   W2[e], S2 ? S2[e] : NULL, o);
+            if (rc != 0)
+                break;
+            double w = gate_p[t * k + j];
+            for (int64_t c = 0; c < d; ++c)
+                y[r * d + c] += w * o[c];
+        }
+    }
+    free(xr);
+    free(o);
+    return rc;
+}

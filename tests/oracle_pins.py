@@ -1,0 +1,451 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each pin takes an `Oracle` instance and raises AssertionError when the oracle
+disagrees with what the pages or the mathematics fix: library routines
+(numpy's Philox bit generator, numpy matmul, scipy's normal CDF and softmax,
+numpy's stable sort), closed forms, brute force over all expert subsets, the
+Gumbel-max theorem, and the router example printed on page P5 §3.1.  The
+mutation test runs the same pins against deliberately broken copies of the
+oracle and requires every copy to fail at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+from scipy import stats
+
+from oracle.oracle import BF16, F32, INT4_G128
+from tests import npref
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _bf16(a):
+    return npref.f64_to_bf16_bits(a)
+
+
+def _tiny(seed, T=12, d=16, d_ff=32, E=6, dtype=F32):
+    """A tiny random layer in float32 or bf16 bits, plus float64 views."""
+    r = _rng(seed)
+    x = r.standard_normal((T, d))
+    Wg = r.standard_normal((d, E)) / math.sqrt(d)
+    W1 = r.standard_normal((E, d_ff, d)) / math.sqrt(d)
+    W2 = r.standard_normal((E, d, d_ff)) / math.sqrt(d_ff)
+    if dtype == F32:
+        raw = [a.astype(np.float32) for a in (x, Wg, W1, W2)]
+        f64 = [a.astype(np.float64) for a in raw]
+    else:
+        raw = [_bf16(a) for a in (x, Wg, W1, W2)]
+        f64 = [npref.bf16_bits_to_f64(a) for a in raw]
+    return raw, f64
+
+
+# ------------------------------------------------------------------ generator
+
+def pin_philox_matches_numpy(orc):
+    """Philox4x64-10 blocks equal numpy's Philox bit generator.  numpy advances
+    its 256-bit counter by one before producing a block, so counter c-1 yields
+    the block of counter c."""
+    mask = (1 << 64) - 1
+    cases = [((0, 0, 0, 0), (0, 0)), ((1, 2, 3, 4), (5, 6)), ((0, 1, 0, 0), (mask, 7)),
+             ((mask, 0, 0, 0), (123456789, 987654321)), ((17, 4, 0, 0), (0, 0)),
+             ((2**40 + 3, 255, 0, 0), (2**63 + 11, 0))]
+    for ctr, key in cases:
+        c = list(ctr)
+        # subtract one with borrow
+        i = 0
+        while True:
+            if c[i] == 0:
+                c[i] = mask
+                i += 1
+                if i == 4:
+                    break
+            else:
+                c[i] -= 1
+                break
+        bg = np.random.Philox(counter=np.array(c, dtype=np.uint64), key=np.array(key, dtype=np.uint64))
+        want = bg.random_raw(4)
+        got = orc.philox(ctr, key)
+        assert np.array_equal(got, want), (ctr, key, got, want)
+
+
+def pin_philox_known_answer(orc):
+    """The published Philox4x64-10 known-answer vectors (tests/golden/philox4x64_10_kat.txt)."""
+    with open(os.path.join(GOLDEN, "philox4x64_10_kat.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            v = [int(w, 16) for w in line.split()]
+            got = orc.philox(v[0:4], v[4:6])
+            assert [int(a) for a in got] == v[6:10], (line, [hex(int(a)) for a in got])
+
+
+def pin_uniform_and_gumbel_distribution(orc):
+    """u lies strictly inside (0,1) and is uniform; g = -ln(-ln u) follows the
+    standard Gumbel law (Kolmogorov-Smirnov against scipy's CDFs)."""
+    us = np.array([orc.uniform(3, t, e) for t in range(400) for e in range(10)])
+    assert np.all(us > 0.0) and np.all(us < 1.0)
+    assert stats.kstest(us, "uniform").pvalue > 1e-4
+    gs = np.array([orc.gumbel(3, t, e) for t in range(400) for e in range(10)])
+    assert np.all(np.isfinite(gs))
+    assert stats.kstest(gs, stats.gumbel_r.cdf).pvalue > 1e-4
+    # distinct (token, expert) keys give distinct draws; the seed matters
+    assert len(np.unique(gs)) == len(gs)
+    assert orc.gumbel(4, 0, 0) != orc.gumbel(3, 0, 0)
+    assert orc.gumbel(3, 1, 0) != orc.gumbel(3, 0, 1)
+
+
+def pin_uniform_stream_layout(orc):
+    """The noise stream's layout (a reading: the pages only ask for a draw per
+    (seed, token, expert)): u for (seed, t, e) takes the top 53 bits of word 0
+    of the Philox4x64-10 block with key (seed, 0) and counter (t, e, 0, 0),
+    read here from numpy's Philox bit generator, plus half an ulp."""
+    for seed, t, e in ((0, 0, 0), (7, 3, 1), (2**40 + 1, 12345, 127), (5, 2**33, 255)):
+        ctr = [t, e, 0, 0]
+        c = list(ctr)
+        i = 0
+        while i < 4 and c[i] == 0:  # counter minus one (numpy pre-increments)
+            c[i] = (1 << 64) - 1
+            i += 1
+        if i < 4:
+            c[i] -= 1
+        r0 = int(np.random.Philox(counter=np.array(c, dtype=np.uint64),
+                                  key=np.array([seed, 0], dtype=np.uint64)).random_raw(1)[0])
+        assert orc.uniform(seed, t, e) == ((r0 >> 11) + 0.5) / 2.0**53
+        assert orc.gumbel(seed, t, e) == -math.log(-math.log(((r0 >> 11) + 0.5) / 2.0**53))
+
+
+# ----------------------------------------------------------------------- GeLU
+
+def pin_gelu(orc):
+    """GeLU(h) = h * Phi(h): table value Phi(1) = 0.8413447460685429, zero at
+    zero, odd-part identity GeLU(h) - GeLU(-h) = h, scipy's normal CDF."""
+    assert orc.gelu(0.0) == 0.0
+    assert abs(orc.gelu(1.0) - 0.8413447460685429) < 1e-15
+    for h in np.linspace(-6, 6, 97):
+        want = npref.gelu_cdf(h)
+        assert abs(orc.gelu(h) - want) <= 1e-14 * max(1.0, abs(want)), h
+        assert abs(orc.gelu(h) - orc.gelu(-h) - h) <= 1e-14 * max(1.0, abs(h)), h
+    assert orc.gelu(40.0) == 40.0
+    assert abs(orc.gelu(-40.0)) < 1e-300
+
+
+# -------------------------------------------------------------------- routing
+
+def pin_logits_closed_forms(orc):
+    """One-hot tokens select rows of Wg exactly; small-integer tokens and gates
+    give exact integer logits (numpy int64 matmul)."""
+    r = _rng(1)
+    d, E = 24, 7
+    Wg = r.standard_normal((d, E)).astype(np.float32)
+    x = np.zeros((d, d), dtype=np.float32)
+    np.fill_diagonal(x, 1.0)
+    out = orc.route(x, Wg, 2, F32, want_zp=True)
+    assert np.array_equal(out["z"], Wg.astype(np.float64))
+    xi = r.integers(-9, 10, size=(10, d))
+    Wi = r.integers(-9, 10, size=(d, E))
+    out = orc.route(xi.astype(np.float32), Wi.astype(np.float32), 2, F32, want_zp=True)
+    assert np.array_equal(out["z"], (xi @ Wi).astype(np.float64))
+    # the same through bf16 storage (small integers are exact in bf16)
+    out = orc.route(_bf16(xi), _bf16(Wi), 2, BF16, want_zp=True)
+    assert np.array_equal(out["z"], (xi @ Wi).astype(np.float64))
+
+
+def pin_logits_library(orc):
+    """bf16 and fp32 logits agree with numpy float64 matmul to rounding."""
+    for dtype in (F32, BF16):
+        (x, Wg, _, _), (xf, Wgf, _, _) = _tiny(2, T=20, d=64, E=9, dtype=dtype)
+        bias = _rng(3).standard_normal(9).astype(np.float32)
+        out = orc.route(x, Wg, 2, dtype, bias=bias, want_zp=True)
+        want = xf @ Wgf + bias.astype(np.float64)
+        assert np.max(np.abs(out["z"] - want)) <= 1e-13 * np.max(np.abs(want))
+
+
+def pin_temperature_scaling(orc):
+    """z = (l + g)/tau: tau=0.5 doubles z exactly, with or without noise."""
+    (x, Wg, _, _), _ = _tiny(4, dtype=BF16)
+    for gum in (False, True):
+        a = orc.route(x, Wg, 2, BF16, tau=1.0, use_gumbel=gum, seed=9, want_zp=True)
+        b = orc.route(x, Wg, 2, BF16, tau=0.5, use_gumbel=gum, seed=9, want_zp=True)
+        assert np.array_equal(b["z"], 2.0 * a["z"])
+        assert np.array_equal(a["ids"], b["ids"])
+
+
+def pin_noise_is_additive_gumbel(orc):
+    """With noise on, z - z_noiseless equals the generator's Gumbel draw for
+    (seed, token_offset + t, e), up to the rounding of one addition."""
+    (x, Wg, _, _), _ = _tiny(5, T=6, E=5, dtype=F32)
+    a = orc.route(x, Wg, 2, F32, want_zp=True)
+    b = orc.route(x, Wg, 2, F32, use_gumbel=True, seed=11, token_offset=100, want_zp=True)
+    for t in range(6):
+        for e in range(5):
+            g = orc.gumbel(11, 100 + t, e)
+            assert abs((b["z"][t, e] - a["z"][t, e]) - g) <= 1e-15 * (abs(a["z"][t, e]) + abs(g) + 1)
+
+
+def pin_token_offset(orc):
+    """Noise is keyed on the absolute token index: routing tokens [5, 5+T) of a
+    batch with offset 0 equals routing the same rows alone with offset 5."""
+    (x, Wg, _, _), _ = _tiny(6, T=16, E=8, dtype=BF16)
+    full = orc.route(x, Wg, 2, BF16, tau=0.5, use_gumbel=True, seed=2, want_zp=True)
+    part = orc.route(x[5:], Wg, 2, BF16, tau=0.5, use_gumbel=True, seed=2, token_offset=5,
+                     want_zp=True)
+    assert np.array_equal(part["z"], full["z"][5:])
+    assert np.array_equal(part["ids"], full["ids"][5:])
+
+
+def pin_topk_bruteforce(orc):
+    """The chosen set is the unique k-subset with the largest sum of z (all
+    C(E,k) subsets enumerated), listed in descending z."""
+    for seed, E, k in ((7, 6, 1), (8, 6, 2), (9, 7, 3), (10, 8, 2), (11, 5, 5)):
+        (x, Wg, _, _), _ = _tiny(seed, T=25, E=E, dtype=F32)
+        out = orc.route(x, Wg, k, F32, use_gumbel=(seed % 2 == 0), seed=seed, want_zp=True)
+        for t in range(25):
+            z = out["z"][t]
+            ids = out["ids"][t]
+            assert set(ids.tolist()) == npref.topk_bruteforce(z, k)
+            assert len(set(ids.tolist())) == k
+            assert all(z[ids[j]] >= z[ids[j + 1]] for j in range(k - 1))
+
+
+def pin_topk_ties_and_nan(orc):
+    """Exact ties go to the lower expert index; NaN ranks below every number."""
+    d, E = 4, 6
+    Wg = np.zeros((d, E), dtype=np.float32)
+    Wg[0, :] = [1.0, 3.0, 3.0, 2.0, 3.0, 0.5]
+    x = np.array([[1, 0, 0, 0]], dtype=np.float32)
+    out = orc.route(x, Wg, 3, F32)
+    assert out["ids"].tolist() == [[1, 2, 4]]
+    out = orc.route(np.zeros((1, d), np.float32), Wg, 4, F32)  # all logits 0
+    assert out["ids"].tolist() == [[0, 1, 2, 3]]
+    Wn = Wg.copy()
+    Wn[0, 1] = np.nan                       # expert 1's logit becomes NaN
+    out = orc.route(x, Wn, 6, F32)
+    assert out["ids"].tolist() == [[2, 4, 3, 0, 5, 1]]
+    xn = np.array([[np.nan, 0, 0, 0]], dtype=np.float32)  # every logit NaN
+    out = orc.route(xn, Wg, 2, F32)
+    assert out["ids"].tolist() == [[0, 1]]
+
+
+def pin_softmax_properties(orc):
+    """Probabilities sum to one, are invariant to a constant logit shift, are
+    1/E for equal logits, equal scipy's softmax, and the gates are exactly the
+    chosen probabilities rounded to fp32 (no renormalisation)."""
+    (x, Wg, _, _), (xf, Wgf, _, _) = _tiny(12, T=30, E=9, dtype=BF16)
+    out = orc.route(x, Wg, 2, BF16, want_zp=True)
+    assert np.allclose(out["p"].sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    from scipy import special
+    assert np.max(np.abs(out["p"] - special.softmax(out["z"], axis=1))) <= 1e-15
+    assert np.array_equal(out["gate_p"], np.take_along_axis(out["p"], out["ids"].astype(np.int64), 1))
+    assert np.array_equal(out["gates"], out["gate_p"].astype(np.float32))
+    shifted = orc.route(x, Wg, 2, BF16, bias=np.full(9, 3.0, np.float32), want_zp=True)
+    assert np.max(np.abs(shifted["p"] - out["p"])) <= 1e-15
+    assert np.array_equal(shifted["ids"], out["ids"])
+    eq = orc.route(np.zeros((3, 16), np.float32), np.ones((16, 9), np.float32), 2, F32, want_zp=True)
+    assert np.allclose(eq["p"], 1.0 / 9, rtol=0, atol=1e-16)
+    one = orc.route(np.ones((3, 16), np.float32), np.ones((16, 1), np.float32), 1, F32)
+    assert np.all(one["gates"] == 1.0) and np.all(one["ids"] == 0)
+
+
+def pin_router_worked_example(orc):
+    """P5 §3.1 prints a router distribution over 128 experts: 0.42 for expert
+    03, 0.38 for 17, 0.12 for 55, 0.05 for 89 and the rest below 0.01, and says
+    top-2 takes experts 03 and 17 with combined probability 0.80.  Feeding
+    logits ln p (the remaining 0.03 spread evenly over the other 124 experts)
+    through the router must reproduce that choice and those gates."""
+    with open(os.path.join(GOLDEN, "p5_router_example.json")) as f:
+        ex = json.load(f)
+    E = ex["num_experts"]
+    p = np.full(E, ex["rest_mass"] / (E - len(ex["listed"])))
+    for e, pe in ex["listed"].items():
+        p[int(e)] = pe
+    logits = np.log(p).astype(np.float32)
+    out = orc.route(np.zeros((1, 8), np.float32), np.zeros((8, E), np.float32), 2, F32,
+                    bias=logits, want_zp=True)
+    assert out["ids"].tolist() == [ex["top2_ids"]]
+    assert np.allclose(out["gates"][0], ex["top2_gates"], rtol=0, atol=1e-6)
+    assert abs(out["gates"][0].sum() - ex["top2_sum"]) < 1e-6
+    # every listed expert below the top-2 has < 0.13; the rest < 0.01
+    assert np.all(np.sort(out["p"][0])[:-4] < 0.01)
+
+
+def pin_gumbel_max_theorem(orc):
+    """Gumbel-max: with noise and tau=1, the first choice is distributed as
+    softmax(l), and the ordered pair (a, b) of the top-2 as p_a p_b / (1 - p_a)
+    (sampling without replacement).  Chi-square over 6000 independent tokens."""
+    E, T = 4, 6000
+    l = np.array([1.0, 0.0, -0.5, 0.7], dtype=np.float32)
+    out = orc.route(np.zeros((T, 2), np.float32), np.zeros((2, E), np.float32), 2, F32,
+                    bias=l, use_gumbel=True, seed=12345)
+    p = np.exp(l.astype(np.float64))
+    p /= p.sum()
+    first = np.bincount(out["ids"][:, 0], minlength=E)
+    assert stats.chisquare(first, p * T).pvalue > 1e-4
+    pairs = np.zeros((E, E))
+    for a, b in out["ids"]:
+        pairs[a, b] += 1
+    want = np.array([[p[a] * p[b] / (1 - p[a]) if a != b else 0.0 for b in range(E)] for a in range(E)])
+    off = ~np.eye(E, dtype=bool)
+    assert stats.chisquare(pairs[off], want[off] * T).pvalue > 1e-4
+    # without noise every token picks the same pair
+    det = orc.route(np.zeros((5, 2), np.float32), np.zeros((2, E), np.float32), 2, F32, bias=l)
+    assert np.all(det["ids"] == [0, 3])
+
+
+# ------------------------------------------------------------------- dispatch
+
+def pin_permute_library(orc):
+    """Counts are numpy's bincount, offsets its cumulative sum, and the
+    dispatch order numpy's stable argsort of the row-major expert ids."""
+    r = _rng(13)
+    for T, k, E in ((50, 2, 8), (37, 3, 5), (1, 1, 1), (64, 2, 128), (0, 2, 4)):
+        ids = np.array([r.permutation(E)[:k] for _ in range(T)], dtype=np.int32).reshape(T, k)
+        out = orc.permute(ids, E)
+        flat = ids.ravel()
+        assert np.array_equal(out["counts"], np.bincount(flat, minlength=E))
+        assert np.array_equal(out["offsets"], np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+        order = np.argsort(flat, kind="stable")
+        assert np.array_equal(out["sorted_token"], order // k)
+        inv = np.empty_like(order)
+        inv[order] = np.arange(len(order))
+        assert np.array_equal(out["pos"].ravel(), inv)
+
+
+# ---------------------------------------------------------------- expert FFN
+
+def pin_ffn_permutation_closed_form(orc):
+    """W1 and W2 as (non-symmetric) 0/1 selection matrices give
+    o = W2 GeLU(W1 x) by index arithmetic alone: o[c] = GeLU(x[src(c)])."""
+    d, d_ff = 8, 12
+    r = _rng(14)
+    rows = r.permutation(d_ff)[:d]          # W1[rows[i], i] = 1 -> h[rows[i]] = x[i]
+    W1 = np.zeros((d_ff, d), np.float32)
+    W1[rows, np.arange(d)] = 1.0
+    perm = r.permutation(d)                 # W2[c, rows[perm[c]]] = 1 -> o[c] = gelu(x[perm[c]])
+    W2 = np.zeros((d, d_ff), np.float32)
+    W2[np.arange(d), rows[perm]] = 1.0
+    x = r.standard_normal(d)
+    o = orc.expert_ffn(x, W1, W2, F32)
+    assert np.max(np.abs(o - npref.gelu_cdf(x[perm]))) <= 1e-15
+
+
+def pin_single_expert_equals_dense(orc):
+    """E=1, k=1: the layer equals the dense FFN W2 GeLU(W1 x), computed with
+    numpy matmul and scipy's normal CDF, in fp32 and in bf16 storage."""
+    for dtype in (F32, BF16):
+        (x, Wg, W1, W2), (xf, _, W1f, W2f) = _tiny(15, T=9, d=32, d_ff=64, E=1, dtype=dtype)
+        out = orc.forward(x, Wg, W1, W2, 1, dtype, dtype)
+        want = npref.gelu_cdf(xf @ W1f[0].T) @ W2f[0].T
+        assert np.all(out["ids"] == 0) and np.all(out["gates"] == 1.0)
+        assert np.max(np.abs(out["y"] - want)) <= 1e-13 * np.max(np.abs(want))
+
+
+def pin_int4_decode(orc):
+    """All sixteen signed codes decode (two's complement nibbles, even column in
+    the low nibble), each 128-column group takes its own scale, and an INT4
+    expert equals the dense FFN on q*s weights."""
+    d, d_ff = 256, 384
+    # every code at every parity, identity-like probing with one-hot rows
+    q = np.tile(np.arange(-8, 8), (d_ff, d // 16))
+    q = np.roll(q, 3, axis=1)
+    scales = np.ones((d_ff, d // 128))
+    scales[:, 1] = 2.0 ** -3
+    codes = npref.pack_int4(q)
+    sb = _bf16(scales)
+    # W2: identity on the first d hidden units, scale 1
+    q2 = np.zeros((d, d_ff), dtype=np.int64)
+    q2[np.arange(d), np.arange(d)] = 1
+    codes2, sb2 = npref.pack_int4(q2), _bf16(np.ones((d, d_ff // 128)))
+    for i in (0, 1, 2, 127, 128, 129, 255):
+        x = np.zeros(d)
+        x[i] = 1.0
+        o = orc.expert_ffn(x, codes, codes2, INT4_G128, S1e=sb, S2e=sb2)
+        h = q[:d, i] * scales[:d, i // 128]
+        want = npref.gelu_cdf(h)
+        assert np.max(np.abs(o - want)) <= 1e-15 * max(1.0, np.max(np.abs(want))), i
+    # random codes and scales against the dense formulation
+    r = _rng(16)
+    qa = r.integers(-8, 8, size=(d_ff, d))
+    qb = r.integers(-8, 8, size=(d, d_ff))
+    sa = _bf16(r.uniform(0.001, 0.02, size=(d_ff, d // 128)))
+    sb_ = _bf16(r.uniform(0.001, 0.02, size=(d, d_ff // 128)))
+    ca, cb = npref.pack_int4(qa), npref.pack_int4(qb)
+    x = r.standard_normal(d)
+    o = orc.expert_ffn(x, ca, cb, INT4_G128, S1e=sa, S2e=sb_)
+    W1f = npref.dequant_int4(ca, sa)
+    W2f = npref.dequant_int4(cb, sb_)
+    want = W2f @ npref.gelu_cdf(W1f @ x)
+    assert np.max(np.abs(o - want)) <= 1e-13 * np.max(np.abs(want))
+    # integer GEMM exactness: scales 1, integer x -> integer h before GeLU
+    ones_a = _bf16(np.ones((d_ff, d // 128)))
+    xi = r.integers(-3, 4, size=d).astype(np.float64)
+    h_exact = qa @ xi.astype(np.int64)
+    W2sel = np.zeros((d, d_ff), dtype=np.int64)
+    W2sel[np.arange(d), np.arange(d)] = 1
+    o = orc.expert_ffn(xi, ca, npref.pack_int4(W2sel), INT4_G128, S1e=ones_a,
+                       S2e=_bf16(np.ones((d, d_ff // 128))))
+    want = npref.gelu_cdf(h_exact[:d].astype(np.float64))
+    assert np.max(np.abs(o - want)) <= 1e-14 * np.max(np.abs(want))
+
+
+# ----------------------------------------------------------------- the layer
+
+def pin_layer_equals_dense_formulation(orc):
+    """The sparse oracle equals the dense evaluate-every-expert-then-mask
+    formulation (numpy) in y, ids and gates, with and without bias and noise."""
+    for seed, dtype, E, k, use_bias, gum, tau in ((17, F32, 6, 2, False, False, 1.0),
+                                                  (18, BF16, 5, 2, True, False, 1.0),
+                                                  (19, BF16, 7, 3, False, True, 0.5),
+                                                  (20, F32, 4, 1, True, True, 0.8)):
+        (x, Wg, W1, W2), (xf, Wgf, W1f, W2f) = _tiny(seed, T=10, d=16, d_ff=24, E=E, dtype=dtype)
+        bias = _rng(seed).standard_normal(E).astype(np.float32) if use_bias else None
+        out = orc.forward(x, Wg, W1, W2, k, dtype, dtype, bias=bias, tau=tau, use_gumbel=gum,
+                          seed=seed)
+        g = None
+        if gum:
+            g = np.array([[orc.gumbel(seed, t, e) for e in range(E)] for t in range(10)])
+        ref = npref.dense_moe(xf, Wgf, W1f, W2f, k, bias=None if bias is None else bias.astype(np.float64),
+                              tau=tau, g=g)
+        assert np.array_equal(out["ids"], ref["ids"])
+        assert np.max(np.abs(out["gate_p"] - ref["gate_p"])) <= 1e-14
+        assert np.max(np.abs(out["y"] - ref["y"])) <= 1e-12 * np.max(np.abs(ref["y"]))
+
+
+def pin_token_permutation_equivariance(orc):
+    """Permuting the tokens permutes y, ids and gates and leaves counts alone."""
+    (x, Wg, W1, W2), _ = _tiny(21, T=14, E=6, dtype=BF16)
+    a = orc.forward(x, Wg, W1, W2, 2, BF16, BF16)
+    perm = _rng(22).permutation(14)
+    b = orc.forward(x[perm], Wg, W1, W2, 2, BF16, BF16)
+    assert np.array_equal(b["ids"], a["ids"][perm])
+    assert np.array_equal(b["gates"], a["gates"][perm])
+    assert np.array_equal(b["y"], a["y"][perm])
+    assert np.array_equal(b["counts"], a["counts"])
+
+
+def pin_invariants_at_tiny_workload(orc):
+    """On the T=64, d=128, d_ff=512, E=8 fp32 workload: k distinct experts per
+    token, counts summing to T*k, and an average active fraction of exactly k/E
+    per token (P2 §2.2 gives 2/128 = 1.56% for 128 experts)."""
+    r = _rng(23)
+    T, d, d_ff, E, k = 64, 128, 512, 8, 2
+    x = r.standard_normal((T, d)).astype(np.float32)
+    Wg = (r.standard_normal((d, E)) / math.sqrt(d)).astype(np.float32)
+    W1 = (r.standard_normal((E, d_ff, d)) / math.sqrt(d)).astype(np.float32)
+    W2 = (r.standard_normal((E, d, d_ff)) / math.sqrt(d_ff)).astype(np.float32)
+    out = orc.forward(x, Wg, W1, W2, k, F32, F32)
+    assert all(len(set(row)) == k for row in out["ids"].tolist())
+    assert out["counts"].sum() == T * k
+    active = np.zeros((T, E), bool)
+    active[np.arange(T)[:, None], out["ids"]] = True
+    assert active.sum(axis=1).mean() / E == k / E
+    assert np.all(np.isfinite(out["y"]))
+
+
+ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

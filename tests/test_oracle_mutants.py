@@ -1,0 +1,77 @@
+"""Plant plausible mistakes in copies of the oracle and require the pin suite
+to catch every one.  Each mutant is one textual edit of moe_oracle.c (a dropped
+term, a wrong sign, index or operand, a swapped nibble ...), compiled with gcc
+into a temporary library; all mutants stay in bounds, so a caught mutant fails
+an assertion rather than crashing.  Runs on the CPU only."""
+import os
+
+import pytest
+
+from oracle import oracle as oracle_mod
+from tests import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle_mod.__file__), "moe_oracle.c")
+
+MUTANTS = [
+    ("bias dropped", "l[e] += (double)bias[e];", "l[e] += 0.0 * (double)bias[e];"),
+    ("gumbel sign", "return -log(-log(u));", "return log(-log(u));"),
+    ("tau multiplies", "z[e] = (l[e] + g) / tau;", "z[e] = (l[e] + g) * tau;"),
+    ("noise not tempered", "z[e] = (l[e] + g) / tau;", "z[e] = l[e] / tau + g;"),
+    ("ties to higher index", "return a < b;", "return a > b;"),
+    ("NaN ranks first", "return nb; /* the non-NaN one wins */", "return na;"),
+    ("ascending selection", "return z[a] > z[b];", "return z[a] < z[b];"),
+    ("softmax mass lost", "p[e] /= s;", "p[e] /= (s + 1.0);"),
+    ("softmax on logits", "p[e] = exp(z[e] - m);", "p[e] = exp(l[e] - m);"),
+    ("gate from slot index", "gates[t * k + j] = (float)p[best];", "gates[t * k + j] = (float)p[j];"),
+    ("gate_p from slot index", "gate_p[t * k + j] = p[best];", "gate_p[t * k + j] = p[j];"),
+    ("gelu tanh form", "return 0.5 * h * (1.0 + erf(h / sqrt(2.0)));",
+     "return 0.5 * h * (1.0 + tanh(0.7978845608028654 * (h + 0.044715 * h * h * h)));"),
+    ("gelu half dropped", "return 0.5 * h * (1.0 + erf(h / sqrt(2.0)));",
+     "return h * (1.0 + erf(h / sqrt(2.0)));"),
+    ("gelu sqrt2 dropped", "return 0.5 * h * (1.0 + erf(h / sqrt(2.0)));",
+     "return 0.5 * h * (1.0 + erf(h));"),
+    ("W1 reads x reversed", "h += load_w(W1e, S1e, w_dtype, d, n, i) * xr[i];",
+     "h += load_w(W1e, S1e, w_dtype, d, n, i) * xr[d - 1 - i];"),
+    ("GeLU skipped", "a[n] = oracle_gelu(h);", "a[n] = h;"),
+    ("W2 reads hidden reversed", "acc += load_w(W2e, S2e, w_dtype, d_ff, c, n) * a[n];",
+     "acc += load_w(W2e, S2e, w_dtype, d_ff, c, n) * a[d_ff - 1 - n];"),
+    ("int4 nibble order", "int nib = (c % 2 == 0) ? (byte & 0x0F) : (byte >> 4);",
+     "int nib = (c % 2 == 0) ? (byte >> 4) : (byte & 0x0F);"),
+    ("int4 unsigned", "return nib >= 8 ? nib - 16 : nib;", "return nib;"),
+    ("int4 group order", "s = bf16_to_double(((const uint16_t *)scales)[n * (K / 128) + c / 128]);",
+     "s = bf16_to_double(((const uint16_t *)scales)[n * (K / 128) + (K / 128 - 1 - c / 128)]);"),
+    ("philox 9 rounds", "for (int r = 0; r < 10; ++r) {", "for (int r = 0; r < 9; ++r) {"),
+    ("philox key bump lost", "k1 += W1;", "k1 += 0;"),
+    ("uniform from second word", "return ((double)(r[0] >> 11) + 0.5)", "return ((double)(r[1] >> 11) + 0.5)"),
+    ("noise ignores token offset", "oracle_gumbel(seed, token_offset + (uint64_t)t, (uint64_t)e)",
+     "oracle_gumbel(seed, (uint64_t)t, (uint64_t)e)"),
+    ("noise key swapped", "oracle_gumbel(seed, token_offset + (uint64_t)t, (uint64_t)e)",
+     "oracle_gumbel(seed, (uint64_t)e, token_offset + (uint64_t)t)"),
+    ("unstable scatter", "int32_t slot = offsets[e] + fill[e];", "int32_t slot = offsets[e + 1] - 1 - fill[e];"),
+    ("combine uses first gate", "double w = gate_p[t * k + j];", "double w = gate_p[t * k];"),
+    ("bf16 widened wrongly", "uint32_t w = (uint32_t)bits << 16;", "uint32_t w = ((uint32_t)bits << 16) | 0x8000u;"),
+    ("logits skip last input", "for (int64_t i = 0; i < d; ++i) {\n            double xi",
+     "for (int64_t i = 0; i + 1 < d; ++i) {\n            double xi"),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, source, name, old, new):
+    assert source.count(old) == 1, f"mutation site for '{name}' not unique in moe_oracle.c"
+    mutated = tmp_path / "mutant.c"
+    mutated.write_text(source.replace(old, new))
+    lib = oracle_mod.build(src=str(mutated), out=str(tmp_path / "libmutant.so"))
+    orc = oracle_mod.Oracle(lib)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the mutant '{name}'"
