@@ -1,0 +1,156 @@
+"""ctypes binding of libmoe_mi355x.so (include/moe.h).
+
+Argument marshalling only: torch tensors are passed as raw device pointers
+(PyTorch supplies device memory and the stream), every step of the layer runs
+in the library's HIP kernels.  Importing this module needs no GPU; loading the
+library fails loudly if it has not been built.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
+F32, BF16, INT4_G128 = 0, 1, 2
+GEMM_AUTO, GEMM_STREAMING, GEMM_TILED = 0, 1, 2
+
+EXPORTS = ("moe_workspace_size", "moe_router_workspace_size", "moe_forward", "moe_router", "moe_permute",
+           "moe_grouped_gemm", "moe_combine", "moe_status_string", "moe_last_hip_error")
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64),
+        ("d", ctypes.c_int64),
+        ("d_ff", ctypes.c_int64),
+        ("E", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+        ("act_dtype", ctypes.c_int32),
+        ("w_dtype", ctypes.c_int32),
+        ("tau", ctypes.c_float),
+        ("use_gumbel", ctypes.c_int32),
+        ("seed", ctypes.c_uint64),
+        ("token_offset", ctypes.c_uint64),
+        ("gemm_path", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, what, hip_error=0):
+        self.status = status
+        self.hip_error = hip_error
+        super().__init__(f"{what}: {status_string(status)} (status {status}, hip error {hip_error})")
+
+
+_lib = None
+
+
+def load(path=LIB_PATH):
+    """Load the built library (once).  Raises FileNotFoundError if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(f"{path} is not built; run __graft_entry__.build() or "
+                                f"python sparse_mixture_experts_03_amd/build.py")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    CFG = ctypes.POINTER(MoeConfig)
+    lib.moe_workspace_size.argtypes = [CFG, ctypes.POINTER(SZ)]
+    lib.moe_router_workspace_size.argtypes = [CFG, ctypes.POINTER(SZ)]
+    lib.moe_forward.argtypes = [CFG, P, P, P, P, P, I64, P, P, I64, P, P, P, P, P, SZ, P]
+    lib.moe_router.argtypes = [CFG, P, P, P, P, P, P, SZ, P]
+    lib.moe_permute.argtypes = [CFG, P, P, P, P, P, P]
+    lib.moe_grouped_gemm.argtypes = [CFG, I32, P, P, P, P, P, I64, P, P]
+    lib.moe_combine.argtypes = [CFG, P, P, P, P, P]
+    for name in ("moe_workspace_size", "moe_router_workspace_size", "moe_forward", "moe_router", "moe_permute",
+                 "moe_grouped_gemm", "moe_combine"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_last_hip_error.argtypes = []
+    lib.moe_last_hip_error.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load().moe_status_string(status).decode()
+
+
+def config(T, d, d_ff, E, k, act_dtype, w_dtype, tau=1.0, use_gumbel=False, seed=0, token_offset=0,
+           gemm_path=GEMM_AUTO):
+    return MoeConfig(T, d, d_ff, E, k, act_dtype, w_dtype, tau, int(bool(use_gumbel)), seed, token_offset,
+                     gemm_path, 0)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _expert_stride(W):
+    return W.stride(0) * W.element_size()
+
+
+def _check(status, what):
+    if status != MOE_OK:
+        raise MoeError(status, what, load().moe_last_hip_error())
+
+
+def moe_workspace_size(cfg):
+    n = ctypes.c_size_t()
+    _check(load().moe_workspace_size(ctypes.byref(cfg), ctypes.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+def moe_router_workspace_size(cfg):
+    n = ctypes.c_size_t()
+    _check(load().moe_router_workspace_size(ctypes.byref(cfg), ctypes.byref(n)), "moe_router_workspace_size")
+    return n.value
+
+
+def moe_forward(cfg, x, Wg, bias, W1, W1_scales, W2, W2_scales, y, expert_ids, gate_weights, counts, workspace,
+                stream=None, W1_stride=None, W2_stride=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().moe_forward(ctypes.byref(cfg), _ptr(x), _ptr(Wg), _ptr(bias),
+                            _ptr(W1), _ptr(W1_scales), W1_stride if W1_stride is not None else _expert_stride(W1),
+                            _ptr(W2), _ptr(W2_scales), W2_stride if W2_stride is not None else _expert_stride(W2),
+                            _ptr(y), _ptr(expert_ids), _ptr(gate_weights), _ptr(counts), _ptr(workspace), ws_bytes,
+                            _stream(stream))
+    _check(st, "moe_forward")
+
+
+def moe_router(cfg, x, Wg, bias, expert_ids, gate_weights, workspace, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().moe_router(ctypes.byref(cfg), _ptr(x), _ptr(Wg), _ptr(bias), _ptr(expert_ids), _ptr(gate_weights),
+                           _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "moe_router")
+
+
+def moe_permute(cfg, expert_ids, counts, offsets, sorted_token, pos, stream=None):
+    st = load().moe_permute(ctypes.byref(cfg), _ptr(expert_ids), _ptr(counts), _ptr(offsets), _ptr(sorted_token),
+                            _ptr(pos), _stream(stream))
+    _check(st, "moe_permute")
+
+
+def moe_grouped_gemm(cfg, which, A, a_rows, offsets, W, W_scales, out, stream=None, W_stride=None):
+    st = load().moe_grouped_gemm(ctypes.byref(cfg), which, _ptr(A), _ptr(a_rows), _ptr(offsets), _ptr(W),
+                                 _ptr(W_scales), W_stride if W_stride is not None else _expert_stride(W), _ptr(out),
+                                 _stream(stream))
+    _check(st, "moe_grouped_gemm")
+
+
+def moe_combine(cfg, Y, pos, gate_weights, y, stream=None):
+    st = load().moe_combine(ctypes.byref(cfg), _ptr(Y), _ptr(pos), _ptr(gate_weights), _ptr(y), _stream(stream))
+    _check(st, "moe_combine")

@@ -1,0 +1,97 @@
+// Internal helpers shared by the gfx950 kernels of the MoE-layer library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Storage codes (match moe_dtype in include/moe.h).
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+constexpr int kINT4 = 2;
+
+// MFMA operand / accumulator vectors.
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).  Lane l supplies row
+// (l % 16) of A and column (l % 16) of B, eight k-values each from k-block
+// (l / 16); it receives D[4*(l/16) + i][l % 16], i = 0..3.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float gelu_erf(float h) {
+    return 0.5f * h * (1.0f + erff(h * 0.70710678118654752440f));
+}
+
+// Map a flat m-tile index onto (expert, first dispatch position, rows) for a
+// grouped GEMM whose experts hold offsets[e+1]-offsets[e] rows, cut into tiles
+// of BM rows.  Tiles are numbered expert-major.  Returns false when mt lies
+// beyond the last real tile.  Called by one whole wavefront (all lanes get
+// the same answer); E <= 256.
+__device__ __forceinline__ bool find_mtile(const int32_t* __restrict__ offsets, int E, int BM, int mt,
+                                           int* expert, int* pos0, int* rows) {
+    const int lane = threadIdx.x & 63;
+    int tiles[4], begin[4];
+    int local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        int e = lane * 4 + j;
+        int n = 0, b = 0;
+        if (e < E) {
+            b = offsets[e];
+            n = offsets[e + 1] - b;
+        }
+        begin[j] = b;
+        tiles[j] = (n + BM - 1) / BM;
+        local += tiles[j];
+    }
+    // inclusive scan of per-lane tile counts across the wavefront
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+    }
+    int excl = incl - local;
+    int total = __shfl(incl, 63, 64);
+    if (mt >= total) return false;
+    // the lane whose range holds mt
+    unsigned long long hit = __ballot(mt >= excl && mt < incl);
+    int src = __ffsll((long long)hit) - 1;
+    int e_found = -1, p0 = 0, r = 0;
+    if (lane == src) {
+        int acc = excl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (e_found < 0 && mt < acc + tiles[j]) {
+                e_found = lane * 4 + j;
+                p0 = begin[j] + (mt - acc) * BM;
+                r = min(BM, offsets[e_found + 1] - p0);
+            }
+            acc += tiles[j];
+        }
+    }
+    *expert = __shfl(e_found, src, 64);
+    *pos0 = __shfl(p0, src, 64);
+    *rows = __shfl(r, src, 64);
+    return true;
+}
+
+}  // namespace moe

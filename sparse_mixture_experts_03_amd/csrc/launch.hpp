@@ -1,0 +1,63 @@
+// Host-side launchers of the library's kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- router
+struct RouterPlan {
+    int tokens_per_tile;   // tokens per partial-logit workgroup (TT * E <= 1024)
+    int tiles;             // token tiles
+    int chunks_per_split;  // 32-column chunks of the input dimension per split
+    int splits;            // workgroups along the input dimension
+    size_t partial_bytes;  // binary64 partial logits [splits][T][E]
+};
+RouterPlan router_plan(int64_t T, int64_t d, int E);
+
+struct RouterArgs {
+    const void* x;
+    const void* Wg;
+    const float* bias;
+    int64_t T, d;
+    int E, k, act_dtype;
+    float tau;
+    int use_gumbel;
+    uint64_t seed, token_offset;
+    double* partial;  // workspace, >= router_plan().partial_bytes
+    int32_t* ids;
+    float* gates;
+};
+hipError_t launch_router(const RouterArgs& a, hipStream_t stream);
+
+// --------------------------------------------------------------- permute
+hipError_t launch_permute(const int32_t* ids, int64_t T, int E, int k, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_token, int32_t* pos, hipStream_t stream);
+// counts[0..E) = 0 (T == 0)
+hipError_t launch_zero_counts(int32_t* counts, int E, int32_t* offsets, hipStream_t stream);
+
+// ---------------------------------------------------------- grouped GEMM
+struct GemmArgs {
+    int which;              // 1: out = GeLU(W1 . A[a_rows]) ; 2: out = W2 . A
+    const void* A;          // activations: x [T][K] (which 1) or H [T*k][K] (which 2)
+    const int32_t* a_rows;  // which 1: dispatch position -> token row of A
+    const int32_t* offsets; // [E+1]
+    const void* W;          // expert 0's [N][K] matrix
+    const void* W_scales;   // INT4: bf16 [E][N][K/128]
+    int64_t W_stride;       // bytes between experts
+    void* out;              // [T*k][N]
+    int64_t T, N, K;        // T: tokens (rows = T * k)
+    int E, k, w_dtype, act_dtype;
+    int path;               // 1 streaming, 2 tiled
+};
+hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream);  // BF16 / INT4 weights
+hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);   // BF16 weights
+hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t stream);     // F32 weights
+
+// --------------------------------------------------------------- combine
+hipError_t launch_combine(const float* Y, const int32_t* pos, const float* gates, void* y, int64_t T, int64_t d,
+                          int k, int act_dtype, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,284 @@
+// C ABI of the MoE-layer forward: argument checks, workspace carve-up and the
+// stream-ordered launch sequence
+//   router (partial logits, finalize) -> permute -> GEMM1 (+GeLU) -> GEMM2 -> combine.
+// No host synchronisation and no host<->device copy happens inside a call;
+// counts and the dispatch order stay on the device and every kernel finds its
+// work from them.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+constexpr int64_t kMaxT = int64_t(1) << 24;
+constexpr int64_t kMaxDim = int64_t(1) << 17;
+constexpr int kMaxE = 256;
+constexpr int kMaxK = 8;
+constexpr int64_t kStreamingMaxT = 16;  // automatic path: streaming kernel up to 16 tokens
+
+moe_status hip_fail(hipError_t e) {
+    g_last_hip_error = (int32_t)e;
+    return MOE_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int64_t elem_bits(int32_t dtype) { return dtype == MOE_DTYPE_F32 ? 32 : dtype == MOE_DTYPE_BF16 ? 16 : 4; }
+
+moe_status check_config(const moe_config* c) {
+    if (!c) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->T < 0 || c->T > kMaxT) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->E < 1 || c->E > kMaxE) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->k < 1 || c->k > kMaxK || c->k > c->E) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->d < 64 || c->d > kMaxDim || c->d % 64 != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->d_ff < 64 || c->d_ff > kMaxDim || c->d_ff % 64 != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (!(c->tau > 0.0f) || !isfinite(c->tau)) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->use_gumbel != 0 && c->use_gumbel != 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->gemm_path < MOE_GEMM_AUTO || c->gemm_path > MOE_GEMM_TILED) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->reserved != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->act_dtype != MOE_DTYPE_F32 && c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->w_dtype < MOE_DTYPE_F32 || c->w_dtype > MOE_DTYPE_INT4_G128) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->w_dtype == MOE_DTYPE_INT4_G128 && (c->d % 128 != 0 || c->d_ff % 128 != 0))
+        return MOE_ERR_INVALID_ARGUMENT;
+    // supported pairings: F32/F32, BF16/BF16, BF16/INT4
+    if ((c->act_dtype == MOE_DTYPE_F32) != (c->w_dtype == MOE_DTYPE_F32)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+struct Layout {
+    size_t partial, offsets, sorted_token, pos, H, Y, total;
+};
+
+Layout layout_of(const moe_config& c) {
+    Layout L;
+    const size_t Tk = (size_t)c.T * (size_t)c.k;
+    const size_t hbytes = c.w_dtype == MOE_DTYPE_F32 ? 4 : 2;
+    size_t off = 0;
+    L.partial = off;
+    off = round_up(off + moe::router_plan(c.T, c.d, c.E).partial_bytes, 256);
+    L.offsets = off;
+    off = round_up(off + sizeof(int32_t) * (size_t)(c.E + 1), 256);
+    L.sorted_token = off;
+    off = round_up(off + sizeof(int32_t) * Tk, 256);
+    L.pos = off;
+    off = round_up(off + sizeof(int32_t) * Tk, 256);
+    L.H = off;
+    off = round_up(off + hbytes * Tk * (size_t)c.d_ff, 256);
+    L.Y = off;
+    off = round_up(off + sizeof(float) * Tk * (size_t)c.d, 256);
+    L.total = c.T == 0 ? 0 : off;
+    return L;
+}
+
+// Expert weight pointer/stride checks for an N x K matrix per expert.
+moe_status check_weights(const moe_config& c, const void* W, const void* S, int64_t stride, int64_t N, int64_t K) {
+    if (!W || !aligned(W, 16)) return MOE_ERR_INVALID_ARGUMENT;
+    const int64_t bytes = N * K * elem_bits(c.w_dtype) / 8;
+    if (stride < bytes || stride % 16 != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (c.w_dtype == MOE_DTYPE_INT4_G128) {
+        if (!S || !aligned(S, 2)) return MOE_ERR_INVALID_ARGUMENT;
+    }
+    return MOE_OK;
+}
+
+int gemm_path_of(const moe_config& c) {
+    if (c.w_dtype == MOE_DTYPE_F32) return 0;
+    if (c.w_dtype == MOE_DTYPE_INT4_G128) return MOE_GEMM_STREAMING;  // tiled INT4 kernel not built yet
+    if (c.gemm_path != MOE_GEMM_AUTO) return c.gemm_path;
+    return c.T <= kStreamingMaxT ? MOE_GEMM_STREAMING : MOE_GEMM_TILED;
+}
+
+hipError_t run_gemm(const moe_config& c, int which, const void* A, const int32_t* a_rows, const int32_t* offsets,
+                    const void* W, const void* S, int64_t stride, void* out, hipStream_t stream) {
+    moe::GemmArgs g;
+    g.which = which;
+    g.A = A;
+    g.a_rows = a_rows;
+    g.offsets = offsets;
+    g.W = W;
+    g.W_scales = S;
+    g.W_stride = stride;
+    g.out = out;
+    g.T = c.T;
+    g.N = which == 1 ? c.d_ff : c.d;
+    g.K = which == 1 ? c.d : c.d_ff;
+    g.E = c.E;
+    g.k = c.k;
+    g.w_dtype = c.w_dtype;
+    g.act_dtype = c.act_dtype;
+    g.path = gemm_path_of(c);
+    if (c.w_dtype == MOE_DTYPE_F32) return moe::launch_gemm_f32(g, stream);
+    if (g.path == MOE_GEMM_STREAMING) return moe::launch_gemm_stream(g, stream);
+    return moe::launch_gemm_tiled(g, stream);
+}
+
+moe::RouterArgs router_args(const moe_config& c, const void* x, const void* Wg, const float* bias, int32_t* ids,
+                            float* gates, void* partial) {
+    moe::RouterArgs r;
+    r.x = x;
+    r.Wg = Wg;
+    r.bias = bias;
+    r.T = c.T;
+    r.d = c.d;
+    r.E = c.E;
+    r.k = c.k;
+    r.act_dtype = c.act_dtype;
+    r.tau = c.tau;
+    r.use_gumbel = c.use_gumbel;
+    r.seed = c.seed;
+    r.token_offset = c.token_offset;
+    r.partial = static_cast<double*>(partial);
+    r.ids = ids;
+    r.gates = gates;
+    return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes) {
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+    *bytes = layout_of(*cfg).total;
+    return MOE_OK;
+}
+
+moe_status moe_router_workspace_size(const moe_config* cfg, size_t* bytes) {
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+    *bytes = cfg->T == 0 ? 0 : round_up(moe::router_plan(cfg->T, cfg->d, cfg->E).partial_bytes, 256);
+    return MOE_OK;
+}
+
+moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, const float* router_bias,
+                       const void* W1, const void* W1_scales, int64_t W1_expert_stride, const void* W2,
+                       const void* W2_scales, int64_t W2_expert_stride, void* y, int32_t* expert_ids,
+                       float* gate_weights, int32_t* counts, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    const moe_config& c = *cfg;
+    if (!counts || !aligned(counts, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    if (c.T == 0) {
+        hipError_t e = moe::launch_zero_counts(counts, c.E, nullptr, stream);
+        return e == hipSuccess ? MOE_OK : hip_fail(e);
+    }
+    if (!x || !aligned(x, 16) || !Wg || !aligned(Wg, 16) || !y || !aligned(y, 16)) return MOE_ERR_INVALID_ARGUMENT;
+    if (!expert_ids || !aligned(expert_ids, 4) || !gate_weights || !aligned(gate_weights, 4))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (router_bias && !aligned(router_bias, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    if ((s = check_weights(c, W1, W1_scales, W1_expert_stride, c.d_ff, c.d)) != MOE_OK) return s;
+    if ((s = check_weights(c, W2, W2_scales, W2_expert_stride, c.d, c.d_ff)) != MOE_OK) return s;
+    const Layout L = layout_of(c);
+    if (!workspace || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+
+    char* ws = static_cast<char*>(workspace);
+    int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+    int32_t* sorted_token = reinterpret_cast<int32_t*>(ws + L.sorted_token);
+    int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
+    void* H = ws + L.H;
+    float* Y = reinterpret_cast<float*>(ws + L.Y);
+
+    hipError_t e = moe::launch_router(router_args(c, x, Wg, router_bias, expert_ids, gate_weights, ws + L.partial),
+                                      stream);
+    if (e != hipSuccess) return hip_fail(e);
+    e = moe::launch_permute(expert_ids, c.T, c.E, c.k, counts, offsets, sorted_token, pos, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    e = run_gemm(c, 1, x, sorted_token, offsets, W1, W1_scales, W1_expert_stride, H, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    e = run_gemm(c, 2, H, nullptr, offsets, W2, W2_scales, W2_expert_stride, Y, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    e = moe::launch_combine(Y, pos, gate_weights, y, c.T, c.d, c.k, c.act_dtype, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return MOE_OK;
+}
+
+moe_status moe_router(const moe_config* cfg, const void* x, const void* Wg, const float* router_bias,
+                      int32_t* expert_ids, float* gate_weights, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    const moe_config& c = *cfg;
+    if (c.T == 0) return MOE_OK;
+    if (!x || !aligned(x, 16) || !Wg || !aligned(Wg, 16)) return MOE_ERR_INVALID_ARGUMENT;
+    if (!expert_ids || !aligned(expert_ids, 4) || !gate_weights || !aligned(gate_weights, 4))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (router_bias && !aligned(router_bias, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    const size_t need = round_up(moe::router_plan(c.T, c.d, c.E).partial_bytes, 256);
+    if (!workspace || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    hipError_t e = moe::launch_router(router_args(c, x, Wg, router_bias, expert_ids, gate_weights, workspace), stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+moe_status moe_permute(const moe_config* cfg, const int32_t* expert_ids, int32_t* counts, int32_t* offsets,
+                       int32_t* sorted_token, int32_t* pos, hipStream_t stream) {
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    const moe_config& c = *cfg;
+    if (!counts || !aligned(counts, 4) || !offsets || !aligned(offsets, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    if (c.T > 0) {
+        if (!expert_ids || !aligned(expert_ids, 4) || !sorted_token || !aligned(sorted_token, 4) || !pos ||
+            !aligned(pos, 4))
+            return MOE_ERR_INVALID_ARGUMENT;
+    }
+    hipError_t e = moe::launch_permute(expert_ids, c.T, c.E, c.k, counts, offsets, sorted_token, pos, stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+moe_status moe_grouped_gemm(const moe_config* cfg, int32_t which, const void* A, const int32_t* a_rows,
+                            const int32_t* offsets, const void* W, const void* W_scales, int64_t W_expert_stride,
+                            void* out, hipStream_t stream) {
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    const moe_config& c = *cfg;
+    if (which != 1 && which != 2) return MOE_ERR_INVALID_ARGUMENT;
+    if (c.T == 0) return MOE_OK;
+    if (!A || !aligned(A, 16) || !offsets || !aligned(offsets, 4) || !out || !aligned(out, 16))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (which == 1 && (!a_rows || !aligned(a_rows, 4))) return MOE_ERR_INVALID_ARGUMENT;
+    const int64_t N = which == 1 ? c.d_ff : c.d;
+    const int64_t K = which == 1 ? c.d : c.d_ff;
+    if ((s = check_weights(c, W, W_scales, W_expert_stride, N, K)) != MOE_OK) return s;
+    hipError_t e = run_gemm(c, which, A, a_rows, offsets, W, W_scales, W_expert_stride, out, stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+moe_status moe_combine(const moe_config* cfg, const float* Y, const int32_t* pos, const float* gate_weights, void* y,
+                       hipStream_t stream) {
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    const moe_config& c = *cfg;
+    if (c.T == 0) return MOE_OK;
+    if (!Y || !aligned(Y, 16) || !pos || !aligned(pos, 4) || !gate_weights || !aligned(gate_weights, 4) || !y ||
+        !aligned(y, 16))
+        return MOE_ERR_INVALID_ARGUMENT;
+    hipError_t e = moe::launch_combine(Y, pos, gate_weights, y, c.T, c.d, c.k, c.act_dtype, stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+const char* moe_status_string(moe_status status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+int32_t moe_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

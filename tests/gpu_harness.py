@@ -1,0 +1,144 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI, run
+the CPU oracle on the same bits, and compare.
+
+Comparison rules:
+  * expert ids: bit-exact, except tokens whose k-th and (k+1)-th largest z (or
+    two chosen z) lie within 1e-12 * max|z| in the oracle: there the binary64
+    rounding order of the logits may legitimately decide, so either choice is
+    accepted (and counted).  With fp64 logits such tokens are ~1e-12 rare.
+  * gate weights: |g - g_ref| <= 4 ulp of fp32 at g_ref.
+  * counts / offsets / sorted_token / pos: bit-exact (computed by the oracle
+    from the GPU's own ids when ambiguous tokens exist).
+  * y: max|y - y_ref| / max|y_ref| <= tol (1e-5 for fp32, 2e-2 for bf16 and
+    INT4 experts), over all tokens or a sample of tokens.
+"""
+import numpy as np
+import torch
+
+import moe_synth
+import sparse_mixture_experts_03_amd as moe
+
+TOL = {moe.F32: 1e-5, moe.BF16: 2e-2}
+AMBIGUOUS_REL = 1e-12
+
+
+def tau32(tau):
+    """The temperature as the library receives it (fp32), widened for the oracle."""
+    return float(np.float32(tau))
+
+
+def abi_config(cfg, gemm_path=moe.GEMM_AUTO, seed=0, token_offset=0):
+    return moe.config(cfg["T"], cfg["d"], cfg["d_ff"], cfg["E"], cfg["k"], cfg["act"], cfg["w"], tau=cfg["tau"],
+                      use_gumbel=cfg["gumbel"], seed=seed, token_offset=token_offset, gemm_path=gemm_path)
+
+
+def run_forward(cfg, inp, gemm_path=moe.GEMM_AUTO, noise_seed=0, token_offset=0, device="cuda"):
+    c = abi_config(cfg, gemm_path, noise_seed, token_offset)
+    layer = moe.MoELayerForward(c, device=device)
+    y, ids, gates, counts = layer(inp["x"], inp["Wg"], inp["bias"], inp["W1"], inp["W2"], inp["S1"], inp["S2"])
+    torch.cuda.synchronize()
+    return dict(y=y, ids=ids, gates=gates, counts=counts, layer=layer)
+
+
+def oracle_route(orc, cfg, inp, noise_seed=0, token_offset=0):
+    bias = None if inp["bias"] is None else inp["bias"].cpu().numpy()
+    return orc.route(moe_synth.to_bits(inp["x"]), moe_synth.to_bits(inp["Wg"]), cfg["k"], cfg["act"], bias=bias,
+                     tau=tau32(cfg["tau"]), use_gumbel=cfg["gumbel"], seed=noise_seed, token_offset=token_offset,
+                     want_zp=True)
+
+
+def ambiguous_tokens(z, k):
+    """Tokens whose top-k choice or order is decided by less than the rounding margin."""
+    zs = -np.sort(-np.where(np.isnan(z), -np.inf, z), axis=1)
+    scale = np.maximum(np.max(np.abs(np.where(np.isfinite(z), z, 0)), axis=1), 1e-300)
+    upto = min(k + 1, z.shape[1])
+    gaps = zs[:, :upto - 1] - zs[:, 1:upto]
+    return np.where(np.any(gaps <= AMBIGUOUS_REL * scale[:, None], axis=1))[0]
+
+
+def check_routing(gpu_ids, gpu_gates, ref, k):
+    """Assert routing parity; returns the list of ambiguous tokens."""
+    amb = set(ambiguous_tokens(ref["z"], k).tolist())
+    diff = np.where(np.any(gpu_ids != ref["ids"], axis=1))[0]
+    bad = [t for t in diff.tolist() if t not in amb]
+    assert not bad, f"expert ids differ at tokens {bad[:10]} (of {len(bad)}); e.g. gpu {gpu_ids[bad[0]]} " \
+                    f"oracle {ref['ids'][bad[0]]}"
+    ok = np.ones(len(gpu_ids), bool)
+    ok[list(amb)] = False
+    g, r = gpu_gates[ok], ref["gates"][ok]
+    ulp = np.spacing(np.abs(r).astype(np.float32)).astype(np.float64)
+    err = np.abs(g.astype(np.float64) - r.astype(np.float64))
+    assert np.all(err <= 4 * ulp), f"gate weights differ by up to {np.max(err / ulp):.1f} ulp"
+    # every token has k distinct experts in range
+    E = ref["z"].shape[1]
+    assert np.all((gpu_ids >= 0) & (gpu_ids < E))
+    assert all(len(set(row)) == k for row in gpu_ids.tolist())
+    return sorted(amb)
+
+
+def check_dispatch(orc, gpu_ids, E, counts, offsets=None, sorted_token=None, pos=None):
+    ref = orc.permute(gpu_ids, E)
+    assert np.array_equal(counts, ref["counts"]), "counts differ"
+    if offsets is not None:
+        assert np.array_equal(offsets, ref["offsets"]), "offsets differ"
+    if sorted_token is not None:
+        assert np.array_equal(sorted_token, ref["sorted_token"]), "sorted_token differs"
+    if pos is not None:
+        assert np.array_equal(pos.reshape(-1), ref["pos"].reshape(-1)), "pos differs"
+    return ref
+
+
+def sample_tokens(ids, E, max_tokens, exclude=(), rng_seed=0):
+    """Tokens to evaluate in the oracle: for each non-empty expert the first and
+    last token of its dispatch segment (the tile boundaries the kernels must
+    get right), then a seeded subsample to max_tokens that keeps the busiest
+    and the least busy expert's boundaries and the first and last token."""
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    order = np.argsort(flat, kind="stable")
+    tok_sorted = order // k
+    counts = np.bincount(flat, minlength=E)
+    offs = np.concatenate([[0], np.cumsum(counts)])
+    must, extra = [0, T - 1], []
+    nz = np.where(counts > 0)[0]
+    busiest, idlest = nz[np.argmax(counts[nz])], nz[np.argmin(counts[nz])]
+    for e in nz:
+        pair = [int(tok_sorted[offs[e]]), int(tok_sorted[offs[e + 1] - 1])]
+        (must if e in (busiest, idlest) else extra).extend(pair)
+    chosen = list(dict.fromkeys(t for t in must if t not in exclude))
+    rest = [t for t in dict.fromkeys(extra) if t not in exclude and t not in chosen]
+    rng = np.random.default_rng(rng_seed)
+    rng.shuffle(rest)
+    chosen += rest[:max(0, max_tokens - len(chosen))]
+    return np.array(sorted(chosen), dtype=np.int64)
+
+
+def oracle_y(orc, cfg, inp, ref, tokens):
+    """Oracle y rows for `tokens`, copying back only the experts they use."""
+    E = cfg["E"]
+    used = sorted(set(ref["ids"][tokens].reshape(-1).tolist()))
+    W1 = [None] * E
+    W2 = [None] * E
+    S1 = [None] * E if inp["S1"] is not None else None
+    S2 = [None] * E if inp["S2"] is not None else None
+    for e in used:
+        W1[e] = moe_synth.to_bits(inp["W1"][e])
+        W2[e] = moe_synth.to_bits(inp["W2"][e])
+        if S1 is not None:
+            S1[e] = moe_synth.to_bits(inp["S1"][e])
+            S2[e] = moe_synth.to_bits(inp["S2"][e])
+    return orc.forward_tokens(moe_synth.to_bits(inp["x"]), ref["ids"], ref["gate_p"], W1, W2, cfg["act"], cfg["w"],
+                              cfg["d_ff"], tokens, S1=S1, S2=S2)
+
+
+def normwise_err(y_gpu_rows, y_ref):
+    return float(np.max(np.abs(y_gpu_rows - y_ref)) / max(np.max(np.abs(y_ref)), 1e-300))
+
+
+def check_y(y_gpu, tokens, y_ref, act):
+    rows = y_gpu[torch.as_tensor(tokens, device=y_gpu.device)].double().cpu().numpy()
+    err = normwise_err(rows, y_ref)
+    tol = TOL[act]
+    assert np.all(np.isfinite(rows)), "non-finite y"
+    assert err <= tol, f"y normwise error {err:.3e} > {tol}"
+    return err

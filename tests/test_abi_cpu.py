@@ -1,0 +1,156 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/moe.h
+declares, and its host-side checks return the documented status codes before
+anything is enqueued (no GPU is touched: every call here is rejected early or
+is a pure size query)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import moe_synth
+import sparse_mixture_experts_03_amd as moe
+from sparse_mixture_experts_03_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libmoe_mi355x.so is not built (run __graft_entry__.build())")
+    return binding.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_config_struct_layout(tmp_path):
+    """The ctypes mirror of moe_config matches the C compiler's layout."""
+    fields = [f for f, _ in binding.MoeConfig._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"moe.h\"\nint main(void){\n"
+                   f'printf("%zu\\n", sizeof(moe_config));\n'
+                   + "".join(f'printf("%zu\\n", offsetof(moe_config, {f}));\n' for f in fields)
+                   + "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                    str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(binding.MoeConfig)
+    assert got[1:] == [getattr(binding.MoeConfig, f).offset for f in fields]
+
+
+def test_status_strings(lib):
+    for s, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported configuration"),
+                    (3, "workspace too small"), (4, "HIP launch failed")]:
+        assert binding.status_string(s) == text
+
+
+def _cfg(**kw):
+    base = dict(T=8, d=256, d_ff=512, E=8, k=2, act_dtype=moe.BF16, w_dtype=moe.BF16)
+    base.update(kw)
+    c = moe.config(base["T"], base["d"], base["d_ff"], base["E"], base["k"], base["act_dtype"], base["w_dtype"])
+    for key in ("tau", "use_gumbel", "gemm_path", "reserved"):
+        if key in kw:
+            setattr(c, key, kw[key])
+    return c
+
+
+BAD = [
+    dict(T=-1), dict(T=(1 << 24) + 1), dict(E=0), dict(E=257), dict(k=0), dict(k=9, E=16), dict(k=5, E=4),
+    dict(d=100), dict(d_ff=96), dict(d=0), dict(d=1 << 18), dict(tau=0.0), dict(tau=-1.0), dict(tau=float("nan")),
+    dict(tau=float("inf")), dict(use_gumbel=2), dict(gemm_path=3), dict(reserved=1), dict(act_dtype=2),
+    dict(w_dtype=3), dict(w_dtype=moe.INT4_G128, d=192), dict(w_dtype=moe.INT4_G128, d_ff=320),
+]
+
+
+@pytest.mark.parametrize("kw", BAD, ids=[str(b) for b in BAD])
+def test_invalid_config_rejected(lib, kw):
+    n = ctypes.c_size_t(12345)
+    assert lib.moe_workspace_size(ctypes.byref(_cfg(**kw)), ctypes.byref(n)) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert n.value == 12345
+
+
+def test_unsupported_pairings(lib):
+    n = ctypes.c_size_t()
+    for a, w in [(moe.F32, moe.BF16), (moe.BF16, moe.F32), (moe.F32, moe.INT4_G128)]:
+        assert lib.moe_workspace_size(ctypes.byref(_cfg(act_dtype=a, w_dtype=w)), ctypes.byref(n)) == \
+            binding.MOE_ERR_UNSUPPORTED
+
+
+def test_workspace_size_accounts_for_buffers(lib):
+    n = ctypes.c_size_t()
+    c = _cfg(T=4096, d=4096, d_ff=16384, E=16)
+    assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == 0
+    Tk = 4096 * 2
+    assert n.value >= Tk * 16384 * 2 + Tk * 4096 * 4 + 2 * Tk * 4 + 17 * 4
+    assert n.value % 256 == 0
+    assert lib.moe_workspace_size(ctypes.byref(_cfg(T=0)), ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.moe_workspace_size(ctypes.byref(c), None) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_workspace_size(None, ctypes.byref(n)) == binding.MOE_ERR_INVALID_ARGUMENT
+
+
+def _forward(lib, c, **ptr):
+    P = ctypes.c_void_p
+    a = dict(x=0x10000, Wg=0x20000, bias=None, W1=0x30000, S1=None, s1=c.d * c.d_ff * 2, W2=0x40000, S2=None,
+             s2=c.d * c.d_ff * 2, y=0x50000, ids=0x60000, gates=0x70000, counts=0x80000, ws=0x90000, wsb=1 << 40)
+    a.update(ptr)
+    return lib.moe_forward(ctypes.byref(c), P(a["x"]), P(a["Wg"]), P(a["bias"]), P(a["W1"]), P(a["S1"]), a["s1"],
+                           P(a["W2"]), P(a["S2"]), a["s2"], P(a["y"]), P(a["ids"]), P(a["gates"]), P(a["counts"]),
+                           P(a["ws"]), a["wsb"], P(0))
+
+
+@pytest.mark.parametrize("bad", [dict(x=None), dict(x=0x10008), dict(Wg=None), dict(y=0x50004), dict(ids=None),
+                                 dict(gates=0x70002), dict(counts=None), dict(W1=None), dict(W2=0x40001),
+                                 dict(s1=100), dict(s2=256 * 512 * 2 + 8), dict(ws=None), dict(ws=0x90010),
+                                 dict(bias=0x1002)])
+def test_forward_rejects_bad_pointers(lib, bad):
+    assert _forward(lib, _cfg(), **bad) == binding.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_forward_rejects_small_workspace(lib):
+    assert _forward(lib, _cfg(), wsb=1024) == binding.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_int4_needs_scales(lib):
+    c = _cfg(w_dtype=moe.INT4_G128)
+    assert _forward(lib, c, s1=256 * 512 // 2, s2=256 * 512 // 2) == binding.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_stage_entry_points_check_arguments(lib):
+    P = ctypes.c_void_p
+    c = _cfg()
+    assert lib.moe_router(ctypes.byref(c), P(0), P(0x1000), None, P(0x2000), P(0x3000), P(0x4000), 1 << 30,
+                          P(0)) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_router(ctypes.byref(c), P(0x1000), P(0x1000), None, P(0x2000), P(0x3000), P(0x4000), 16,
+                          P(0)) == binding.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert lib.moe_permute(ctypes.byref(c), P(0x1000), None, P(0x2000), P(0x3000), P(0x4000),
+                           P(0)) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_grouped_gemm(ctypes.byref(c), 3, P(0x1000), P(0x1000), P(0x1000), P(0x1000), None, 1 << 20,
+                                P(0x1000), P(0)) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_grouped_gemm(ctypes.byref(c), 1, P(0x1000), None, P(0x1000), P(0x1000), None, 1 << 20,
+                                P(0x1000), P(0)) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_combine(ctypes.byref(c), P(0x1000), P(0x1000), P(0x1000), P(0x1001),
+                           P(0)) == binding.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_workloads_are_valid_configs(lib):
+    n = ctypes.c_size_t()
+    for name in moe_synth.WORKLOADS:
+        w = moe_synth.workload(name)
+        c = moe.config(w["T"], w["d"], w["d_ff"], w["E"], w["k"], w["act"], w["w"], tau=w["tau"],
+                       use_gumbel=w["gumbel"])
+        assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == 0, name
