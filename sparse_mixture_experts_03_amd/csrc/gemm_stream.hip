@@ -5,9 +5,13 @@
 // weights never stay in cache).  This kernel therefore reads every weight of
 // every active expert exactly once per 16 routed tokens and does the
 // arithmetic on MFMA so that the matrix cores never limit the stream:
-//   workgroup = 32 weight rows x one 16-row tile of the dispatch order;
-//   its four wavefronts split K, each streaming 16-byte row segments straight
-//   from HBM into MFMA operands (no LDS staging: nothing is reused);
+//   workgroup = 16*NB weight rows x one 16-row tile of the dispatch order;
+//   its four wavefronts split K; each streams its rows in stages of 256 or 512
+//   bytes per row with fully coalesced non-temporal 16-byte loads (a wavefront
+//   instruction reads whole 128-byte lines), parks the stage in a private
+//   padded LDS buffer while the next stage is in flight, and reads it back in
+//   MFMA operand layout (the MFMA row layout would otherwise split every line
+//   over two instructions);
 //   the four partial tiles are summed in LDS in a fixed order (deterministic).
 // MFMA operand roles are swapped (weights are the 16-row "A" side, tokens the
 // "B" side) so each lane ends with four consecutive output features of one
@@ -22,21 +26,48 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#ifndef MOE_STREAM_NB_BF16
+#define MOE_STREAM_NB_BF16 1   // 16-row weight tiles per workgroup, bf16 experts
+#endif
+#ifndef MOE_STREAM_NB_INT4
+#define MOE_STREAM_NB_INT4 2   // 16-row weight tiles per workgroup, INT4 experts
+#endif
+#ifndef MOE_STREAM_STAGE_BF16
+#define MOE_STREAM_STAGE_BF16 256  // bytes of each weight row per pipeline stage, bf16 experts
+#endif
+#ifndef MOE_STREAM_STAGE_INT4
+#define MOE_STREAM_STAGE_INT4 512  // bytes of each weight row per pipeline stage, INT4 experts
+#endif
+#ifndef MOE_STREAM_NT
+#define MOE_STREAM_NT 1        // 1: non-temporal hint on weight loads
+#endif
+
 namespace moe {
 
 namespace {
 
-constexpr int kStreamRows = 32;  // weight rows per workgroup (two 16-row MFMA tiles)
-constexpr int kStreamBM = 16;    // dispatch rows per tile
+constexpr int kStreamBM = 16;  // dispatch rows per tile
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Weight loads: read once, never reused.
+__device__ __forceinline__ uint4 ldw16(const void* p) {
+#if MOE_STREAM_NT
+    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+#else
+    return ld16(p);
+#endif
+}
 
 // Eight signed INT4 codes (one 32-bit word, code i in bits 4i..4i+3) to eight
 // bf16 values 136 + q_i, as one MFMA operand.
 __device__ __forceinline__ bf16x8 int4x8_to_bf16_offset136(uint32_t w) {
-    uint32_t v = w ^ 0x88888888u;                 // q + 8, offset binary
-    uint32_t lo = v & 0x0f0f0f0fu;                 // codes 0,2,4,6 in byte 0..3
-    uint32_t hi = (v >> 4) & 0x0f0f0f0fu;          // codes 1,3,5,7
+    const uint32_t v = w ^ 0x88888888u;          // q + 8, offset binary
+    const uint32_t lo = v & 0x0f0f0f0fu;         // codes 0,2,4,6 in bytes 0..3
+    const uint32_t hi = (v >> 4) & 0x0f0f0f0fu;  // codes 1,3,5,7
     uint4 r;
     // dword p = bf16(128 + c[2p]) | bf16(128 + c[2p+1]) << 16 ; bf16(128 + c) = 0x4300 | c
     r.x = __builtin_amdgcn_perm(hi, lo, 0x0c040c00u) | 0x43004300u;
@@ -62,13 +93,18 @@ __device__ __forceinline__ void store_tile(void* out, int64_t N, int p0, int row
     }
 }
 
-template <int WQ, int WHICH>
+template <int WQ, int WHICH, int NB, int kStageBytes>
 __global__ void __launch_bounds__(256)
 gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
                    const int32_t* __restrict__ offsets, int E, const uint8_t* __restrict__ W,
                    const uint16_t* __restrict__ Wsc, int64_t W_stride, void* __restrict__ out, int N, int K,
                    int ntiles_n) {
-    __shared__ f32x4 red[3][2][64];
+    constexpr int ROWS = 16 * NB;              // weight rows per workgroup
+    constexpr int SEGS = kStageBytes / 16;     // 16-byte segments per row per stage
+    constexpr int LROW = kStageBytes + 16;     // padded LDS row (conflict-free 16-row column reads)
+    constexpr int LOADS = ROWS * SEGS / 64;    // 16-byte loads per lane per stage
+    __shared__ __attribute__((aligned(16))) uint8_t stage_lds[4][ROWS * LROW];
+    __shared__ f32x4 red[3][NB][64];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int mt = blockIdx.x / ntiles_n;
@@ -78,115 +114,134 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
 
     const int r = lane & 15;
     const int g = lane >> 4;
-    const int n0 = nt * kStreamRows;
+    const int n0 = nt * ROWS;
     const bool mvalid = r < rows;
     int64_t arow = 0;
     if (mvalid) arow = (WHICH == 1) ? (int64_t)a_rows[p0 + r] : (int64_t)(p0 + r);
     const uint16_t* xrow = A + arow * K;
-    const uint8_t* Wexp = W + (int64_t)e * W_stride;
+    const int64_t row_bytes = (WQ == kBF16) ? (int64_t)K * 2 : (int64_t)K / 2;
+    const uint8_t* Wblk = W + (int64_t)e * W_stride + (int64_t)n0 * row_bytes;
+    uint8_t* lds = stage_lds[wave];
     const uint4 zero4 = make_uint4(0, 0, 0, 0);
 
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    // This wavefront's stages (kStageBytes of every row each) of the K range.
+    const int nstages = (int)((row_bytes + kStageBytes - 1) / kStageBytes);
+    const int st0 = wave * nstages / 4, st1 = (wave + 1) * nstages / 4;
 
-    if constexpr (WQ == kBF16) {
-        // chunk = 64 columns; lane group g covers columns [16g, 16g+16) of it
-        const int nchunks = K / 64;
-        const int c0 = wave * nchunks / 4, c1 = (wave + 1) * nchunks / 4;
-        const uint16_t* w0 = reinterpret_cast<const uint16_t*>(Wexp) + (int64_t)(n0 + r) * K + 16 * g;
-        const uint16_t* w1 = w0 + (int64_t)16 * K;
-        const uint16_t* xg = xrow + 16 * g;
-        int c = c0;
-        for (; c + 4 <= c1; c += 4) {
-            uint4 wa[4][2], wb[4][2], xv[4][2];
+    // coalesced loads: instruction i, lane L -> row (64i + L) / SEGS, segment (64i + L) % SEGS
+    auto gload = [&](int st, uint4 (&buf)[LOADS]) {
+        const int64_t s0 = (int64_t)st * kStageBytes;
+        const int64_t valid = min((int64_t)kStageBytes, row_bytes - s0);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int kb = (c + u) * 64;
-                wa[u][0] = ld16(w0 + kb);
-                wa[u][1] = ld16(w0 + kb + 8);
-                wb[u][0] = ld16(w1 + kb);
-                wb[u][1] = ld16(w1 + kb + 8);
-                xv[u][0] = mvalid ? ld16(xg + kb) : zero4;
-                xv[u][1] = mvalid ? ld16(xg + kb + 8) : zero4;
-            }
+        for (int i = 0; i < LOADS; ++i) {
+            const int flat = 64 * i + lane;
+            const int row = flat / SEGS, seg = flat % SEGS;
+            buf[i] = (seg * 16 < valid) ? ldw16(Wblk + (int64_t)row * row_bytes + s0 + seg * 16) : zero4;
+        }
+    };
+    auto lstore = [&](const uint4 (&buf)[LOADS]) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+        for (int i = 0; i < LOADS; ++i) {
+            const int flat = 64 * i + lane;
+            const int row = flat / SEGS, seg = flat % SEGS;
+            *reinterpret_cast<uint4*>(lds + row * LROW + seg * 16) = buf[i];
+        }
+    };
+
+    f32x4 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    // INT4 scales: this lane's output rows n0 + 16b + 4g + i
+    const int groups = K / 128;
+    const uint16_t* sc = (WQ == kINT4) ? Wsc + (int64_t)e * N * groups + (int64_t)(n0 + 4 * g) * groups : nullptr;
+    const uint4 ones = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
+
+    uint4 cur[LOADS], nxt[LOADS];
+    if (st0 < st1) gload(st0, cur);
+    for (int st = st0; st < st1; ++st) {
+        if (st + 1 < st1) gload(st + 1, nxt);
+        lstore(cur);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        const int64_t s0 = (int64_t)st * kStageBytes;
+        const int valid = (int)min((int64_t)kStageBytes, row_bytes - s0);
+        if constexpr (WQ == kBF16) {
+            // 64-column chunks (128 bytes per row); lane group g takes segments 2g, 2g+1
+            const int kbase = (int)(s0 / 2);
+            for (int cc = 0; cc < valid / 128; ++cc) {
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    acc0 = mfma16x16x32(as_bf16x8(wa[u][s]), as_bf16x8(xv[u][s]), acc0);
-                    acc1 = mfma16x16x32(as_bf16x8(wb[u][s]), as_bf16x8(xv[u][s]), acc1);
+                    const int koff = cc * 64 + (2 * g + s) * 8;
+                    const uint4 xa = mvalid ? ld16(xrow + kbase + koff) : zero4;
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        const uint4 wa =
+                            *reinterpret_cast<const uint4*>(lds + (16 * b + r) * LROW + cc * 128 + (2 * g + s) * 16);
+                        acc[b] = mfma16x16x32(as_bf16x8(wa), as_bf16x8(xa), acc[b]);
+                    }
                 }
             }
-        }
-        for (; c < c1; ++c) {
-            const int kb = c * 64;
+        } else {
+            // one 128-column scale group per 64 bytes of each row; lane group g takes columns [32g, 32g+32)
+            const int gbase = (int)(s0 / 64);
+            for (int cc = 0; cc < valid / 64; ++cc) {
+                const int grp = gbase + cc;
+                uint4 xv[4];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                uint4 xa = mvalid ? ld16(xg + kb + 8 * s) : zero4;
-                acc0 = mfma16x16x32(as_bf16x8(ld16(w0 + kb + 8 * s)), as_bf16x8(xa), acc0);
-                acc1 = mfma16x16x32(as_bf16x8(ld16(w1 + kb + 8 * s)), as_bf16x8(xa), acc1);
+                for (int s = 0; s < 4; ++s) xv[s] = mvalid ? ld16(xrow + grp * 128 + 32 * g + 8 * s) : zero4;
+                f32x4 t[NB], sx = (f32x4){0.f, 0.f, 0.f, 0.f};
+                uint4 q[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    t[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                    q[b] = *reinterpret_cast<const uint4*>(lds + (16 * b + r) * LROW + cc * 64 + 16 * g);
+                }
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const bf16x8 xb = as_bf16x8(xv[s]);
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        const uint32_t word = s == 0 ? q[b].x : s == 1 ? q[b].y : s == 2 ? q[b].z : q[b].w;
+                        t[b] = mfma16x16x32(int4x8_to_bf16_offset136(word), xb, t[b]);
+                    }
+                    sx = mfma16x16x32(as_bf16x8(ones), xb, sx);
+                }
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float sv = bf16_bits_to_float(sc[(int64_t)(16 * b + i) * groups + grp]);
+                        acc[b][i] = fmaf(sv, fmaf(-136.0f, sx[i], t[b][i]), acc[b][i]);
+                    }
             }
         }
-    } else {
-        // chunk = one 128-column scale group; lane group g covers columns [32g, 32g+32)
-        const int nchunks = K / 128;
-        const int c0 = wave * nchunks / 4, c1 = (wave + 1) * nchunks / 4;
-        const int64_t row_bytes = K / 2;
-        const uint8_t* w0 = Wexp + (int64_t)(n0 + r) * row_bytes + 16 * g;
-        const uint8_t* w1 = w0 + 16 * row_bytes;
-        const uint16_t* xg = xrow + 32 * g;
-        // scales of this lane's four output rows (4 * (lane/16) + i) in both tiles
-        const int groups = K / 128;
-        const uint16_t* sc = Wsc + (int64_t)e * N * groups + (int64_t)(n0 + 4 * g) * groups;
-        const uint4 ones = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
-        for (int c = c0; c < c1; ++c) {
-            uint4 q0 = ld16(w0 + (int64_t)c * 64);
-            uint4 q1 = ld16(w1 + (int64_t)c * 64);
-            uint4 xv[4];
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
-            for (int s = 0; s < 4; ++s) xv[s] = mvalid ? ld16(xg + c * 128 + 8 * s) : zero4;
-            f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0, sx = t0;
-            const uint32_t qa[4] = {q0.x, q0.y, q0.z, q0.w};
-            const uint32_t qb[4] = {q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                bf16x8 xb = as_bf16x8(xv[s]);
-                t0 = mfma16x16x32(int4x8_to_bf16_offset136(qa[s]), xb, t0);
-                t1 = mfma16x16x32(int4x8_to_bf16_offset136(qb[s]), xb, t1);
-                sx = mfma16x16x32(as_bf16x8(ones), xb, sx);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float s0 = bf16_bits_to_float(sc[(int64_t)i * groups + c]);
-                float s1 = bf16_bits_to_float(sc[(int64_t)(16 + i) * groups + c]);
-                acc0[i] = fmaf(s0, fmaf(-136.0f, sx[i], t0[i]), acc0[i]);
-                acc1[i] = fmaf(s1, fmaf(-136.0f, sx[i], t1[i]), acc1[i]);
-            }
-        }
+        for (int i = 0; i < LOADS; ++i) cur[i] = nxt[i];
     }
 
     // fixed-order reduction of the four K-slices
     if (wave > 0) {
-        red[wave - 1][0][lane] = acc0;
-        red[wave - 1][1][lane] = acc1;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) red[wave - 1][b][lane] = acc[b];
     }
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
-        for (int v = 0; v < 3; ++v) {
-            acc0 += red[v][0][lane];
-            acc1 += red[v][1][lane];
+        for (int b = 0; b < NB; ++b) {
+            f32x4 v = acc[b];
+#pragma unroll
+            for (int w = 0; w < 3; ++w) v += red[w][b][lane];
+            store_tile<WHICH>(out, N, p0, rows, n0 + 16 * b, v, lane);
         }
-        store_tile<WHICH>(out, N, p0, rows, n0, acc0, lane);
-        store_tile<WHICH>(out, N, p0, rows, n0 + 16, acc1, lane);
     }
 }
 
-}  // namespace
-
-hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream) {
+template <int WQ, int NB, int SB>
+hipError_t launch_stream_nb(const GemmArgs& a, hipStream_t stream) {
     const int64_t Tk = a.T * a.k;
     const int64_t max_mtiles = Tk / kStreamBM + (Tk < a.E ? Tk : a.E);
-    const int ntiles_n = (int)(a.N / kStreamRows);
+    const int ntiles_n = (int)(a.N / (16 * NB));
     const int64_t blocks = max_mtiles * ntiles_n;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
@@ -194,22 +249,21 @@ hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream) {
     const uint8_t* W = static_cast<const uint8_t*>(a.W);
     const uint16_t* S = static_cast<const uint16_t*>(a.W_scales);
     dim3 grid((unsigned)blocks), block(256);
-    if (a.w_dtype == kBF16) {
-        if (a.which == 1)
-            hipLaunchKernelGGL((gemm_stream_kernel<kBF16, 1>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
-                               S, a.W_stride, a.out, (int)a.N, (int)a.K, ntiles_n);
-        else
-            hipLaunchKernelGGL((gemm_stream_kernel<kBF16, 2>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
-                               S, a.W_stride, a.out, (int)a.N, (int)a.K, ntiles_n);
-    } else {
-        if (a.which == 1)
-            hipLaunchKernelGGL((gemm_stream_kernel<kINT4, 1>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
-                               S, a.W_stride, a.out, (int)a.N, (int)a.K, ntiles_n);
-        else
-            hipLaunchKernelGGL((gemm_stream_kernel<kINT4, 2>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
-                               S, a.W_stride, a.out, (int)a.N, (int)a.K, ntiles_n);
-    }
+    if (a.which == 1)
+        hipLaunchKernelGGL((gemm_stream_kernel<WQ, 1, NB, SB>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W, S,
+                           a.W_stride, a.out, (int)a.N, (int)a.K, ntiles_n);
+    else
+        hipLaunchKernelGGL((gemm_stream_kernel<WQ, 2, NB, SB>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W, S,
+                           a.W_stride, a.out, (int)a.N, (int)a.K, ntiles_n);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream) {
+    // N is a multiple of 64, so any NB in {1, 2, 4} tiles it exactly.
+    if (a.w_dtype == kBF16) return launch_stream_nb<kBF16, MOE_STREAM_NB_BF16, MOE_STREAM_STAGE_BF16>(a, stream);
+    return launch_stream_nb<kINT4, MOE_STREAM_NB_INT4, MOE_STREAM_STAGE_INT4>(a, stream);
 }
 
 }  // namespace moe

@@ -9,10 +9,11 @@ namespace moe {
 
 // ---------------------------------------------------------------- router
 struct RouterPlan {
-    int tokens_per_tile;   // tokens per partial-logit workgroup (TT * E <= 1024)
+    int tokens_per_tile;   // tokens per partial-logit workgroup
     int tiles;             // token tiles
-    int chunks_per_split;  // 32-column chunks of the input dimension per split
-    int splits;            // workgroups along the input dimension
+    int expert_groups;     // power of two >= E / 8: 8-expert groups per Wg row
+    int rows_per_split;    // input rows (of d) per split
+    int splits;            // workgroups along the input dimension (<= 64)
     size_t partial_bytes;  // binary64 partial logits [splits][T][E]
 };
 RouterPlan router_plan(int64_t T, int64_t d, int E);

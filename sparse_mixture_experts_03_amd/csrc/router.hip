@@ -20,8 +20,41 @@ namespace moe {
 namespace {
 
 constexpr int kRouterThreads = 256;
-constexpr int kRouterKC = 32;          // input columns staged per step (LDS <= 33 KB at E = 256)
-constexpr int kRouterPairsPerThread = 4;  // (token, expert) pairs per thread: TT*E <= 1024
+constexpr int kTT = 8;           // tokens per partial-logit workgroup
+constexpr int kRowChunk = 256;   // input rows staged in LDS per step
+constexpr int kMaxSplits = 64;
+
+// Eight consecutive experts of one Wg row (Wg is d x E row-major), as floats.
+// Vector loads when every row holds whole groups of eight (E % 8 == 0).
+template <int ACT>
+__device__ __forceinline__ void load_wg8(const void* Wg, int64_t row, int E, int e0, bool vec, float w[8]) {
+    if constexpr (ACT == kBF16) {
+        const uint16_t* p = static_cast<const uint16_t*>(Wg) + row * E + e0;
+        if (vec) {
+            uint4 v = *reinterpret_cast<const uint4*>(p);
+            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                w[2 * j] = __uint_as_float(u[j] << 16);
+                w[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w[j] = (e0 + j < E) ? bf16_bits_to_float(p[j]) : 0.0f;
+        }
+    } else {
+        const float* p = static_cast<const float*>(Wg) + row * E + e0;
+        if (vec) {
+            float4 a = *reinterpret_cast<const float4*>(p);
+            float4 b = *reinterpret_cast<const float4*>(p + 4);
+            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+            w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w[j] = (e0 + j < E) ? p[j] : 0.0f;
+        }
+    }
+}
 
 template <int ACT>
 __device__ __forceinline__ float load_act(const void* p, int64_t i) {
@@ -32,61 +65,79 @@ __device__ __forceinline__ float load_act(const void* p, int64_t i) {
     }
 }
 
-// Partial logits over one slice of the input dimension.
+// Partial logits of an 8-token tile over one slice of the input dimension.
+// Thread (eg, rl): expert group eg (8 consecutive experts) and row lane rl;
+// it accumulates 8 tokens x 8 experts in binary64 over rows k = rl (mod RL).
+// Row lanes are then reduced with a fixed butterfly inside each wavefront and
+// a fixed-order sum over the four wavefronts.
 // grid = (token tiles, splits); partial is [splits][T][E] binary64.
 template <int ACT>
 __global__ void __launch_bounds__(kRouterThreads)
-router_partial_kernel(const void* __restrict__ x, const void* __restrict__ Wg, int T, int d, int E,
-                      int TT, int chunks_per_split, double* __restrict__ partial) {
-    extern __shared__ float smem[];
-    const int xs_stride = kRouterKC + 1;
-    float* xs = smem;                      // [TT][KC+1]
-    float* ws = smem + TT * xs_stride;     // [KC][E]
+router_partial_kernel(const void* __restrict__ x, const void* __restrict__ Wg, int T, int d, int E, int egp,
+                      int rows_per_split, double* __restrict__ partial) {
+    __shared__ float xs[kRowChunk][kTT];      // staged x slice, token fastest
+    __shared__ double red[4][32][kTT * 8];    // per-wave sums, 64 KB
     const int tid = threadIdx.x;
-    const int t0 = blockIdx.x * TT;
-    const int split = blockIdx.y;
-    const int k_begin = split * chunks_per_split * kRouterKC;
-    const int k_end = min(d, k_begin + chunks_per_split * kRouterKC);
-    const int npairs = TT * E;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int eg = tid & (egp - 1);
+    const int rl = tid / egp;
+    const int RL = kRouterThreads / egp;
+    const int e0 = eg * 8;
+    const bool active = e0 < E;
+    const bool vec = E % 8 == 0;
+    const int t0 = blockIdx.x * kTT;
+    const int k_begin = blockIdx.y * rows_per_split;
+    const int k_end = min(d, k_begin + rows_per_split);
 
-    double acc[kRouterPairsPerThread];
+    double acc[kTT][8];
 #pragma unroll
-    for (int j = 0; j < kRouterPairsPerThread; ++j) acc[j] = 0.0;
+    for (int t = 0; t < kTT; ++t)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[t][j] = 0.0;
 
-    for (int kc = k_begin; kc < k_end; kc += kRouterKC) {
-        for (int i = tid; i < TT * kRouterKC; i += kRouterThreads) {
-            int tt = i / kRouterKC, kk = i % kRouterKC;
-            int t = t0 + tt, kx = kc + kk;
-            xs[tt * xs_stride + kk] = (t < T && kx < k_end) ? load_act<ACT>(x, (int64_t)t * d + kx) : 0.0f;
-        }
-        for (int i = tid; i < kRouterKC * E; i += kRouterThreads) {
-            int kk = i / E, e = i % E;
-            int kx = kc + kk;
-            ws[i] = (kx < k_end) ? load_act<ACT>(Wg, (int64_t)kx * E + e) : 0.0f;
+    for (int kc = k_begin; kc < k_end; kc += kRowChunk) {
+        const int rows = min(kRowChunk, k_end - kc);
+        for (int i = tid; i < kRowChunk * kTT; i += kRouterThreads) {
+            const int t = i / kRowChunk, kk = i % kRowChunk;
+            xs[kk][t] = (t0 + t < T && kk < rows) ? load_act<ACT>(x, (int64_t)(t0 + t) * d + kc + kk) : 0.0f;
         }
         __syncthreads();
+        if (active) {
+            for (int kk = rl; kk < rows; kk += RL) {
+                float w[8];
+                load_wg8<ACT>(Wg, kc + kk, E, e0, vec, w);
+                const float4 xa = *reinterpret_cast<const float4*>(&xs[kk][0]);
+                const float4 xb = *reinterpret_cast<const float4*>(&xs[kk][4]);
+                const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
-        for (int j = 0; j < kRouterPairsPerThread; ++j) {
-            int p = tid + j * kRouterThreads;
-            if (p < npairs) {
-                int tt = p / E, e = p % E;
-                const float* xr = xs + tt * xs_stride;
-                double a = acc[j];
-                for (int kk = 0; kk < kRouterKC; ++kk)
-                    a = fma((double)xr[kk], (double)ws[kk * E + e], a);
-                acc[j] = a;
+                for (int t = 0; t < kTT; ++t)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) acc[t][j] = fma((double)xv[t], (double)w[j], acc[t][j]);
             }
         }
         __syncthreads();
     }
+    // butterfly over the row-lane bits of the lane index
+    for (int off = egp; off < 64; off <<= 1) {
 #pragma unroll
-    for (int j = 0; j < kRouterPairsPerThread; ++j) {
-        int p = tid + j * kRouterThreads;
-        if (p < npairs) {
-            int tt = p / E, e = p % E;
-            int t = t0 + tt;
-            if (t < T) partial[((int64_t)split * T + t) * E + e] = acc[j];
-        }
+        for (int t = 0; t < kTT; ++t)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[t][j] += __shfl_xor(acc[t][j], off, 64);
+    }
+    if (lane < egp) {
+#pragma unroll
+        for (int t = 0; t < kTT; ++t)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) red[wave][lane][t * 8 + j] = acc[t][j];
+    }
+    __syncthreads();
+    for (int i = tid; i < kTT * E; i += kRouterThreads) {
+        const int t = i / E, e = i % E;
+        if (t0 + t >= T) continue;
+        const int g = e / 8, j = e % 8;
+        const double v = ((red[0][g][t * 8 + j] + red[1][g][t * 8 + j]) + red[2][g][t * 8 + j]) + red[3][g][t * 8 + j];
+        partial[((int64_t)blockIdx.y * T + t0 + t) * E + e] = v;
     }
 }
 
@@ -117,7 +168,7 @@ __device__ __forceinline__ double gumbel_draw(uint64_t seed, uint64_t token, uin
 }
 
 // Is (za, ea) ranked before (zb, eb)?  Larger z first, NaN last, ties to the
-// lower expert index.  Invalid slots carry e = INT_MAX and never win.
+// lower expert index.
 __device__ __forceinline__ bool ranks_before(double za, int ea, double zb, int eb) {
     bool na = isnan(za), nb = isnan(zb);
     if (na != nb) return nb;
@@ -127,29 +178,42 @@ __device__ __forceinline__ bool ranks_before(double za, int ea, double zb, int e
 
 constexpr int kNoExpert = 0x7fffffff;
 
-// One wavefront per token: sum the partial logits in split order, add bias
-// and noise, apply the temperature, pick the top-k, and form the softmax gates.
+// One workgroup per token.  Thread e sums the split partials of expert e (all
+// loads issued before the adds, summed in split order), adds bias and noise
+// and applies the temperature; wavefront 0 then picks the top-k and forms the
+// softmax gates from the E values in LDS.
 __global__ void __launch_bounds__(256)
 router_finalize_kernel(const double* __restrict__ partial, int nsplit, int T, int E, int k,
                        const float* __restrict__ bias, double tau, int use_gumbel, uint64_t seed,
                        uint64_t token_offset, int32_t* __restrict__ ids, float* __restrict__ gates) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
+    __shared__ double zs[256];
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (tid < E) {
+        const double* src = partial + (int64_t)t * E + tid;
+        const int64_t step = (int64_t)T * E;
+        double v[kMaxSplits];
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s)
+            if (s < nsplit) v[s] = src[s * step];
+        double l = 0.0;
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s)
+            if (s < nsplit) l += v[s];
+        if (bias) l += (double)bias[tid];
+        const double g = use_gumbel ? gumbel_draw(seed, token_offset + (uint64_t)t, (uint64_t)tid) : 0.0;
+        zs[tid] = (l + g) / tau;
+    }
+    __syncthreads();
+    if (tid >= 64) return;
+    const int lane = tid;
     double z[4];
     bool live[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        int e = lane + 64 * j;
+        const int e = lane + 64 * j;
         live[j] = e < E;
-        z[j] = 0.0;
-        if (live[j]) {
-            double l = 0.0;
-            for (int s = 0; s < nsplit; ++s) l += partial[((int64_t)s * T + t) * E + e];
-            if (bias) l += (double)bias[e];
-            double g = use_gumbel ? gumbel_draw(seed, token_offset + (uint64_t)t, (uint64_t)e) : 0.0;
-            z[j] = (l + g) / tau;
-        }
+        z[j] = live[j] ? zs[e] : 0.0;
     }
     // softmax denominator over all experts (max-subtracted)
     double m = -INFINITY;
@@ -174,15 +238,15 @@ router_finalize_kernel(const double* __restrict__ partial, int nsplit, int T, in
         int be = kNoExpert;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            int e = lane + 64 * j;
+            const int e = lane + 64 * j;
             if (live[j] && !taken[j] && (be == kNoExpert || ranks_before(z[j], e, bz, be))) {
                 bz = z[j];
                 be = e;
             }
         }
         for (int off = 32; off >= 1; off >>= 1) {
-            double oz = __shfl_xor(bz, off, 64);
-            int oe = __shfl_xor(be, off, 64);
+            const double oz = __shfl_xor(bz, off, 64);
+            const int oe = __shfl_xor(be, off, 64);
             if (oe != kNoExpert && (be == kNoExpert || ranks_before(oz, oe, bz, be))) {
                 bz = oz;
                 be = oe;
@@ -193,7 +257,7 @@ router_finalize_kernel(const double* __restrict__ partial, int nsplit, int T, in
             if (lane + 64 * j == be) taken[j] = true;
         if (lane == 0) {
             ids[(int64_t)t * k + r] = be;
-            double p = any_nan ? (double)NAN : exp(bz - m) / s;
+            const double p = any_nan ? (double)NAN : exp(bz - m) / s;
             gates[(int64_t)t * k + r] = (float)p;
         }
     }
@@ -203,38 +267,41 @@ router_finalize_kernel(const double* __restrict__ partial, int nsplit, int T, in
 
 RouterPlan router_plan(int64_t T, int64_t d, int E) {
     RouterPlan p;
-    int tt = 1024 / E;
-    if (tt > 64) tt = 64;
-    if (tt < 1) tt = 1;
-    p.tokens_per_tile = tt;
-    p.tiles = (int)((T + tt - 1) / tt);
-    int nchunks = (int)((d + kRouterKC - 1) / kRouterKC);
-    int want = p.tiles > 0 ? (512 + p.tiles - 1) / p.tiles : 1;
-    if (want < 1) want = 1;
+    p.tokens_per_tile = kTT;
+    p.tiles = (int)((T + kTT - 1) / kTT);
+    int egp = 1;
+    while (egp * 8 < E) egp <<= 1;
+    p.expert_groups = egp;
+    // Enough workgroups to spread the d x E gating matrix over the chip
+    // (~256), each split at least one 256-row chunk, at most 64 splits.
+    const int nchunks = (int)((d + kRowChunk - 1) / kRowChunk);
+    int want = p.tiles > 0 ? (256 + p.tiles - 1) / p.tiles : 1;
     if (want > nchunks) want = nchunks;
-    p.chunks_per_split = (nchunks + want - 1) / want;
-    p.splits = (nchunks + p.chunks_per_split - 1) / p.chunks_per_split;
+    if (want > kMaxSplits) want = kMaxSplits;
+    if (want < 1) want = 1;
+    const int chunks_per_split = (nchunks + want - 1) / want;
+    p.rows_per_split = chunks_per_split * kRowChunk;
+    p.splits = (nchunks + chunks_per_split - 1) / chunks_per_split;
     p.partial_bytes = (size_t)p.splits * (size_t)T * (size_t)E * sizeof(double);
     return p;
 }
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t stream) {
     if (a.T == 0) return hipSuccess;
-    RouterPlan p = router_plan(a.T, a.d, a.E);
+    const RouterPlan p = router_plan(a.T, a.d, a.E);
     dim3 grid1(p.tiles, p.splits);
-    size_t lds = sizeof(float) * ((size_t)p.tokens_per_tile * (kRouterKC + 1) + (size_t)kRouterKC * a.E);
     if (a.act_dtype == kF32) {
-        hipLaunchKernelGGL(router_partial_kernel<kF32>, grid1, dim3(kRouterThreads), lds, stream, a.x, a.Wg,
-                           (int)a.T, (int)a.d, a.E, p.tokens_per_tile, p.chunks_per_split, a.partial);
+        hipLaunchKernelGGL(router_partial_kernel<kF32>, grid1, dim3(kRouterThreads), 0, stream, a.x, a.Wg, (int)a.T,
+                           (int)a.d, a.E, p.expert_groups, p.rows_per_split, a.partial);
     } else {
-        hipLaunchKernelGGL(router_partial_kernel<kBF16>, grid1, dim3(kRouterThreads), lds, stream, a.x, a.Wg,
-                           (int)a.T, (int)a.d, a.E, p.tokens_per_tile, p.chunks_per_split, a.partial);
+        hipLaunchKernelGGL(router_partial_kernel<kBF16>, grid1, dim3(kRouterThreads), 0, stream, a.x, a.Wg,
+                           (int)a.T, (int)a.d, a.E, p.expert_groups, p.rows_per_split, a.partial);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    dim3 grid2((unsigned)((a.T + 3) / 4));
-    hipLaunchKernelGGL(router_finalize_kernel, grid2, dim3(256), 0, stream, a.partial, p.splits, (int)a.T, a.E,
-                       a.k, a.bias, (double)a.tau, a.use_gumbel, a.seed, a.token_offset, a.ids, a.gates);
+    hipLaunchKernelGGL(router_finalize_kernel, dim3((unsigned)a.T), dim3(256), 0, stream, a.partial, p.splits,
+                       (int)a.T, a.E, a.k, a.bias, (double)a.tau, a.use_gumbel, a.seed, a.token_offset, a.ids,
+                       a.gates);
     return hipGetLastError();
 }
 
