@@ -29,11 +29,31 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// 16-byte load through the global address space (global_load_dwordx4, which
+// counts only against vmcnt; a generic pointer would give a flat load whose
+// completion also gates every LDS wait).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4_t global_u32x4;
+__device__ __forceinline__ uint4 ldg16(const void* p) {
+    const u32x4_t v = *(global_u32x4*)(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).  Lane l supplies row
 // (l % 16) of A and column (l % 16) of B, eight k-values each from k-block
 // (l / 16); it receives D[4*(l/16) + i][l % 16], i = 0..3.
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).  Lane l supplies row
+// (l % 32) of A and column (l % 32) of B, eight k-values each from k-block
+// (l / 32); it receives D[8*(v/4) + 4*(l/32) + (v%4)][l % 32] in element v,
+// v = 0..15.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float gelu_erf(float h) {
