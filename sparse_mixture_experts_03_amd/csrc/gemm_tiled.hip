@@ -5,16 +5,18 @@
 // really a grouped GEMM over the tokens scattered to each expert, and P2 §3.3
 // credits fusing the activation into the expert GEMM.  Here:
 //   workgroup tile = 256 weight rows x 256 dispatch rows (one expert), K in
-//   steps of 64;
+//   stages of 32;
 //   tiles go straight from HBM/L2 into LDS with gfx950's global_load_lds
-//   (16 bytes per lane, no register staging), double-buffered in four 32 KB
-//   arrays: stage k+1 streams in while stage k is multiplied, one barrier per
-//   step.  Every 128-byte tile row keeps its eight 16-byte segments in slots
-//   permuted by (row & 7) (an XOR swizzle), so both the loads and the 16-row
-//   MFMA fragment reads are free of LDS bank conflicts without padding;
+//   (16 bytes per lane, no register staging) through a ring of four 32 KB
+//   stages: stage k+3 streams in while stage k is multiplied (about 1.3 us of
+//   MFMA work hides the load latency), one barrier per stage.  Every 64-byte
+//   tile row keeps its four 16-byte segments in slots permuted by
+//   (row >> 2) & 3 (an XOR swizzle), so both the loads and the 32-row MFMA
+//   fragment reads are free of LDS bank conflicts without padding;
 //   4 wavefronts in a 2 x 2 arrangement, each 128 x 128 outputs as 16 MFMA
 //   32x32x16 bf16 tiles with fp32 accumulation (256 accumulators in AGPRs:
-//   64 flops per byte read from LDS);
+//   64 flops per byte read from LDS); an expert's last, partial tile uses a
+//   128- or 64-row variant (4 x 1 wavefronts) so padding stays small;
 //   GEMM1's epilogue applies GeLU and stores bf16 H; GEMM2's stores fp32 Y.
 // The m-tiles of all experts are numbered expert-major and located from the
 // offsets on the device, so skewed loads (0 .. thousands of rows per expert)
@@ -28,134 +30,197 @@ namespace {
 
 constexpr int kTBN = 256;   // weight rows per tile
 constexpr int kTBM = 256;   // dispatch rows per tile
-constexpr int kTBK = 64;    // K per step (128 bytes of every tile row)
-constexpr int kTileBytes = 256 * kTBK * 2;
+constexpr int kTBK = 32;    // K per stage (64 bytes of every tile row)
+constexpr int kStages = 4;  // LDS ring: stage k+3 streams in while stage k is multiplied
+constexpr int kTileBytes = 256 * kTBK * 2;  // 16 KB per operand per stage
 
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
 
-// One wavefront copies 8 tile rows x 128 bytes (1 KB) of the current K step
-// into LDS: lane L fetches logical segment (L & 7) ^ (L >> 3) of row L >> 3,
-// which lands at LDS byte 16 * L of the 1 KB block, i.e. physical slot L & 7
-// of that row.  `base` is wave-uniform and `off` a 32-bit byte offset (one
-// expert's weights and every activation array stay below 4 GiB), so the load
-// takes the scalar-base + vector-offset form.
+// One wavefront copies 16 tile rows x 64 bytes (1 KB) of one stage into LDS:
+// lane L fetches logical segment (L & 3) ^ ((L >> 4) & 3) of row L >> 2, which
+// lands at LDS byte 16 * L of the 1 KB block, i.e. physical slot L & 3 of that
+// row.  `base` is wave-uniform and `off` a 32-bit byte offset (one expert's
+// weights and every activation array stay below 4 GiB), so the load takes the
+// scalar-base + vector-offset form.
 __device__ __forceinline__ void copy_rows_to_lds(const char* base, uint32_t off, uint8_t* lds_block) {
     __builtin_amdgcn_global_load_lds((gvoid*)(base + off), (lvoid*)lds_block, 16, 0, 0);
 }
 
-// MFMA fragment: 8 bf16 of logical segment `seg` of tile row `row`.
-__device__ __forceinline__ bf16x8 frag(const uint8_t* tile, int row, int seg) {
-    return as_bf16x8(*reinterpret_cast<const uint4*>(tile + row * 128 + 16 * (seg ^ (row & 7))));
+// LDS byte offset of logical segment `seg` (0..3) of tile row `row`.
+// Physical slot = seg ^ ((row >> 2) & 3): any 8 consecutive rows read at one
+// logical segment touch 8 distinct 16-byte bank groups.
+__device__ __forceinline__ uint32_t frag_offset(int row, int seg) {
+    return (uint32_t)(row * 64 + 16 * (seg ^ ((row >> 2) & 3)));
 }
 
-template <int WHICH>
-__global__ void __launch_bounds__(256, 1)
-gemm_tiled_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
-                       const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ W,
-                       int64_t W_stride_elems, void* __restrict__ out, int N, int K, int ntiles_n) {
-    __shared__ __attribute__((aligned(1024))) uint8_t Wt0[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t Wt1[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t Xt0[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t Xt1[kTileBytes];
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lvoid*)p;
+}
 
-    // An (empty) statement that clobbers an AGPR tells the backend this kernel
-    // uses AGPRs, so it gives the MFMAs their AGPR-accumulator form (256
-    // accumulators live in AGPRs, operands in VGPRs) instead of VGPR-form
-    // MFMAs with the AGPRs as spill space.
-    asm volatile("" ::: "a0");
+// The fragment reads are issued as inline asm: the compiler cannot tell LDS
+// reads of one ring slot from the direct-to-LDS loads still filling the
+// others and would otherwise wait for every load in flight before each read.
+// Their completion is awaited explicitly (lgkmcnt) before the MFMAs use them.
+__device__ __forceinline__ bf16x8 ds_read16(uint32_t addr) {
+    bf16x8 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without the compiler's release/acquire fence (which would
+// also wait for the direct-to-LDS loads of the stages still in flight); the
+// explicit vmcnt waits before it publish exactly the stage that is due.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// One workgroup tile: 256 weight rows x XROWS dispatch rows, wavefront w
+// owning TI 32-row weight tiles x TJ 32-row dispatch tiles.  XROWS = 256: 2 x 2
+// wavefronts of 128 x 128; XROWS = 128: 4 x 1 of 64 x 128; XROWS = 64: 4 x 1
+// of 64 x 64.  The smaller shapes serve the last, partial tile of an expert
+// so that a remainder of 40 rows costs a quarter tile, not a full one.
+template <int WHICH, int TI, int TJ, int XROWS>
+__device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*Xt)[kTileBytes],
+                                          const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
+                                          const uint16_t* Wexp, void* __restrict__ out, int N, int K, int n0, int p0,
+                                          int rows) {
+    constexpr int WN_WAVES = 256 / (32 * TI);  // wavefronts along the weight rows
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int mt = blockIdx.x / ntiles_n;
-    const int nt = blockIdx.x - mt * ntiles_n;
-    int e, p0, rows;
-    if (!find_mtile(offsets, E, kTBM, mt, &e, &p0, &rows)) return;
-    const int n0 = nt * kTBN;
-    const uint16_t* Wexp = W + (int64_t)e * W_stride_elems;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it stay scalar
 
-    // This wavefront copies tile rows [64 * wave, 64 * wave + 64) of both tiles,
-    // 8 rows per instruction.  Rows past N (weights) or past the tile's
-    // dispatch rows (tokens) are clamped to a valid row: they only feed
-    // outputs that are never stored.
-    const int lseg = (lane & 7) ^ (lane >> 3);
+    // This wavefront copies tile rows [64 * wave, 64 * wave + 64) of the
+    // weight tile, and of the dispatch tile if they lie inside XROWS, 16 rows
+    // per instruction (4 instructions per operand per stage).  Rows past N
+    // (weights) or past the tile's dispatch rows (tokens) are clamped to a
+    // valid row: they only feed outputs that are never stored.
+    const bool xload = 64 * wave < XROWS;
+    const int lseg = (lane & 3) ^ ((lane >> 4) & 3);
     const char* wbase = reinterpret_cast<const char*>(Wexp);
     const char* xbase = reinterpret_cast<const char*>(A);
     const uint32_t rowbytes = (uint32_t)K * 2;
-    uint32_t woff[8], xoff[8];
+    uint32_t woff[4], xoff[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int trow = 64 * wave + 8 * i + (lane >> 3);
+    for (int i = 0; i < 4; ++i) {
+        const int trow = 64 * wave + 16 * i + (lane >> 2);
         woff[i] = (uint32_t)min(n0 + trow, N - 1) * rowbytes + 16 * lseg;
         const int drow = min(trow, rows - 1);
         const uint32_t arow = (WHICH == 1) ? (uint32_t)a_rows[p0 + drow] : (uint32_t)(p0 + drow);
         xoff[i] = arow * rowbytes + 16 * lseg;
     }
-    auto issue = [&](int kt, uint8_t* wt, uint8_t* xt) {
+    // 4 (weights) + 4 (dispatch rows, when this wavefront copies any) loads per stage
+    auto issue = [&](int kt, int buf) {
         const uint32_t kb = (uint32_t)kt * (kTBK * 2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            copy_rows_to_lds(wbase, woff[i] + kb, wt + (64 * wave + 8 * i) * 128);
-            copy_rows_to_lds(xbase, xoff[i] + kb, xt + (64 * wave + 8 * i) * 128);
+        for (int i = 0; i < 4; ++i) copy_rows_to_lds(wbase, woff[i] + kb, &Wt[buf][(64 * wave + 16 * i) * 64]);
+        if (xload) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) copy_rows_to_lds(xbase, xoff[i] + kb, &Xt[buf][(64 * wave + 16 * i) * 64]);
+        }
+    };
+    // wait until at most `stages` later stages of this wavefront's loads are in flight
+    auto wait_stages = [&](int stages) {
+        if (xload) {
+            if (stages >= 2) wait_vmcnt<16>(); else if (stages == 1) wait_vmcnt<8>(); else wait_vmcnt<0>();
+        } else {
+            if (stages >= 2) wait_vmcnt<8>(); else if (stages == 1) wait_vmcnt<4>(); else wait_vmcnt<0>();
         }
     };
 
-    const int wn = (wave & 1) * 128;   // this wave's weight rows within the tile
-    const int wm = (wave >> 1) * 128;  // this wave's dispatch rows within the tile
+    const int wn = (wave % WN_WAVES) * (32 * TI);  // this wave's weight rows within the tile
+    const int wm = (wave / WN_WAVES) * (32 * TJ);  // this wave's dispatch rows within the tile
     const int r = lane & 31;
     const int h = lane >> 5;
-    f32x16 acc[4][4];
+    f32x16 acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    // four k-substeps of 16: lane half h reads logical segment 2 * ks + h
-    auto compute = [&](const uint8_t* wt, const uint8_t* xt) {
+    // two k-substeps of 16: lane half h reads logical segment 2 * ks + h.
+    // Substep 1's fragments are read while substep 0's MFMAs run.
+    uint32_t wrow_off[TI], xrow_off[TJ];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 wf[4], xf[4];
+    for (int i = 0; i < TI; ++i) wrow_off[i] = frag_offset(wn + 32 * i + r, 0);  // XOR 16*seg selects segment seg
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wf[i] = frag(wt, wn + 32 * i + r, 2 * ks + h);
+    for (int j = 0; j < TJ; ++j) xrow_off[j] = frag_offset(wm + 32 * j + r, 0);
+    auto compute = [&](int buf) {
+        const uint32_t wb = lds_addr(Wt[buf]), xb = lds_addr(Xt[buf]);
+        bf16x8 wf[2][TI], xf[2][TJ];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) xf[j] = frag(xt, wm + 32 * j + r, 2 * ks + h);
+        for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < TI; ++i) wf[ks][i] = ds_read16(wb + (wrow_off[i] ^ (16 * (2 * ks + h))));
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(wf[i], xf[j], acc[i][j]);
-            __builtin_amdgcn_sched_barrier(0);  // bound the fragments in flight to one substep
+            for (int j = 0; j < TJ; ++j) xf[ks][j] = ds_read16(xb + (xrow_off[j] ^ (16 * (2 * ks + h))));
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ks == 0) {
+                if constexpr (TI + TJ == 8) {
+                    asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(wf[0][0]), "+v"(wf[0][1]), "+v"(wf[0][2]),
+                                 "+v"(wf[0][3]), "+v"(xf[0][0]), "+v"(xf[0][1]), "+v"(xf[0][2]), "+v"(xf[0][3]));
+                } else if constexpr (TI + TJ == 6) {
+                    asm volatile("s_waitcnt lgkmcnt(6)" : "+v"(wf[0][0]), "+v"(wf[0][1]), "+v"(xf[0][0]),
+                                 "+v"(xf[0][1]), "+v"(xf[0][2]), "+v"(xf[0][3]));
+                } else {
+                    asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(wf[0][0]), "+v"(wf[0][1]), "+v"(xf[0][0]),
+                                 "+v"(xf[0][1]));
+                }
+            } else {
+                if constexpr (TI + TJ == 8) {
+                    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(wf[1][0]), "+v"(wf[1][1]), "+v"(wf[1][2]),
+                                 "+v"(wf[1][3]), "+v"(xf[1][0]), "+v"(xf[1][1]), "+v"(xf[1][2]), "+v"(xf[1][3]));
+                } else if constexpr (TI + TJ == 6) {
+                    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(wf[1][0]), "+v"(wf[1][1]), "+v"(xf[1][0]),
+                                 "+v"(xf[1][1]), "+v"(xf[1][2]), "+v"(xf[1][3]));
+                } else {
+                    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(wf[1][0]), "+v"(wf[1][1]), "+v"(xf[1][0]),
+                                 "+v"(xf[1][1]));
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32x32x16(wf[ks][i], xf[ks][j], acc[i][j]);
         }
     };
 
+    // Ring of kStages buffers.  Step k waits until its own loads have landed
+    // (the loads of the two later stages stay in flight), then one barrier
+    // both publishes stage k and frees the buffer of stage k-1, into which
+    // stage k+3 is issued.  The steady state runs in a loop without exits;
+    // the last steps drain the ring.
     const int nk = K / kTBK;
-    issue(0, Wt0, Xt0);
+    const int pre = min(nk, kStages - 1);
+    for (int s = 0; s < pre; ++s) issue(s, s);
     int kt = 0;
-    for (; kt + 2 <= nk; kt += 2) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        issue(kt + 1, Wt1, Xt1);
-        compute(Wt0, Xt0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (kt + 2 < nk) issue(kt + 2, Wt0, Xt0);
-        compute(Wt1, Xt1);
+    for (; kt + kStages - 1 < nk; ++kt) {
+        wait_stages(2);
+        barrier();
+        issue(kt + kStages - 1, (kt + kStages - 1) % kStages);
+        compute(kt % kStages);
     }
-    if (kt < nk) {  // odd number of K steps: the last one sits in buffer 0
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        compute(Wt0, Xt0);
+    for (; kt < nk; ++kt) {  // drain: every remaining stage is already issued
+        wait_stages(nk - kt - 1);
+        barrier();
+        compute(kt % kStages);
     }
 
     // epilogue: element v of acc[i][j] is D[n = wn + 32i + 8(v/4) + 4h + (v%4)][m = wm + 32j + r]
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < TJ; ++j) {
         const int m = wm + 32 * j + r;
         if (m >= rows) continue;
         const int64_t orow = (int64_t)(p0 + m) * N;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < TI; ++i) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int n = n0 + wn + 32 * i + 8 * q + 4 * h;
@@ -173,6 +238,32 @@ gemm_tiled_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict
             }
         }
     }
+}
+
+template <int WHICH>
+__global__ void __launch_bounds__(256, 1)
+gemm_tiled_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
+                       const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ W,
+                       int64_t W_stride_elems, void* __restrict__ out, int N, int K, int ntiles_n) {
+    __shared__ __attribute__((aligned(1024))) uint8_t Wt[kStages][kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t Xt[kStages][kTileBytes];
+
+    // An (empty) statement that clobbers an AGPR tells the backend this kernel
+    // uses AGPRs, so it gives the MFMAs their AGPR-accumulator form (the
+    // accumulators live in AGPRs, operands in VGPRs).
+    asm volatile("" ::: "a0");
+    const int mt = blockIdx.x / ntiles_n;
+    const int nt = blockIdx.x - mt * ntiles_n;
+    int e, p0, rows;
+    if (!find_mtile(offsets, E, kTBM, mt, &e, &p0, &rows)) return;
+    const int n0 = nt * kTBN;
+    const uint16_t* Wexp = W + (int64_t)e * W_stride_elems;
+    if (rows > 128)
+        tile_gemm<WHICH, 4, 4, 256>(Wt, Xt, A, a_rows, Wexp, out, N, K, n0, p0, rows);
+    else if (rows > 64)
+        tile_gemm<WHICH, 2, 4, 128>(Wt, Xt, A, a_rows, Wexp, out, N, K, n0, p0, rows);
+    else
+        tile_gemm<WHICH, 2, 2, 64>(Wt, Xt, A, a_rows, Wexp, out, N, K, n0, p0, rows);
 }
 
 }  // namespace
