@@ -129,8 +129,12 @@ def main():
     ev1.record(stream)
     ev1.synchronize()
     gemm_ms = ev0.elapsed_time(ev1) / reps
-    path = "streaming" if (cfg["w"] != moe.F32 and (cfg["w"] == moe.INT4_G128 or T <= 16)) else (
-        "f32" if cfg["w"] == moe.F32 else "tiled")
+    if cfg["w"] == moe.F32:
+        path = "f32"
+    elif T <= 16 or (cfg["w"] == moe.INT4_G128 and (d % 1024 or d_ff % 1024)):
+        path = "streaming"  # the automatic choice of the library
+    else:
+        path = "tiled"
     gemm_bytes = active * w_bytes + Tk * d * abytes + Tk * d_ff * hbytes
     gemm_flops = 2.0 * Tk * d * d_ff
     kernel_name = f"moe_grouped_gemm_w1_{path}"

@@ -34,7 +34,11 @@
  *    codes pack two signed two's-complement nibbles per byte, even column in
  *    the low nibble ([E][N][K/2] bytes); their scales are bf16 [E][N][K/128].
  *  - Sizes: 0 <= T <= 2^24, 1 <= E <= 256, 1 <= k <= min(E, 8), d and d_ff
- *    multiples of 64 (of 128 for INT4 experts), d, d_ff <= 2^17.
+ *    multiples of 64 (of 128 for INT4 experts), d, d_ff <= 2^17.  Every
+ *    activation array (x, y, and the workspace's [T*k][d_ff] and
+ *    [T*k][d] float intermediates) and each expert's matrix must stay below
+ *    4 GiB (larger batches are split by the caller); otherwise
+ *    MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -66,9 +70,11 @@ typedef enum moe_dtype {
 
 /* Expert-GEMM implementation choice. */
 typedef enum moe_gemm_path {
-    MOE_GEMM_AUTO = 0,       /* streaming when T*k <= 64, tiled otherwise */
+    MOE_GEMM_AUTO = 0,       /* streaming when T <= 16 (or INT4 weights that the tiled kernel
+                                cannot take), tiled otherwise */
     MOE_GEMM_STREAMING = 1,  /* weight-streaming kernel: 16-token MFMA tiles, every weight read once per 16 rows */
-    MOE_GEMM_TILED = 2       /* LDS-tiled MFMA kernel for many tokens per expert */
+    MOE_GEMM_TILED = 2       /* LDS-tiled MFMA kernel for many tokens per expert; INT4 weights need d and
+                                d_ff multiples of 1024 (else MOE_ERR_UNSUPPORTED) and 16-byte aligned scales */
 } moe_gemm_path;
 
 typedef struct moe_config {
@@ -151,7 +157,9 @@ moe_status moe_permute(const moe_config *cfg, const int32_t *expert_ids, int32_t
  *                A = H as written by which == 1 (a_rows ignored); out = Y,
  *                float [T*k][d].
  * GeLU(h) = h * Phi(h) (erf form).  Accumulation is fp32 (MFMA for BF16/INT4
- * weights); INT4 weights are applied as exact q * s.
+ * weights).  INT4 weights are applied as exact q * s by the streaming kernel;
+ * the tiled kernel multiplies by q * s rounded to bf16 (nearest even; relative
+ * error at most 2^-8 per weight).
  *   offsets [E+1] int32 (device, in), as written by moe_permute.
  */
 moe_status moe_grouped_gemm(const moe_config *cfg, int32_t which, const void *A, const int32_t *a_rows,

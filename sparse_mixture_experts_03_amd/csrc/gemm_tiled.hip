@@ -9,10 +9,13 @@
 //   tiles go straight from HBM/L2 into LDS with gfx950's global_load_lds
 //   (16 bytes per lane, no register staging) through a ring of four 32 KB
 //   stages: stage k+3 streams in while stage k is multiplied (about 1.3 us of
-//   MFMA work hides the load latency), one barrier per stage.  Every 64-byte
+//   MFMA work hides the load latency), one barrier per stage.  INT4 weights
+//   (P1 §5.4, P2 §2.3) instead arrive as codes in registers four stages ahead;
+//   each thread turns one weight row of a stage into bf16(q * s) and writes it
+//   into the same LDS layout, so the MFMA loop is shared.  Every 64-byte
 //   tile row keeps its four 16-byte segments in slots permuted by
-//   (row >> 2) & 3 (an XOR swizzle), so both the loads and the 32-row MFMA
-//   fragment reads are free of LDS bank conflicts without padding;
+//   (row >> 2) & 3 (an XOR swizzle), so the loads, the dequantised stores and
+//   the 32-row MFMA fragment reads are free of LDS bank conflicts;
 //   4 wavefronts in a 2 x 2 arrangement, each 128 x 128 outputs as 16 MFMA
 //   32x32x16 bf16 tiles with fp32 accumulation (256 accumulators in AGPRs:
 //   64 flops per byte read from LDS); an expert's last, partial tile uses a
@@ -78,58 +81,68 @@ __device__ __forceinline__ void wait_vmcnt() {
 // explicit vmcnt waits before it publish exactly the stage that is due.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// ---- INT4 weight rows -------------------------------------------------
+// This thread's 16 code bytes and its 2-byte group scale, read from LDS
+// (both written there by direct-to-LDS loads of its own wavefront).
+__device__ __forceinline__ void ds_read_codes(uint32_t caddr, uint32_t saddr, u32x4_t& c, uint32_t& sbits) {
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_u16 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(c), "=v"(sbits)
+                 : "v"(caddr), "v"(saddr));
+}
+
+__device__ __forceinline__ void ds_write16(uint32_t addr, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const u32x4_t v = {a, b, c, d};
+    asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+
+// 32 INT4 codes of one tile row and stage (16 bytes; byte j of word w holds
+// k = 8w + 2j in its low nibble and k = 8w + 2j + 1 in its high nibble) with
+// their group's bf16 scale -> 32 bf16 values bf16(q * s), written as the
+// row's four 16-byte logical segments into their swizzled LDS slots.
+// q * s is formed exactly as fma(q + 8, s, -8 s) ((q + 8) * s has at most 12
+// significant bits) and rounded once, to nearest even.
+__device__ __forceinline__ void dequant_row_to_lds(u32x4_t c, uint32_t sbits, uint32_t row_addr, int swz) {
+    const float s = bf16_bits_to_float(sbits);
+    const float m8s = -8.0f * s;
+    const uint32_t words[4] = {c.x, c.y, c.z, c.w};
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int seg = 0; seg < 4; ++seg) {
+        const uint32_t lo = (words[seg] & 0x0f0f0f0fu) ^ 0x08080808u;         // q + 8 of even k
+        const uint32_t hi = ((words[seg] >> 4) & 0x0f0f0f0fu) ^ 0x08080808u;  // q + 8 of odd k
+        uint32_t packed[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float a = __builtin_fmaf((float)((lo >> (8 * j)) & 0xffu), s, m8s);
+            const float b = __builtin_fmaf((float)((hi >> (8 * j)) & 0xffu), s, m8s);
+            const bf16x2_t v = {(__bf16)a, (__bf16)b};
+            packed[j] = __builtin_bit_cast(uint32_t, v);
+        }
+        ds_write16(row_addr + 16 * (seg ^ swz), packed[0], packed[1], packed[2], packed[3]);
+    }
+}
+
 // One workgroup tile: 256 weight rows x XROWS dispatch rows, wavefront w
 // owning TI 32-row weight tiles x TJ 32-row dispatch tiles.  XROWS = 256: 2 x 2
 // wavefronts of 128 x 128; XROWS = 128: 4 x 1 of 64 x 128; XROWS = 64: 4 x 1
 // of 64 x 64.  The smaller shapes serve the last, partial tile of an expert
 // so that a remainder of 40 rows costs a quarter tile, not a full one.
-template <int WHICH, int TI, int TJ, int XROWS>
-__device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*Xt)[kTileBytes],
+// WQ = kBF16: Wexp is the expert's bf16 [N][K] matrix; WQ = kINT4: its packed
+// codes [N][K/2] with bf16 scales Wsc [N][K/128].
+template <int WQ, int WHICH, int TI, int TJ, int XROWS>
+__device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*Xt)[kTileBytes], uint8_t (*Ct)[4096],
+                                          uint8_t (*St)[4096],
                                           const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
-                                          const uint16_t* Wexp, void* __restrict__ out, int N, int K, int n0, int p0,
-                                          int rows) {
+                                          const void* Wexp, const void* Wsc, void* __restrict__ out, int N, int K,
+                                          int n0, int p0, int rows) {
     constexpr int WN_WAVES = 256 / (32 * TI);  // wavefronts along the weight rows
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it stay scalar
 
-    // This wavefront copies tile rows [64 * wave, 64 * wave + 64) of the
-    // weight tile, and of the dispatch tile if they lie inside XROWS, 16 rows
-    // per instruction (4 instructions per operand per stage).  Rows past N
-    // (weights) or past the tile's dispatch rows (tokens) are clamped to a
-    // valid row: they only feed outputs that are never stored.
-    const bool xload = 64 * wave < XROWS;
-    const int lseg = (lane & 3) ^ ((lane >> 4) & 3);
-    const char* wbase = reinterpret_cast<const char*>(Wexp);
+    const int lseg = (lane & 3) ^ ((lane >> 4) & 3);  // logical segment this lane copies
     const char* xbase = reinterpret_cast<const char*>(A);
-    const uint32_t rowbytes = (uint32_t)K * 2;
-    uint32_t woff[4], xoff[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int trow = 64 * wave + 16 * i + (lane >> 2);
-        woff[i] = (uint32_t)min(n0 + trow, N - 1) * rowbytes + 16 * lseg;
-        const int drow = min(trow, rows - 1);
-        const uint32_t arow = (WHICH == 1) ? (uint32_t)a_rows[p0 + drow] : (uint32_t)(p0 + drow);
-        xoff[i] = arow * rowbytes + 16 * lseg;
-    }
-    // 4 (weights) + 4 (dispatch rows, when this wavefront copies any) loads per stage
-    auto issue = [&](int kt, int buf) {
-        const uint32_t kb = (uint32_t)kt * (kTBK * 2);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) copy_rows_to_lds(wbase, woff[i] + kb, &Wt[buf][(64 * wave + 16 * i) * 64]);
-        if (xload) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) copy_rows_to_lds(xbase, xoff[i] + kb, &Xt[buf][(64 * wave + 16 * i) * 64]);
-        }
-    };
-    // wait until at most `stages` later stages of this wavefront's loads are in flight
-    auto wait_stages = [&](int stages) {
-        if (xload) {
-            if (stages >= 2) wait_vmcnt<16>(); else if (stages == 1) wait_vmcnt<8>(); else wait_vmcnt<0>();
-        } else {
-            if (stages >= 2) wait_vmcnt<8>(); else if (stages == 1) wait_vmcnt<4>(); else wait_vmcnt<0>();
-        }
-    };
+    const uint32_t xrowbytes = (uint32_t)K * 2;
 
     const int wn = (wave % WN_WAVES) * (32 * TI);  // this wave's weight rows within the tile
     const int wm = (wave / WN_WAVES) * (32 * TJ);  // this wave's dispatch rows within the tile
@@ -192,25 +205,170 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
         }
     };
 
-    // Ring of kStages buffers.  Step k waits until its own loads have landed
-    // (the loads of the two later stages stay in flight), then one barrier
-    // both publishes stage k and frees the buffer of stage k-1, into which
-    // stage k+3 is issued.  The steady state runs in a loop without exits;
-    // the last steps drain the ring.
     const int nk = K / kTBK;
-    const int pre = min(nk, kStages - 1);
-    for (int s = 0; s < pre; ++s) issue(s, s);
-    int kt = 0;
-    for (; kt + kStages - 1 < nk; ++kt) {
-        wait_stages(2);
-        barrier();
-        issue(kt + kStages - 1, (kt + kStages - 1) % kStages);
-        compute(kt % kStages);
-    }
-    for (; kt < nk; ++kt) {  // drain: every remaining stage is already issued
-        wait_stages(nk - kt - 1);
-        barrier();
-        compute(kt % kStages);
+    if constexpr (WQ == kBF16) {
+        // This wavefront copies tile rows [64 * wave, 64 * wave + 64) of the
+        // weight tile, and of the dispatch tile if they lie inside XROWS, 16
+        // rows per instruction (4 instructions per operand per stage).  Rows
+        // past N (weights) or past the tile's dispatch rows (tokens) are
+        // clamped to a valid row: they only feed outputs that are never stored.
+        const bool xload = 64 * wave < XROWS;
+        const char* wbase = reinterpret_cast<const char*>(Wexp);
+        uint32_t woff[4], xoff[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int trow = 64 * wave + 16 * i + (lane >> 2);
+            woff[i] = (uint32_t)min(n0 + trow, N - 1) * xrowbytes + 16 * lseg;
+            const int drow = min(trow, rows - 1);
+            const uint32_t arow = (WHICH == 1) ? (uint32_t)a_rows[p0 + drow] : (uint32_t)(p0 + drow);
+            xoff[i] = arow * xrowbytes + 16 * lseg;
+        }
+        // 4 (weights) + 4 (dispatch rows, when this wavefront copies any) loads per stage
+        auto issue = [&](int kt, int buf) {
+            const uint32_t kb = (uint32_t)kt * (kTBK * 2);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) copy_rows_to_lds(wbase, woff[i] + kb, &Wt[buf][(64 * wave + 16 * i) * 64]);
+            if (xload) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) copy_rows_to_lds(xbase, xoff[i] + kb, &Xt[buf][(64 * wave + 16 * i) * 64]);
+            }
+        };
+        // wait until at most `stages` later stages of this wavefront's loads are in flight
+        auto wait_stages = [&](int stages) {
+            if (xload) {
+                if (stages >= 2) wait_vmcnt<16>(); else if (stages == 1) wait_vmcnt<8>(); else wait_vmcnt<0>();
+            } else {
+                if (stages >= 2) wait_vmcnt<8>(); else if (stages == 1) wait_vmcnt<4>(); else wait_vmcnt<0>();
+            }
+        };
+
+        // Ring of kStages buffers.  Step k waits until its own loads have landed
+        // (the loads of the two later stages stay in flight), then one barrier
+        // both publishes stage k and frees the buffer of stage k-1, into which
+        // stage k+3 is issued.  The steady state runs in a loop without exits;
+        // the last steps drain the ring.
+        const int pre = min(nk, kStages - 1);
+        for (int s = 0; s < pre; ++s) issue(s, s);
+        int kt = 0;
+        for (; kt + kStages - 1 < nk; ++kt) {
+            wait_stages(2);
+            barrier();
+            issue(kt + kStages - 1, (kt + kStages - 1) % kStages);
+            compute(kt % kStages);
+        }
+        for (; kt < nk; ++kt) {  // drain: every remaining stage is already issued
+            wait_stages(nk - kt - 1);
+            barrier();
+            compute(kt % kStages);
+        }
+    } else {
+        // INT4: thread t dequantises weight-tile row t.  Its 16 bytes of codes
+        // for stage j, C(j), are copied at step j-4 into code slot j % 4 by one
+        // direct-to-LDS load per wavefront (lane L's bytes land at 16 L of the
+        // wavefront's 1 KB, so only the wavefront's own vmcnt guards them),
+        // and the dispatch rows X(j) at step j-3, spread evenly over the four
+        // wavefronts (XROWS / 64 loads each).  A wavefront's loads thus go out
+        // in the order
+        //   C(0) X(0) C(1) X(1) C(2) X(2) C(3) | X(3) C(4) | X(4) C(5) | ...
+        // (prologue | step 0 | step 1 ...), and a wait for one of them counts
+        // the loads issued after it.  The scales of the row's next 8 groups
+        // (16 bytes, 32 stages) follow the same route every 32 stages, issued
+        // before the codes of the first stage that needs them; being extra
+        // loads that the counts leave out, they can only lengthen a wait.
+        // Step s:
+        //   wait for X(s) and for this thread's LDS stores (W(s), written at
+        //   step s-1); barrier (publishes stage s, frees the slot of s-1);
+        //   issue X(s+3) into that slot and C(s+4); wait for C(s+1) and
+        //   dequantise it into LDS slot (s+1) % 4 (last read at step s-3,
+        //   before the barrier of step s-2); multiply stage s.
+        // K is a multiple of 1024: the stages come in whole blocks of 32.
+        constexpr int XL = XROWS / 64;  // dispatch-row loads per wavefront per stage
+        const char* cbase = reinterpret_cast<const char*>(Wexp);
+        const char* sbase = reinterpret_cast<const char*>(Wsc);
+        const uint32_t wrow = (uint32_t)min(n0 + tid, N - 1);
+        const uint32_t coff = wrow * ((uint32_t)K / 2);
+        const uint32_t soff = wrow * ((uint32_t)K / 128) * 2;
+        // rows past the tile's dispatch rows are clamped (as above)
+        uint32_t xoff_e[XL];
+#pragma unroll
+        for (int i = 0; i < XL; ++i) {
+            const int trow = wave * (XROWS / 4) + 16 * i + (lane >> 2);
+            const int drow = min(trow, rows - 1);
+            const uint32_t arow = (WHICH == 1) ? (uint32_t)a_rows[p0 + drow] : (uint32_t)(p0 + drow);
+            xoff_e[i] = arow * xrowbytes + 16 * lseg;
+        }
+        auto issue_xe = [&](int kt, int buf) {
+            const uint32_t kb = (uint32_t)kt * (kTBK * 2);
+#pragma unroll
+            for (int i = 0; i < XL; ++i)
+                copy_rows_to_lds(xbase, xoff_e[i] + kb, &Xt[buf][(wave * (XROWS / 4) + 16 * i) * 64]);
+        };
+        auto issue_c = [&](int kt) { copy_rows_to_lds(cbase, coff + (uint32_t)kt * 16, &Ct[kt % kStages][wave * 1024]); };
+        auto issue_scales = [&](int blk) {  // groups 8 blk .. 8 blk + 7 (stages 32 blk .. 32 blk + 31)
+            copy_rows_to_lds(sbase, soff + (uint32_t)blk * 16, &St[blk & 1][wave * 1024]);
+        };
+        const uint32_t cread = lds_addr(Ct[0]) + (uint32_t)tid * 16;
+        const uint32_t sread = lds_addr(St[0]) + (uint32_t)tid * 16;
+        const uint32_t wdst = (uint32_t)tid * 64;
+        const int swz = (tid >> 2) & 3;
+        // rem = stages after s (>= 0); the counts follow the issue order above
+        auto wait_x = [&](int rem) {
+            if (rem >= 3) wait_vmcnt<3 + 2 * XL>();
+            else if (rem == 2) wait_vmcnt<2 + 2 * XL>();
+            else if (rem == 1) wait_vmcnt<1 + XL>();
+            else wait_vmcnt<0>();
+        };
+        // C(s+1) landed; rem = stages after s (>= 1)
+        auto wait_c = [&](int rem) {
+            if (rem >= 4) wait_vmcnt<3 + 3 * XL>();
+            else if (rem == 3) wait_vmcnt<2 + 3 * XL>();
+            else if (rem == 2) wait_vmcnt<1 + 2 * XL>();
+            else wait_vmcnt<XL>();
+        };
+        auto dequant = [&](int j) {  // stage j's codes and scale -> LDS slot j % 4
+            u32x4_t c;
+            uint32_t sc;
+            ds_read_codes(cread + (uint32_t)(j % kStages) * 4096,
+                          sread + (uint32_t)((j >> 5) & 1) * 4096 + (uint32_t)((j >> 2) & 7) * 2, c, sc);
+            dequant_row_to_lds(c, sc, lds_addr(Wt[j % kStages]) + wdst, swz);
+        };
+        // prologue
+        issue_scales(0);
+        issue_c(0);
+        issue_xe(0, 0);
+        issue_c(1);
+        issue_xe(1, 1);
+        issue_c(2);
+        issue_xe(2, 2);
+        issue_c(3);
+        wait_c(4);
+        dequant(0);
+
+        // one step; J = s % 4 (static), rem = nk - 1 - s (static in each call below)
+        auto step = [&](int s, const int J, const int rem) {
+            wait_x(rem);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            barrier();
+            if (rem >= 3) issue_xe(s + 3, (J + 3) % kStages);
+            if (rem >= 4) issue_c(s + 4);
+            if (rem >= 1) {
+                wait_c(rem);
+                dequant(s + 1);
+            }
+            compute(J);
+        };
+        int s0 = 0;
+        for (; s0 + 8 <= nk; s0 += 4) {  // steady state: every step has 4 or more stages after it
+            if ((s0 & 31) == 0 && s0 + 32 < nk) issue_scales((s0 >> 5) + 1);
+            step(s0, 0, 4);
+            step(s0 + 1, 1, 4);
+            step(s0 + 2, 2, 4);
+            step(s0 + 3, 3, 4);
+        }
+        step(s0, 0, 3);  // the last four stages
+        step(s0 + 1, 1, 2);
+        step(s0 + 2, 2, 1);
+        step(s0 + 3, 3, 0);
     }
 
     // epilogue: element v of acc[i][j] is D[n = wn + 32i + 8(v/4) + 4h + (v%4)][m = wm + 32j + r]
@@ -240,13 +398,17 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
     }
 }
 
-template <int WHICH>
+// W: the experts' weights, W_stride bytes apart (bf16 [N][K] or INT4 codes
+// [N][K/2]); Wsc: INT4 scales bf16 [E][N][K/128] (unused for bf16).
+template <int WQ, int WHICH>
 __global__ void __launch_bounds__(256, 1)
-gemm_tiled_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
-                       const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ W,
-                       int64_t W_stride_elems, void* __restrict__ out, int N, int K, int ntiles_n) {
+gemm_tiled_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
+                  const int32_t* __restrict__ offsets, int E, const uint8_t* __restrict__ W, int64_t W_stride,
+                  const uint16_t* __restrict__ Wsc, void* __restrict__ out, int N, int K, int ntiles_n) {
     __shared__ __attribute__((aligned(1024))) uint8_t Wt[kStages][kTileBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t Xt[kStages][kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t Ct[WQ == kINT4 ? kStages : 1][4096];  // INT4 code ring
+    __shared__ __attribute__((aligned(1024))) uint8_t St[WQ == kINT4 ? 2 : 1][4096];        // INT4 scale ring
 
     // An (empty) statement that clobbers an AGPR tells the backend this kernel
     // uses AGPRs, so it gives the MFMAs their AGPR-accumulator form (the
@@ -256,14 +418,18 @@ gemm_tiled_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict
     const int nt = blockIdx.x - mt * ntiles_n;
     int e, p0, rows;
     if (!find_mtile(offsets, E, kTBM, mt, &e, &p0, &rows)) return;
+    e = __builtin_amdgcn_readfirstlane(e);  // uniform across the workgroup: keep the bases scalar
+    p0 = __builtin_amdgcn_readfirstlane(p0);
+    rows = __builtin_amdgcn_readfirstlane(rows);
     const int n0 = nt * kTBN;
-    const uint16_t* Wexp = W + (int64_t)e * W_stride_elems;
+    const void* Wexp = W + (int64_t)e * W_stride;
+    const void* Wsc_e = (WQ == kINT4) ? (const void*)(Wsc + (int64_t)e * N * (K / 128)) : nullptr;
     if (rows > 128)
-        tile_gemm<WHICH, 4, 4, 256>(Wt, Xt, A, a_rows, Wexp, out, N, K, n0, p0, rows);
+        tile_gemm<WQ, WHICH, 4, 4, 256>(Wt, Xt, Ct, St, A, a_rows, Wexp, Wsc_e, out, N, K, n0, p0, rows);
     else if (rows > 64)
-        tile_gemm<WHICH, 2, 4, 128>(Wt, Xt, A, a_rows, Wexp, out, N, K, n0, p0, rows);
+        tile_gemm<WQ, WHICH, 2, 4, 128>(Wt, Xt, Ct, St, A, a_rows, Wexp, Wsc_e, out, N, K, n0, p0, rows);
     else
-        tile_gemm<WHICH, 2, 2, 64>(Wt, Xt, A, a_rows, Wexp, out, N, K, n0, p0, rows);
+        tile_gemm<WQ, WHICH, 2, 2, 64>(Wt, Xt, Ct, St, A, a_rows, Wexp, Wsc_e, out, N, K, n0, p0, rows);
 }
 
 }  // namespace
@@ -276,14 +442,25 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const uint16_t* A = static_cast<const uint16_t*>(a.A);
-    const uint16_t* W = static_cast<const uint16_t*>(a.W);
+    const uint8_t* W = static_cast<const uint8_t*>(a.W);
+    const uint16_t* S = static_cast<const uint16_t*>(a.W_scales);
     dim3 grid((unsigned)blocks), block(256);
-    if (a.which == 1)
-        hipLaunchKernelGGL(gemm_tiled_bf16_kernel<1>, grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
-                           a.W_stride / 2, a.out, (int)a.N, (int)a.K, ntiles_n);
-    else
-        hipLaunchKernelGGL(gemm_tiled_bf16_kernel<2>, grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
-                           a.W_stride / 2, a.out, (int)a.N, (int)a.K, ntiles_n);
+    const int N = (int)a.N, K = (int)a.K;
+    if (a.w_dtype == kINT4) {
+        if (a.which == 1)
+            hipLaunchKernelGGL((gemm_tiled_kernel<kINT4, 1>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
+                               a.W_stride, S, a.out, N, K, ntiles_n);
+        else
+            hipLaunchKernelGGL((gemm_tiled_kernel<kINT4, 2>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
+                               a.W_stride, S, a.out, N, K, ntiles_n);
+    } else {
+        if (a.which == 1)
+            hipLaunchKernelGGL((gemm_tiled_kernel<kBF16, 1>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
+                               a.W_stride, S, a.out, N, K, ntiles_n);
+        else
+            hipLaunchKernelGGL((gemm_tiled_kernel<kBF16, 2>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
+                               a.W_stride, S, a.out, N, K, ntiles_n);
+    }
     return hipGetLastError();
 }
 

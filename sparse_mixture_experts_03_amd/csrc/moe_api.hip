@@ -20,6 +20,7 @@ constexpr int64_t kMaxDim = int64_t(1) << 17;
 constexpr int kMaxE = 256;
 constexpr int kMaxK = 8;
 constexpr int64_t kStreamingMaxT = 16;  // automatic path: streaming kernel up to 16 tokens
+constexpr int64_t kMaxArrayBytes = int64_t(1) << 32;
 
 moe_status hip_fail(hipError_t e) {
     g_last_hip_error = (int32_t)e;
@@ -31,6 +32,10 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 int64_t elem_bits(int32_t dtype) { return dtype == MOE_DTYPE_F32 ? 32 : dtype == MOE_DTYPE_BF16 ? 16 : 4; }
+
+// The tiled kernel takes INT4 weights when both GEMMs' K (d and d_ff) hold
+// whole blocks of 8 scale groups.
+bool int4_tiled_ok(const moe_config& c) { return c.d % 1024 == 0 && c.d_ff % 1024 == 0; }
 
 moe_status check_config(const moe_config* c) {
     if (!c) return MOE_ERR_INVALID_ARGUMENT;
@@ -49,6 +54,15 @@ moe_status check_config(const moe_config* c) {
         return MOE_ERR_INVALID_ARGUMENT;
     // supported pairings: F32/F32, BF16/BF16, BF16/INT4
     if ((c->act_dtype == MOE_DTYPE_F32) != (c->w_dtype == MOE_DTYPE_F32)) return MOE_ERR_UNSUPPORTED;
+    // the tiled INT4 kernel fetches 8 group scales (16 bytes) at a time
+    if (c->w_dtype == MOE_DTYPE_INT4_G128 && c->gemm_path == MOE_GEMM_TILED && !int4_tiled_ok(*c))
+        return MOE_ERR_UNSUPPORTED;
+    // kernels address each activation array and each expert's matrix with 32-bit byte offsets
+    const int64_t ab = c->act_dtype == MOE_DTYPE_F32 ? 4 : 2;
+    const int64_t Tk = c->T * c->k;
+    if (c->T * c->d * ab >= kMaxArrayBytes || Tk * c->d_ff * 4 >= kMaxArrayBytes || Tk * c->d * 4 >= kMaxArrayBytes ||
+        c->d * c->d_ff * elem_bits(c->w_dtype) / 8 >= kMaxArrayBytes)
+        return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -77,22 +91,24 @@ Layout layout_of(const moe_config& c) {
     return L;
 }
 
+// GEMM kernel for a config: 0 (F32 weights), MOE_GEMM_STREAMING or MOE_GEMM_TILED.
+int gemm_path_of(const moe_config& c) {
+    if (c.w_dtype == MOE_DTYPE_F32) return 0;
+    if (c.gemm_path != MOE_GEMM_AUTO) return c.gemm_path;
+    if (c.T <= kStreamingMaxT) return MOE_GEMM_STREAMING;
+    if (c.w_dtype == MOE_DTYPE_INT4_G128 && !int4_tiled_ok(c)) return MOE_GEMM_STREAMING;
+    return MOE_GEMM_TILED;
+}
+
 // Expert weight pointer/stride checks for an N x K matrix per expert.
 moe_status check_weights(const moe_config& c, const void* W, const void* S, int64_t stride, int64_t N, int64_t K) {
     if (!W || !aligned(W, 16)) return MOE_ERR_INVALID_ARGUMENT;
     const int64_t bytes = N * K * elem_bits(c.w_dtype) / 8;
     if (stride < bytes || stride % 16 != 0) return MOE_ERR_INVALID_ARGUMENT;
     if (c.w_dtype == MOE_DTYPE_INT4_G128) {
-        if (!S || !aligned(S, 2)) return MOE_ERR_INVALID_ARGUMENT;
+        if (!S || !aligned(S, gemm_path_of(c) == MOE_GEMM_TILED ? 16 : 2)) return MOE_ERR_INVALID_ARGUMENT;
     }
     return MOE_OK;
-}
-
-int gemm_path_of(const moe_config& c) {
-    if (c.w_dtype == MOE_DTYPE_F32) return 0;
-    if (c.w_dtype == MOE_DTYPE_INT4_G128) return MOE_GEMM_STREAMING;  // tiled INT4 kernel not built yet
-    if (c.gemm_path != MOE_GEMM_AUTO) return c.gemm_path;
-    return c.T <= kStreamingMaxT ? MOE_GEMM_STREAMING : MOE_GEMM_TILED;
 }
 
 hipError_t run_gemm(const moe_config& c, int which, const void* A, const int32_t* a_rows, const int32_t* offsets,

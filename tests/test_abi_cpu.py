@@ -91,6 +91,34 @@ def test_unsupported_pairings(lib):
             binding.MOE_ERR_UNSUPPORTED
 
 
+def test_int4_tiled_needs_whole_scale_blocks(lib):
+    """The tiled kernel takes INT4 weights only when d and d_ff are multiples
+    of 1024; an explicit request otherwise is unsupported, the automatic
+    choice falls back to the streaming kernel."""
+    n = ctypes.c_size_t()
+    for d, d_ff, want in [(1024, 3072, 0), (384, 768, binding.MOE_ERR_UNSUPPORTED),
+                          (1024, 1536, binding.MOE_ERR_UNSUPPORTED)]:
+        c = _cfg(T=512, d=d, d_ff=d_ff, w_dtype=moe.INT4_G128, gemm_path=moe.GEMM_TILED)
+        assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == want, (d, d_ff)
+        c = _cfg(T=512, d=d, d_ff=d_ff, w_dtype=moe.INT4_G128, gemm_path=moe.GEMM_AUTO)
+        assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == 0, (d, d_ff)
+
+
+def test_int4_tiled_scales_alignment(lib):
+    c = _cfg(T=512, d=1024, d_ff=1024, w_dtype=moe.INT4_G128, gemm_path=moe.GEMM_TILED)
+    wb = 1024 * 1024 // 2
+    assert _forward(lib, c, s1=wb, s2=wb, S1=0xA0008, S2=0xB0000, wsb=1 << 40) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert _forward(lib, c, s1=wb, s2=wb, S1=0xA0000, S2=0xB0002, wsb=1 << 40) == binding.MOE_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(T=1 << 19, d=4096, k=2),            # Y: 2^19 * 2 * 4096 * 4 bytes = 32 GiB
+                                dict(T=1 << 16, d=1024, d_ff=1 << 15, k=2),  # [T*k][d_ff] intermediate = 16 GiB
+                                dict(T=64, d=1 << 16, d_ff=1 << 15, w_dtype=moe.BF16)])  # one expert = 4 GiB
+def test_arrays_over_4gib_unsupported(lib, kw):
+    n = ctypes.c_size_t()
+    assert lib.moe_workspace_size(ctypes.byref(_cfg(**kw)), ctypes.byref(n)) == binding.MOE_ERR_UNSUPPORTED
+
+
 def test_workspace_size_accounts_for_buffers(lib):
     n = ctypes.c_size_t()
     c = _cfg(T=4096, d=4096, d_ff=16384, E=16)

@@ -109,6 +109,10 @@ FORWARD_CASES = {
     "bf16-T9-d256-dff512-E1-k1": (case(9, 256, 512, 1, k=1), [moe.GEMM_STREAMING, moe.GEMM_TILED]),
     "int4-T12-d512-dff1024-E8-gumbel": (case(12, 512, 1024, 8, w=INT4, tau=0.5, gumbel=True), [moe.GEMM_AUTO]),
     "int4-T200-d384-dff768-E8-gumbel": (case(200, 384, 768, 8, w=INT4, tau=0.5, gumbel=True), [moe.GEMM_AUTO]),
+    # K = 1024 and 3072: one and three 32-stage scale blocks; skewed rows exercise all three tile heights
+    "int4-T200-d1024-dff3072-E8-skewed": (case(200, 1024, 3072, 8, w=INT4, bias=True),
+                                          [moe.GEMM_STREAMING, moe.GEMM_TILED]),
+    "int4-T40-d1024-dff1024-E64-k8": (case(40, 1024, 1024, 64, k=8, w=INT4), [moe.GEMM_TILED]),
     "f32-T130-d192-dff320-E5-k3": (case(130, 192, 320, 5, k=3, act=F32, w=F32, bias=True), [moe.GEMM_AUTO]),
 }
 FORWARD_PARAMS = [(n, p) for n, (_, paths) in FORWARD_CASES.items() for p in paths]
@@ -151,9 +155,11 @@ def test_deterministic_repeats(dev):
             assert torch.equal(a, b)
 
 
-def test_paths_agree(dev):
-    """The streaming and tiled kernels compute the same function (to fp32 rounding)."""
-    cfg = case(64, 512, 1024, 8)
+@pytest.mark.parametrize("w", [BF16, INT4], ids=["bf16", "int4"])
+def test_paths_agree(dev, w):
+    """The streaming and tiled kernels compute the same function (to fp32
+    rounding; INT4: the tiled kernel rounds each q * s to bf16)."""
+    cfg = case(64, 1024, 2048, 8, w=w)
     inp = _inputs(cfg, dev, seed=6)
     a = H.run_forward(cfg, inp, gemm_path=moe.GEMM_STREAMING)
     b = H.run_forward(cfg, inp, gemm_path=moe.GEMM_TILED)
