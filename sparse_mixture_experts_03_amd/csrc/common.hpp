@@ -60,57 +60,78 @@ __device__ __forceinline__ float gelu_erf(float h) {
     return 0.5f * h * (1.0f + erff(h * 0.70710678118654752440f));
 }
 
-// Map a flat m-tile index onto (expert, first dispatch position, rows) for a
-// grouped GEMM whose experts hold offsets[e+1]-offsets[e] rows, cut into tiles
-// of BM rows.  Tiles are numbered expert-major.  Returns false when mt lies
-// beyond the last real tile.  Called by one whole wavefront (all lanes get
-// the same answer); E <= 256.
-__device__ __forceinline__ bool find_mtile(const int32_t* __restrict__ offsets, int E, int BM, int mt,
-                                           int* expert, int* pos0, int* rows) {
+// The m-tiles of a grouped GEMM whose experts hold offsets[e+1]-offsets[e]
+// rows, cut into tiles of BM rows and numbered expert-major.  Built by one
+// whole wavefront (every lane gets the same total); E <= 256, 4 experts per
+// lane.
+struct MtileScan {
+    int tiles[4], begin[4];  // this lane's experts 4 lane .. 4 lane + 3
+    int excl, incl;          // m-tiles of the experts before / up to this lane's
+    int total;               // all m-tiles
+};
+
+__device__ __forceinline__ MtileScan scan_mtiles(const int32_t* __restrict__ offsets, int E, int BM) {
     const int lane = threadIdx.x & 63;
-    int tiles[4], begin[4];
+    MtileScan s;
     int local = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        int e = lane * 4 + j;
+        const int e = lane * 4 + j;
         int n = 0, b = 0;
         if (e < E) {
             b = offsets[e];
             n = offsets[e + 1] - b;
         }
-        begin[j] = b;
-        tiles[j] = (n + BM - 1) / BM;
-        local += tiles[j];
+        s.begin[j] = b;
+        s.tiles[j] = (n + BM - 1) / BM;
+        local += s.tiles[j];
     }
     // inclusive scan of per-lane tile counts across the wavefront
     int incl = local;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        int v = __shfl_up(incl, off, 64);
+        const int v = __shfl_up(incl, off, 64);
         if (lane >= off) incl += v;
     }
-    int excl = incl - local;
-    int total = __shfl(incl, 63, 64);
-    if (mt >= total) return false;
-    // the lane whose range holds mt
-    unsigned long long hit = __ballot(mt >= excl && mt < incl);
-    int src = __ffsll((long long)hit) - 1;
+    s.incl = incl;
+    s.excl = incl - local;
+    s.total = __shfl(incl, 63, 64);
+    return s;
+}
+
+// (expert, first dispatch position, rows) of m-tile mt < s.total; called by
+// the whole wavefront that built s.
+__device__ __forceinline__ void lookup_mtile(const MtileScan& s, const int32_t* __restrict__ offsets, int BM, int mt,
+                                             int* expert, int* pos0, int* rows) {
+    const int lane = threadIdx.x & 63;
+    const unsigned long long hit = __ballot(mt >= s.excl && mt < s.incl);  // the lane whose range holds mt
+    const int src = __ffsll((long long)hit) - 1;
     int e_found = -1, p0 = 0, r = 0;
     if (lane == src) {
-        int acc = excl;
+        int acc = s.excl;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            if (e_found < 0 && mt < acc + tiles[j]) {
+            if (e_found < 0 && mt < acc + s.tiles[j]) {
                 e_found = lane * 4 + j;
-                p0 = begin[j] + (mt - acc) * BM;
+                p0 = s.begin[j] + (mt - acc) * BM;
                 r = min(BM, offsets[e_found + 1] - p0);
             }
-            acc += tiles[j];
+            acc += s.tiles[j];
         }
     }
     *expert = __shfl(e_found, src, 64);
     *pos0 = __shfl(p0, src, 64);
     *rows = __shfl(r, src, 64);
+}
+
+// Map a flat m-tile index onto (expert, first dispatch position, rows).
+// Returns false when mt lies beyond the last real tile.  Called by one whole
+// wavefront.
+__device__ __forceinline__ bool find_mtile(const int32_t* __restrict__ offsets, int E, int BM, int mt, int* expert,
+                                           int* pos0, int* rows) {
+    const MtileScan s = scan_mtiles(offsets, E, BM);
+    if (mt >= s.total) return false;
+    lookup_mtile(s, offsets, BM, mt, expert, pos0, rows);
     return true;
 }
 

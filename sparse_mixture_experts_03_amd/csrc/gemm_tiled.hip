@@ -10,9 +10,9 @@
 //   (16 bytes per lane, no register staging) through a ring of four 32 KB
 //   stages: stage k+3 streams in while stage k is multiplied (about 1.3 us of
 //   MFMA work hides the load latency), one barrier per stage.  INT4 weights
-//   (P1 §5.4, P2 §2.3) instead arrive as codes in registers four stages ahead;
-//   each thread turns one weight row of a stage into bf16(q * s) and writes it
-//   into the same LDS layout, so the MFMA loop is shared.  Every 64-byte
+//   (P1 §5.4, P2 §2.3) instead arrive in LDS as codes four stages ahead; the
+//   workgroup turns them into bf16(q * s) in the same LDS layout, so the MFMA
+//   loop is shared.  Every 64-byte
 //   tile row keeps its four 16-byte segments in slots permuted by
 //   (row >> 2) & 3 (an XOR swizzle), so the loads, the dequantised stores and
 //   the 32-row MFMA fragment reads are free of LDS bank conflicts;
@@ -36,6 +36,9 @@ constexpr int kTBM = 256;   // dispatch rows per tile
 constexpr int kTBK = 32;    // K per stage (64 bytes of every tile row)
 constexpr int kStages = 4;  // LDS ring: stage k+3 streams in while stage k is multiplied
 constexpr int kTileBytes = 256 * kTBK * 2;  // 16 KB per operand per stage
+constexpr uint32_t kXcds = 8;       // accelerator complex dies, each with its own L2
+constexpr uint32_t kXcdSlots = 32;  // resident workgroups per XCD (32 CUs, one workgroup each)
+constexpr int kGroupM = 4;          // m-tiles per group of the tile order
 
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
@@ -82,12 +85,25 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // ---- INT4 weight rows -------------------------------------------------
-// This thread's 16 code bytes and its 2-byte group scale, read from LDS
-// (both written there by direct-to-LDS loads of its own wavefront).
-__device__ __forceinline__ void ds_read_codes(uint32_t caddr, uint32_t saddr, u32x4_t& c, uint32_t& sbits) {
-    asm volatile("ds_read_b128 %0, %2\n\tds_read_u16 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-                 : "=v"(c), "=v"(sbits)
-                 : "v"(caddr), "v"(saddr));
+// Four code words (8 INT4 codes each) of this thread, one from each of four
+// code rows (word addresses c0 + 256 j), read from LDS where the wavefront's
+// own direct-to-LDS loads put them.  The outputs are early-clobber: a load's
+// result may land before the next load of the group has read the address.
+__device__ __forceinline__ void ds_read_codes(uint32_t c0, uint32_t& w0, uint32_t& w1, uint32_t& w2, uint32_t& w3) {
+    asm volatile(
+        "ds_read_b32 %0, %4\n\tds_read_b32 %1, %4 offset:256\n\t"
+        "ds_read_b32 %2, %4 offset:512\n\tds_read_b32 %3, %4 offset:768\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3)
+        : "v"(c0));
+}
+// The matching four bf16 group scales (256 bytes apart in the scale ring),
+// zero-extended.
+__device__ __forceinline__ void ds_read_scales(uint32_t s0, uint32_t& a, uint32_t& b, uint32_t& c, uint32_t& d) {
+    asm volatile(
+        "ds_read_u16 %0, %4\n\tds_read_u16 %1, %4 offset:256\n\t"
+        "ds_read_u16 %2, %4 offset:512\n\tds_read_u16 %3, %4 offset:768\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d)
+        : "v"(s0));
 }
 
 __device__ __forceinline__ void ds_write16(uint32_t addr, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -95,31 +111,26 @@ __device__ __forceinline__ void ds_write16(uint32_t addr, uint32_t a, uint32_t b
     asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
-// 32 INT4 codes of one tile row and stage (16 bytes; byte j of word w holds
-// k = 8w + 2j in its low nibble and k = 8w + 2j + 1 in its high nibble) with
-// their group's bf16 scale -> 32 bf16 values bf16(q * s), written as the
-// row's four 16-byte logical segments into their swizzled LDS slots.
+// One code word (8 INT4 codes: byte j holds k = 2j in its low nibble and
+// k = 2j + 1 in its high nibble) with its group's bf16 scale -> one 16-byte
+// tile segment of 8 bf16 values bf16(q * s), written to LDS at `addr`.
 // q * s is formed exactly as fma(q + 8, s, -8 s) ((q + 8) * s has at most 12
 // significant bits) and rounded once, to nearest even.
-__device__ __forceinline__ void dequant_row_to_lds(u32x4_t c, uint32_t sbits, uint32_t row_addr, int swz) {
+__device__ __forceinline__ void dequant_word_to_lds(uint32_t word, uint32_t sbits, uint32_t addr) {
     const float s = bf16_bits_to_float(sbits);
     const float m8s = -8.0f * s;
-    const uint32_t words[4] = {c.x, c.y, c.z, c.w};
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const uint32_t lo = (word & 0x0f0f0f0fu) ^ 0x08080808u;         // q + 8 of even k
+    const uint32_t hi = ((word >> 4) & 0x0f0f0f0fu) ^ 0x08080808u;  // q + 8 of odd k
+    uint32_t packed[4];
 #pragma unroll
-    for (int seg = 0; seg < 4; ++seg) {
-        const uint32_t lo = (words[seg] & 0x0f0f0f0fu) ^ 0x08080808u;         // q + 8 of even k
-        const uint32_t hi = ((words[seg] >> 4) & 0x0f0f0f0fu) ^ 0x08080808u;  // q + 8 of odd k
-        uint32_t packed[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float a = __builtin_fmaf((float)((lo >> (8 * j)) & 0xffu), s, m8s);
-            const float b = __builtin_fmaf((float)((hi >> (8 * j)) & 0xffu), s, m8s);
-            const bf16x2_t v = {(__bf16)a, (__bf16)b};
-            packed[j] = __builtin_bit_cast(uint32_t, v);
-        }
-        ds_write16(row_addr + 16 * (seg ^ swz), packed[0], packed[1], packed[2], packed[3]);
+    for (int j = 0; j < 4; ++j) {
+        const float a = __builtin_fmaf((float)((lo >> (8 * j)) & 0xffu), s, m8s);
+        const float b = __builtin_fmaf((float)((hi >> (8 * j)) & 0xffu), s, m8s);
+        const bf16x2_t v = {(__bf16)a, (__bf16)b};
+        packed[j] = __builtin_bit_cast(uint32_t, v);
     }
+    ds_write16(addr, packed[0], packed[1], packed[2], packed[3]);
 }
 
 // One workgroup tile: 256 weight rows x XROWS dispatch rows, wavefront w
@@ -262,10 +273,11 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
             compute(kt % kStages);
         }
     } else {
-        // INT4: thread t dequantises weight-tile row t.  Its 16 bytes of codes
-        // for stage j, C(j), are copied at step j-4 into code slot j % 4 by one
-        // direct-to-LDS load per wavefront (lane L's bytes land at 16 L of the
-        // wavefront's 1 KB, so only the wavefront's own vmcnt guards them),
+        // INT4: the 16 code bytes per weight-tile row for stage j, C(j), are
+        // copied at step j-4 into code slot j % 4 (one direct-to-LDS load per
+        // wavefront: lane L's bytes land at 16 L of the wavefront's 1 KB, and
+        // each wavefront dequantises only the rows it copied itself, so its own
+        // vmcnt guards them),
         // and the dispatch rows X(j) at step j-3, spread evenly over the four
         // wavefronts (XROWS / 64 loads each).  A wavefront's loads thus go out
         // in the order
@@ -285,7 +297,9 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
         constexpr int XL = XROWS / 64;  // dispatch-row loads per wavefront per stage
         const char* cbase = reinterpret_cast<const char*>(Wexp);
         const char* sbase = reinterpret_cast<const char*>(Wsc);
-        const uint32_t wrow = (uint32_t)min(n0 + tid, N - 1);
+        // lane L of wavefront w copies the codes (and scales) of weight-tile
+        // row 64 (L / 16) + 16 w + L % 16: the rows this wavefront dequantises
+        const uint32_t wrow = (uint32_t)min(n0 + 64 * (lane >> 4) + 16 * wave + (lane & 15), N - 1);
         const uint32_t coff = wrow * ((uint32_t)K / 2);
         const uint32_t soff = wrow * ((uint32_t)K / 128) * 2;
         // rows past the tile's dispatch rows are clamped (as above)
@@ -307,10 +321,19 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
         auto issue_scales = [&](int blk) {  // groups 8 blk .. 8 blk + 7 (stages 32 blk .. 32 blk + 31)
             copy_rows_to_lds(sbase, soff + (uint32_t)blk * 16, &St[blk & 1][wave * 1024]);
         };
-        const uint32_t cread = lds_addr(Ct[0]) + (uint32_t)tid * 16;
-        const uint32_t sread = lds_addr(St[0]) + (uint32_t)tid * 16;
-        const uint32_t wdst = (uint32_t)tid * 64;
-        const int swz = (tid >> 2) & 3;
+        // Dequantisation: thread (wavefront w, lane l) writes 16-byte physical
+        // slot l & 3 of weight-tile rows 64 j + 16 w + l / 4, j = 0..3, so each
+        // of its LDS stores covers 1 KB contiguously (free of bank conflicts);
+        // that slot holds logical segment lseg of every one of those rows.  Row
+        // 64 j + 16 w + r was copied by lane 16 j + r of this wavefront: its
+        // codes sit at 1024 w + 256 j + 16 r of the code slot.
+        const uint32_t cread = lds_addr(Ct[0]) + 1024 * wave + 16 * (lane >> 2) + 4 * lseg;
+        const uint32_t sread = lds_addr(St[0]) + 1024 * wave + 16 * (lane >> 2);
+        const uint32_t wdst = 1024 * wave + 16 * lane;
+        uint32_t sc0, sc1, sc2, sc3;  // group scales of this thread's four rows
+        auto read_scales = [&](int g) {
+            ds_read_scales(sread + (uint32_t)((g >> 3) & 1) * 4096 + (uint32_t)(g & 7) * 2, sc0, sc1, sc2, sc3);
+        };
         // rem = stages after s (>= 0); the counts follow the issue order above
         auto wait_x = [&](int rem) {
             if (rem >= 3) wait_vmcnt<3 + 2 * XL>();
@@ -325,12 +348,14 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
             else if (rem == 2) wait_vmcnt<1 + 2 * XL>();
             else wait_vmcnt<XL>();
         };
-        auto dequant = [&](int j) {  // stage j's codes and scale -> LDS slot j % 4
-            u32x4_t c;
-            uint32_t sc;
-            ds_read_codes(cread + (uint32_t)(j % kStages) * 4096,
-                          sread + (uint32_t)((j >> 5) & 1) * 4096 + (uint32_t)((j >> 2) & 7) * 2, c, sc);
-            dequant_row_to_lds(c, sc, lds_addr(Wt[j % kStages]) + wdst, swz);
+        auto dequant = [&](int j) {  // stage j's codes -> LDS slot j % 4 (scales of group j / 4 loaded)
+            uint32_t w0, w1, w2, w3;
+            ds_read_codes(cread + (uint32_t)(j % kStages) * 4096, w0, w1, w2, w3);
+            const uint32_t wb = lds_addr(Wt[j % kStages]) + wdst;
+            dequant_word_to_lds(w0, sc0, wb);
+            dequant_word_to_lds(w1, sc1, wb + 4096);
+            dequant_word_to_lds(w2, sc2, wb + 8192);
+            dequant_word_to_lds(w3, sc3, wb + 12288);
         };
         // prologue
         issue_scales(0);
@@ -342,6 +367,7 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
         issue_xe(2, 2);
         issue_c(3);
         wait_c(4);
+        read_scales(0);
         dequant(0);
 
         // one step; J = s % 4 (static), rem = nk - 1 - s (static in each call below)
@@ -353,6 +379,7 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
             if (rem >= 4) issue_c(s + 4);
             if (rem >= 1) {
                 wait_c(rem);
+                if (J == 3) read_scales((s + 1) >> 2);  // stage s + 1 opens a new group
                 dequant(s + 1);
             }
             compute(J);
@@ -414,10 +441,26 @@ gemm_tiled_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_
     // uses AGPRs, so it gives the MFMAs their AGPR-accumulator form (the
     // accumulators live in AGPRs, operands in VGPRs).
     asm volatile("" ::: "a0");
-    const int mt = blockIdx.x / ntiles_n;
-    const int nt = blockIdx.x - mt * ntiles_n;
+    // Tile order.  Workgroups go to the 8 XCDs in turn (block b to XCD b % 8)
+    // and each XCD keeps 32 of them resident (one per CU), so block b is
+    // given tile ((b / 8) / 32 * 8 + b % 8) * 32 + (b / 8) % 32: each XCD
+    // works through runs of 32 consecutive tiles.  Tiles are numbered in
+    // groups of kGroupM m-tiles, m fastest, so a run of 32 covers 4 m-tiles x
+    // 8 n-tiles and every weight and dispatch-row slab it streams is read from
+    // that XCD's L2 by 4 or 8 workgroups.
+    const MtileScan scan = scan_mtiles(offsets, E, kTBM);
+    const uint32_t b = blockIdx.x, xcd = b % kXcds, i = b / kXcds;
+    const uint32_t t = ((i / kXcdSlots) * kXcds + xcd) * kXcdSlots + i % kXcdSlots;
+    const int M = scan.total;
+    if (t >= (uint32_t)M * (uint32_t)ntiles_n) return;
+    const int group = (int)t / (kGroupM * ntiles_n);
+    const int first_m = group * kGroupM;
+    const int gm = min(kGroupM, M - first_m);
+    const int local = (int)t - first_m * ntiles_n;
+    const int mt = first_m + local % gm;
+    const int nt = local / gm;
     int e, p0, rows;
-    if (!find_mtile(offsets, E, kTBM, mt, &e, &p0, &rows)) return;
+    lookup_mtile(scan, offsets, kTBM, mt, &e, &p0, &rows);
     e = __builtin_amdgcn_readfirstlane(e);  // uniform across the workgroup: keep the bases scalar
     p0 = __builtin_amdgcn_readfirstlane(p0);
     rows = __builtin_amdgcn_readfirstlane(rows);
@@ -438,7 +481,9 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
     const int64_t Tk = a.T * a.k;
     const int64_t max_mtiles = Tk / kTBM + (Tk < a.E ? Tk : a.E);
     const int ntiles_n = (int)((a.N + kTBN - 1) / kTBN);
-    const int64_t blocks = max_mtiles * ntiles_n;
+    // whole rounds of kXcds * kXcdSlots blocks keep the tile order a bijection
+    const int64_t round = kXcds * kXcdSlots;
+    const int64_t blocks = (max_mtiles * ntiles_n + round - 1) / round * round;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const uint16_t* A = static_cast<const uint16_t*>(a.A);
