@@ -4,18 +4,17 @@
 // W2, so one kernel serves all experts; P3 §4.2 notes the per-expert work is
 // really a grouped GEMM over the tokens scattered to each expert, and P2 §3.3
 // credits fusing the activation into the expert GEMM.  Here:
-//   workgroup tile = 256 weight rows x 256 dispatch rows (one expert), K in
-//   stages of 32;
+//   workgroup tile = 256 weight rows x 256 dispatch rows (one expert);
 //   tiles go straight from HBM/L2 into LDS with gfx950's global_load_lds
-//   (16 bytes per lane, no register staging) through a ring of four 32 KB
-//   stages: stage k+3 streams in while stage k is multiplied (about 1.3 us of
-//   MFMA work hides the load latency), one barrier per stage.  INT4 weights
-//   (P1 §5.4, P2 §2.3) instead arrive in LDS as codes four stages ahead; the
-//   workgroup turns them into bf16(q * s) in the same LDS layout, so the MFMA
-//   loop is shared.  Every 64-byte
-//   tile row keeps its four 16-byte segments in slots permuted by
-//   (row >> 2) & 3 (an XOR swizzle), so the loads, the dequantised stores and
-//   the 32-row MFMA fragment reads are free of LDS bank conflicts;
+//   (16 bytes per lane, no register staging).  bf16 weights: K-stages of 64,
+//   so every tile row of a stage is one whole 128-byte line, double-buffered
+//   (2 x 64 KB).  INT4 weights (P1 §5.4, P2 §2.3): K-stages of 32 in a ring
+//   of four, the dispatch rows three stages ahead and the codes four; the
+//   workgroup turns each stage's codes into bf16(q * s) in LDS, in the layout
+//   the bf16 tiles use, so the MFMA step is the same.  One barrier per stage.
+//   Tile rows keep their 16-byte segments in XOR-permuted slots, so the
+//   loads, the dequantised stores and the 32-row MFMA fragment reads are free
+//   of LDS bank conflicts;
 //   4 wavefronts in a 2 x 2 arrangement, each 128 x 128 outputs as 16 MFMA
 //   32x32x16 bf16 tiles with fp32 accumulation (256 accumulators in AGPRs:
 //   64 flops per byte read from LDS); an expert's last, partial tile uses a
@@ -36,9 +35,6 @@ constexpr int kTBM = 256;   // dispatch rows per tile
 constexpr int kTBK = 32;    // K per stage (64 bytes of every tile row)
 constexpr int kStages = 4;  // LDS ring: stage k+3 streams in while stage k is multiplied
 constexpr int kTileBytes = 256 * kTBK * 2;  // 16 KB per operand per stage
-constexpr uint32_t kXcds = 8;       // accelerator complex dies, each with its own L2
-constexpr uint32_t kXcdSlots = 32;  // resident workgroups per XCD (32 CUs, one workgroup each)
-constexpr int kGroupM = 4;          // m-tiles per group of the tile order
 
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
@@ -131,6 +127,37 @@ __device__ __forceinline__ void dequant_word_to_lds(uint32_t word, uint32_t sbit
         packed[j] = __builtin_bit_cast(uint32_t, v);
     }
     ds_write16(addr, packed[0], packed[1], packed[2], packed[3]);
+}
+
+// Epilogue: element v of acc[i][j] is D[n = wn + 32i + 8(v/4) + 4h + (v%4)][m = wm + 32j + r];
+// GEMM1 stores bf16 GeLU(D), GEMM2 stores fp32 D, for rows below `rows` and n below N.
+template <int WHICH, int TI, int TJ>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[TI][TJ], void* __restrict__ out, int N, int n0, int p0,
+                                           int rows, int wn, int wm, int r, int h) {
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+        const int m = wm + 32 * j + r;
+        if (m >= rows) continue;
+        const int64_t orow = (int64_t)(p0 + m) * N;
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn + 32 * i + 8 * q + 4 * h;
+                if (n >= N) continue;
+                const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
+                const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+                if constexpr (WHICH == 1) {
+                    uint2 packed;
+                    packed.x = float_to_bf16_bits(gelu_erf(v0)) | (float_to_bf16_bits(gelu_erf(v1)) << 16);
+                    packed.y = float_to_bf16_bits(gelu_erf(v2)) | (float_to_bf16_bits(gelu_erf(v3)) << 16);
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + orow + n) = packed;
+                } else {
+                    *reinterpret_cast<float4*>(static_cast<float*>(out) + orow + n) = make_float4(v0, v1, v2, v3);
+                }
+            }
+        }
+    }
 }
 
 // One workgroup tile: 256 weight rows x XROWS dispatch rows, wavefront w
@@ -398,31 +425,130 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
         step(s0 + 3, 3, 0);
     }
 
-    // epilogue: element v of acc[i][j] is D[n = wn + 32i + 8(v/4) + 4h + (v%4)][m = wm + 32j + r]
+    store_tile<WHICH, TI, TJ>(acc, out, N, n0, p0, rows, wn, wm, r, h);
+}
+
+// bf16 weights, K-stages of 64: each stage holds 128 bytes (one whole
+// 128-byte line) of every tile row, 32 KB per operand, double-buffered in
+// the same 128 KB of LDS.  Copying whole lines runs the direct-to-LDS loads
+// about 1.5x faster than half lines (measured on L2-resident data: 16 rows x
+// 64 B per instruction reach 21-24 TB/s, 8 rows x 128 B 33 TB/s).  The
+// eight 16-byte segments of a row sit in slots permuted by (row >> 1) & 7,
+// so 16 consecutive rows read at one logical segment hit 16 distinct bank
+// groups.  Step k waits for its own loads, one barrier publishes stage k and
+// frees the other buffer, stage k+1 is issued into it and stage k is
+// multiplied (four k-substeps of 16).  Logical segment seg of tile row
+// `row` sits at byte row * 128 + 16 * (seg ^ ((row >> 1) & 7)) of a stage.
+
+template <int WHICH, int TI, int TJ, int XROWS>
+__device__ __forceinline__ void tile_gemm_bf16_bk64(uint8_t* Wl, uint8_t* Xl, const uint16_t* __restrict__ A,
+                                                    const int32_t* __restrict__ a_rows, const void* Wexp,
+                                                    void* __restrict__ out, int N, int K, int n0, int p0, int rows) {
+    constexpr int WN_WAVES = 256 / (32 * TI);
+    constexpr uint32_t kStage = 256 * 128;  // bytes per operand per stage
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // This wavefront copies tile rows [64 w, 64 w + 64) of the weight tile,
+    // and of the dispatch tile if they lie inside XROWS: 8 instructions of 8
+    // rows x 128 bytes per operand.  Lane L of instruction i takes physical
+    // slot L % 8 of row 64 w + 8 i + L / 8.  Rows past N or past the tile's
+    // dispatch rows are clamped to a valid row (their outputs are not stored).
+    const bool xload = 64 * wave < XROWS;
+    const char* wbase = reinterpret_cast<const char*>(Wexp);
+    const char* xbase = reinterpret_cast<const char*>(A);
+    const uint32_t rowbytes = (uint32_t)K * 2;
+    uint32_t woff[8], xoff[8];
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-        const int m = wm + 32 * j + r;
-        if (m >= rows) continue;
-        const int64_t orow = (int64_t)(p0 + m) * N;
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn + 32 * i + 8 * q + 4 * h;
-                if (n >= N) continue;
-                const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
-                const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-                if constexpr (WHICH == 1) {
-                    uint2 packed;
-                    packed.x = float_to_bf16_bits(gelu_erf(v0)) | (float_to_bf16_bits(gelu_erf(v1)) << 16);
-                    packed.y = float_to_bf16_bits(gelu_erf(v2)) | (float_to_bf16_bits(gelu_erf(v3)) << 16);
-                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + orow + n) = packed;
-                } else {
-                    *reinterpret_cast<float4*>(static_cast<float*>(out) + orow + n) = make_float4(v0, v1, v2, v3);
-                }
-            }
-        }
+    for (int i = 0; i < 8; ++i) {
+        const int trow = 64 * wave + 8 * i + (lane >> 3);
+        const uint32_t seg = (uint32_t)((lane & 7) ^ ((trow >> 1) & 7));
+        woff[i] = (uint32_t)min(n0 + trow, N - 1) * rowbytes + 16 * seg;
+        const int drow = min(trow, rows - 1);
+        const uint32_t arow = (WHICH == 1) ? (uint32_t)a_rows[p0 + drow] : (uint32_t)(p0 + drow);
+        xoff[i] = arow * rowbytes + 16 * seg;
     }
+    auto issue = [&](int kt, int buf) {
+        const uint32_t kb = (uint32_t)kt * 128;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) copy_rows_to_lds(wbase, woff[i] + kb, Wl + buf * kStage + (64 * wave + 8 * i) * 128);
+        if (xload) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                copy_rows_to_lds(xbase, xoff[i] + kb, Xl + buf * kStage + (64 * wave + 8 * i) * 128);
+        }
+    };
+
+    const int wn = (wave % WN_WAVES) * (32 * TI);
+    const int wm = (wave / WN_WAVES) * (32 * TJ);
+    const int r = lane & 31;
+    const int h = lane >> 5;
+    f32x16 acc[TI][TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    // every fragment row of this lane is r modulo 16, so one slot permutation serves all
+    uint32_t wrow_off[TI], xrow_off[TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) wrow_off[i] = (uint32_t)(wn + 32 * i + r) * 128;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) xrow_off[j] = (uint32_t)(wm + 32 * j + r) * 128;
+    const uint32_t swz = (uint32_t)((r >> 1) & 7);
+    // two k-substeps: lane half h reads logical segments 2 ks + h, ks = 2 kp, 2 kp + 1
+    auto compute_pair = [&](uint32_t wb, uint32_t xb, int kp) {
+        const uint32_t sa = 16 * ((uint32_t)(4 * kp + h) ^ swz), sb = 16 * ((uint32_t)(4 * kp + 2 + h) ^ swz);
+        bf16x8 wf[2][TI], xf[2][TJ];
+#pragma unroll
+        for (int i = 0; i < TI; ++i) wf[0][i] = ds_read16(wb + wrow_off[i] + sa);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) xf[0][j] = ds_read16(xb + xrow_off[j] + sa);
+#pragma unroll
+        for (int i = 0; i < TI; ++i) wf[1][i] = ds_read16(wb + wrow_off[i] + sb);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) xf[1][j] = ds_read16(xb + xrow_off[j] + sb);
+        if constexpr (TI + TJ == 8) {
+            asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(wf[0][0]), "+v"(wf[0][1]), "+v"(wf[0][2]), "+v"(wf[0][3]),
+                         "+v"(xf[0][0]), "+v"(xf[0][1]), "+v"(xf[0][2]), "+v"(xf[0][3]));
+        } else if constexpr (TI + TJ == 6) {
+            asm volatile("s_waitcnt lgkmcnt(6)" : "+v"(wf[0][0]), "+v"(wf[0][1]), "+v"(xf[0][0]), "+v"(xf[0][1]),
+                         "+v"(xf[0][2]), "+v"(xf[0][3]));
+        } else {
+            asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(wf[0][0]), "+v"(wf[0][1]), "+v"(xf[0][0]), "+v"(xf[0][1]));
+        }
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32x32x16(wf[0][i], xf[0][j], acc[i][j]);
+        if constexpr (TI + TJ == 8) {
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(wf[1][0]), "+v"(wf[1][1]), "+v"(wf[1][2]), "+v"(wf[1][3]),
+                         "+v"(xf[1][0]), "+v"(xf[1][1]), "+v"(xf[1][2]), "+v"(xf[1][3]));
+        } else if constexpr (TI + TJ == 6) {
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(wf[1][0]), "+v"(wf[1][1]), "+v"(xf[1][0]), "+v"(xf[1][1]),
+                         "+v"(xf[1][2]), "+v"(xf[1][3]));
+        } else {
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(wf[1][0]), "+v"(wf[1][1]), "+v"(xf[1][0]), "+v"(xf[1][1]));
+        }
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32x32x16(wf[1][i], xf[1][j], acc[i][j]);
+    };
+
+    const int nk = K / 64;
+    issue(0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_vmcnt<0>();  // stage kt is the only one in flight
+        barrier();
+        if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+        const uint32_t wb = lds_addr(Wl + (kt & 1) * kStage), xb = lds_addr(Xl + (kt & 1) * kStage);
+        compute_pair(wb, xb, 0);
+        compute_pair(wb, xb, 1);
+    }
+    store_tile<WHICH, TI, TJ>(acc, out, N, n0, p0, rows, wn, wm, r, h);
 }
 
 // W: the experts' weights, W_stride bytes apart (bf16 [N][K] or INT4 codes
@@ -441,24 +567,14 @@ gemm_tiled_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_
     // uses AGPRs, so it gives the MFMAs their AGPR-accumulator form (the
     // accumulators live in AGPRs, operands in VGPRs).
     asm volatile("" ::: "a0");
-    // Tile order.  Workgroups go to the 8 XCDs in turn (block b to XCD b % 8)
-    // and each XCD keeps 32 of them resident (one per CU), so block b is
-    // given tile ((b / 8) / 32 * 8 + b % 8) * 32 + (b / 8) % 32: each XCD
-    // works through runs of 32 consecutive tiles.  Tiles are numbered in
-    // groups of kGroupM m-tiles, m fastest, so a run of 32 covers 4 m-tiles x
-    // 8 n-tiles and every weight and dispatch-row slab it streams is read from
-    // that XCD's L2 by 4 or 8 workgroups.
+    // Tiles in m-major order: the workgroups running at one time (one per CU,
+    // handed to the XCDs in turn) share the dispatch-row tiles of one or two
+    // m-tiles and stream different weight tiles.  (Grouping 4-16 m-tiles per
+    // XCD to share weight tiles in L2 measured no faster.)
     const MtileScan scan = scan_mtiles(offsets, E, kTBM);
-    const uint32_t b = blockIdx.x, xcd = b % kXcds, i = b / kXcds;
-    const uint32_t t = ((i / kXcdSlots) * kXcds + xcd) * kXcdSlots + i % kXcdSlots;
-    const int M = scan.total;
-    if (t >= (uint32_t)M * (uint32_t)ntiles_n) return;
-    const int group = (int)t / (kGroupM * ntiles_n);
-    const int first_m = group * kGroupM;
-    const int gm = min(kGroupM, M - first_m);
-    const int local = (int)t - first_m * ntiles_n;
-    const int mt = first_m + local % gm;
-    const int nt = local / gm;
+    const int mt = blockIdx.x / ntiles_n;
+    const int nt = blockIdx.x - mt * ntiles_n;
+    if (mt >= scan.total) return;
     int e, p0, rows;
     lookup_mtile(scan, offsets, kTBM, mt, &e, &p0, &rows);
     e = __builtin_amdgcn_readfirstlane(e);  // uniform across the workgroup: keep the bases scalar
@@ -467,6 +583,15 @@ gemm_tiled_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_
     const int n0 = nt * kTBN;
     const void* Wexp = W + (int64_t)e * W_stride;
     const void* Wsc_e = (WQ == kINT4) ? (const void*)(Wsc + (int64_t)e * N * (K / 128)) : nullptr;
+    if constexpr (WQ == kBF16) {
+        if (rows > 128)
+            tile_gemm_bf16_bk64<WHICH, 4, 4, 256>(&Wt[0][0], &Xt[0][0], A, a_rows, Wexp, out, N, K, n0, p0, rows);
+        else if (rows > 64)
+            tile_gemm_bf16_bk64<WHICH, 2, 4, 128>(&Wt[0][0], &Xt[0][0], A, a_rows, Wexp, out, N, K, n0, p0, rows);
+        else
+            tile_gemm_bf16_bk64<WHICH, 2, 2, 64>(&Wt[0][0], &Xt[0][0], A, a_rows, Wexp, out, N, K, n0, p0, rows);
+        return;
+    }
     if (rows > 128)
         tile_gemm<WQ, WHICH, 4, 4, 256>(Wt, Xt, Ct, St, A, a_rows, Wexp, Wsc_e, out, N, K, n0, p0, rows);
     else if (rows > 64)
@@ -481,9 +606,7 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
     const int64_t Tk = a.T * a.k;
     const int64_t max_mtiles = Tk / kTBM + (Tk < a.E ? Tk : a.E);
     const int ntiles_n = (int)((a.N + kTBN - 1) / kTBN);
-    // whole rounds of kXcds * kXcdSlots blocks keep the tile order a bijection
-    const int64_t round = kXcds * kXcdSlots;
-    const int64_t blocks = (max_mtiles * ntiles_n + round - 1) / round * round;
+    const int64_t blocks = max_mtiles * ntiles_n;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const uint16_t* A = static_cast<const uint16_t*>(a.A);
