@@ -72,7 +72,8 @@ typedef enum moe_dtype {
 typedef enum moe_gemm_path {
     MOE_GEMM_AUTO = 0,       /* streaming when T <= 16 (or INT4 weights that the tiled kernel
                                 cannot take), tiled otherwise */
-    MOE_GEMM_STREAMING = 1,  /* weight-streaming kernel: 16-token MFMA tiles, every weight read once per 16 rows */
+    MOE_GEMM_STREAMING = 1,  /* weight-streaming kernel: every weight read once per 16 rows of an
+                                expert (T <= 16), 32 rows (T <= 32) or 64 rows */
     MOE_GEMM_TILED = 2       /* LDS-tiled MFMA kernel for many tokens per expert; INT4 weights need d and
                                 d_ff multiples of 1024 (else MOE_ERR_UNSUPPORTED) and 16-byte aligned scales */
 } moe_gemm_path;

@@ -70,7 +70,9 @@ struct MtileScan {
     int total;               // all m-tiles
 };
 
-__device__ __forceinline__ MtileScan scan_mtiles(const int32_t* __restrict__ offsets, int E, int BM) {
+// Only experts whose row count n satisfies rows_lo < n <= rows_hi get tiles.
+__device__ __forceinline__ MtileScan scan_mtiles(const int32_t* __restrict__ offsets, int E, int BM, int rows_lo = 0,
+                                                 int rows_hi = 0x7fffffff) {
     const int lane = threadIdx.x & 63;
     MtileScan s;
     int local = 0;
@@ -81,6 +83,7 @@ __device__ __forceinline__ MtileScan scan_mtiles(const int32_t* __restrict__ off
         if (e < E) {
             b = offsets[e];
             n = offsets[e + 1] - b;
+            if (n <= rows_lo || n > rows_hi) n = 0;
         }
         s.begin[j] = b;
         s.tiles[j] = (n + BM - 1) / BM;
@@ -128,8 +131,8 @@ __device__ __forceinline__ void lookup_mtile(const MtileScan& s, const int32_t* 
 // Returns false when mt lies beyond the last real tile.  Called by one whole
 // wavefront.
 __device__ __forceinline__ bool find_mtile(const int32_t* __restrict__ offsets, int E, int BM, int mt, int* expert,
-                                           int* pos0, int* rows) {
-    const MtileScan s = scan_mtiles(offsets, E, BM);
+                                           int* pos0, int* rows, int rows_lo = 0, int rows_hi = 0x7fffffff) {
+    const MtileScan s = scan_mtiles(offsets, E, BM, rows_lo, rows_hi);
     if (mt >= s.total) return false;
     lookup_mtile(s, offsets, BM, mt, expert, pos0, rows);
     return true;

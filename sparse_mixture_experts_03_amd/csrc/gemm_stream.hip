@@ -3,9 +3,10 @@
 // P2 §2.3: at decode sizes the cost of an expert is moving its weights (the
 // MoE layer there spends more time in weight traffic than in GEMM, and the
 // weights never stay in cache).  This kernel therefore reads every weight of
-// every active expert exactly once per 16 routed tokens and does the
-// arithmetic on MFMA so that the matrix cores never limit the stream:
-//   workgroup = 16*NB weight rows x one 16-row tile of the dispatch order;
+// every active expert exactly once per 16*MT routed tokens (MT = 1, 2 or 4)
+// and does the arithmetic on MFMA so that the matrix cores never limit the
+// stream:
+//   workgroup = 16*NB weight rows x one 16*MT-row tile of the dispatch order;
 //   its four wavefronts split K; each streams its rows in stages of 256 or 512
 //   bytes per row with fully coalesced non-temporal 16-byte loads (a wavefront
 //   instruction reads whole 128-byte lines), parks the stage in a private
@@ -93,32 +94,44 @@ __device__ __forceinline__ void store_tile(void* out, int64_t N, int p0, int row
     }
 }
 
-template <int WQ, int WHICH, int NB, int kStageBytes>
+// Only experts holding n rows with rows_lo < n <= rows_hi are multiplied here.
+template <int WQ, int WHICH, int NB, int MT, int kStageBytes>
 __global__ void __launch_bounds__(256)
 gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
                    const int32_t* __restrict__ offsets, int E, const uint8_t* __restrict__ W,
                    const uint16_t* __restrict__ Wsc, int64_t W_stride, void* __restrict__ out, int N, int K,
-                   int ntiles_n) {
+                   int ntiles_n, int rows_lo, int rows_hi) {
     constexpr int ROWS = 16 * NB;              // weight rows per workgroup
     constexpr int SEGS = kStageBytes / 16;     // 16-byte segments per row per stage
     constexpr int LROW = kStageBytes + 16;     // padded LDS row (conflict-free 16-row column reads)
     constexpr int LOADS = ROWS * SEGS / 64;    // 16-byte loads per lane per stage
-    __shared__ __attribute__((aligned(16))) uint8_t stage_lds[4][ROWS * LROW];
-    __shared__ f32x4 red[3][NB][64];
+    // per-wavefront stage buffers; after the K loop the same LDS holds the partial tiles
+    constexpr int kStageLds = 4 * ROWS * LROW;
+    constexpr int kRedBytes = 3 * NB * MT * 64 * 16;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kStageLds > kRedBytes ? kStageLds : kRedBytes];
+    uint8_t (*stage_lds)[ROWS * LROW] = reinterpret_cast<uint8_t (*)[ROWS * LROW]>(smem);
+    f32x4 (*red)[NB * MT][64] = reinterpret_cast<f32x4 (*)[NB * MT][64]>(smem);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int mt = blockIdx.x / ntiles_n;
     const int nt = blockIdx.x - mt * ntiles_n;
     int e, p0, rows;
-    if (!find_mtile(offsets, E, kStreamBM, mt, &e, &p0, &rows)) return;
+    if (!find_mtile(offsets, E, kStreamBM * MT, mt, &e, &p0, &rows, rows_lo, rows_hi)) return;
 
     const int r = lane & 15;
     const int g = lane >> 4;
     const int n0 = nt * ROWS;
-    const bool mvalid = r < rows;
-    int64_t arow = 0;
-    if (mvalid) arow = (WHICH == 1) ? (int64_t)a_rows[p0 + r] : (int64_t)(p0 + r);
-    const uint16_t* xrow = A + arow * K;
+    // dispatch row 16 c + r of the tile feeds MFMA column tile c
+    bool mvalid[MT];
+    const uint16_t* xrow[MT];
+#pragma unroll
+    for (int c = 0; c < MT; ++c) {
+        const int m = 16 * c + r;
+        mvalid[c] = m < rows;
+        int64_t arow = 0;
+        if (mvalid[c]) arow = (WHICH == 1) ? (int64_t)a_rows[p0 + m] : (int64_t)(p0 + m);
+        xrow[c] = A + arow * K;
+    }
     const int64_t row_bytes = (WQ == kBF16) ? (int64_t)K * 2 : (int64_t)K / 2;
     const uint8_t* Wblk = W + (int64_t)e * W_stride + (int64_t)n0 * row_bytes;
     uint8_t* lds = stage_lds[wave];
@@ -148,9 +161,11 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
         }
     };
 
-    f32x4 acc[NB];
+    f32x4 acc[NB][MT];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int c = 0; c < MT; ++c) acc[b][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     // INT4 scales: this lane's output rows n0 + 16b + 4g + i
     const int groups = K / 128;
@@ -172,12 +187,15 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     const int koff = cc * 64 + (2 * g + s) * 8;
-                    const uint4 xa = mvalid ? ld16(xrow + kbase + koff) : zero4;
+                    uint4 xa[MT];
+#pragma unroll
+                    for (int c = 0; c < MT; ++c) xa[c] = mvalid[c] ? ld16(xrow[c] + kbase + koff) : zero4;
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
                         const uint4 wa =
                             *reinterpret_cast<const uint4*>(lds + (16 * b + r) * LROW + cc * 128 + (2 * g + s) * 16);
-                        acc[b] = mfma16x16x32(as_bf16x8(wa), as_bf16x8(xa), acc[b]);
+#pragma unroll
+                        for (int c = 0; c < MT; ++c) acc[b][c] = mfma16x16x32(as_bf16x8(wa), as_bf16x8(xa[c]), acc[b][c]);
                     }
                 }
             }
@@ -186,32 +204,41 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
             const int gbase = (int)(s0 / 64);
             for (int cc = 0; cc < valid / 64; ++cc) {
                 const int grp = gbase + cc;
-                uint4 xv[4];
+                uint4 xv[MT][4];
 #pragma unroll
-                for (int s = 0; s < 4; ++s) xv[s] = mvalid ? ld16(xrow + grp * 128 + 32 * g + 8 * s) : zero4;
-                f32x4 t[NB], sx = (f32x4){0.f, 0.f, 0.f, 0.f};
+                for (int c = 0; c < MT; ++c)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) xv[c][s] = mvalid[c] ? ld16(xrow[c] + grp * 128 + 32 * g + 8 * s) : zero4;
+                f32x4 t[NB][MT], sx[MT];
                 uint4 q[NB];
 #pragma unroll
+                for (int c = 0; c < MT; ++c) sx[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
                 for (int b = 0; b < NB; ++b) {
-                    t[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int c = 0; c < MT; ++c) t[b][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
                     q[b] = *reinterpret_cast<const uint4*>(lds + (16 * b + r) * LROW + cc * 64 + 16 * g);
                 }
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    const bf16x8 xb = as_bf16x8(xv[s]);
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
                         const uint32_t word = s == 0 ? q[b].x : s == 1 ? q[b].y : s == 2 ? q[b].z : q[b].w;
-                        t[b] = mfma16x16x32(int4x8_to_bf16_offset136(word), xb, t[b]);
+                        const bf16x8 wq = int4x8_to_bf16_offset136(word);
+#pragma unroll
+                        for (int c = 0; c < MT; ++c) t[b][c] = mfma16x16x32(wq, as_bf16x8(xv[c][s]), t[b][c]);
                     }
-                    sx = mfma16x16x32(as_bf16x8(ones), xb, sx);
+#pragma unroll
+                    for (int c = 0; c < MT; ++c) sx[c] = mfma16x16x32(as_bf16x8(ones), as_bf16x8(xv[c][s]), sx[c]);
                 }
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const float sv = bf16_bits_to_float(sc[(int64_t)(16 * b + i) * groups + grp]);
-                        acc[b][i] = fmaf(sv, fmaf(-136.0f, sx[i], t[b][i]), acc[b][i]);
+#pragma unroll
+                        for (int c = 0; c < MT; ++c)
+                            acc[b][c][i] = fmaf(sv, fmaf(-136.0f, sx[c][i], t[b][c][i]), acc[b][c][i]);
                     }
             }
         }
@@ -220,27 +247,32 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
         for (int i = 0; i < LOADS; ++i) cur[i] = nxt[i];
     }
 
-    // fixed-order reduction of the four K-slices
+    // fixed-order reduction of the four K-slices (in the stage buffers, once every wavefront is done with them)
+    __syncthreads();
     if (wave > 0) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) red[wave - 1][b][lane] = acc[b];
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int c = 0; c < MT; ++c) red[wave - 1][b * MT + c][lane] = acc[b][c];
     }
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            f32x4 v = acc[b];
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int w = 0; w < 3; ++w) v += red[w][b][lane];
-            store_tile<WHICH>(out, N, p0, rows, n0 + 16 * b, v, lane);
-        }
+            for (int c = 0; c < MT; ++c) {
+                f32x4 v = acc[b][c];
+#pragma unroll
+                for (int w = 0; w < 3; ++w) v += red[w][b * MT + c][lane];
+                store_tile<WHICH>(out, N, p0 + 16 * c, rows - 16 * c, n0 + 16 * b, v, lane);
+            }
     }
 }
 
-template <int WQ, int NB, int SB>
+template <int WQ, int NB, int MT, int SB>
 hipError_t launch_stream_nb(const GemmArgs& a, hipStream_t stream) {
     const int64_t Tk = a.T * a.k;
-    const int64_t max_mtiles = Tk / kStreamBM + (Tk < a.E ? Tk : a.E);
+    const int64_t max_mtiles = Tk / (kStreamBM * MT) + (Tk < a.E ? Tk : a.E);
     const int ntiles_n = (int)(a.N / (16 * NB));
     const int64_t blocks = max_mtiles * ntiles_n;
     if (blocks == 0) return hipSuccess;
@@ -250,20 +282,35 @@ hipError_t launch_stream_nb(const GemmArgs& a, hipStream_t stream) {
     const uint16_t* S = static_cast<const uint16_t*>(a.W_scales);
     dim3 grid((unsigned)blocks), block(256);
     if (a.which == 1)
-        hipLaunchKernelGGL((gemm_stream_kernel<WQ, 1, NB, SB>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W, S,
-                           a.W_stride, a.out, (int)a.N, (int)a.K, ntiles_n);
+        hipLaunchKernelGGL((gemm_stream_kernel<WQ, 1, NB, MT, SB>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E,
+                           W, S, a.W_stride, a.out, (int)a.N, (int)a.K, ntiles_n, a.rows_lo, a.rows_hi);
     else
-        hipLaunchKernelGGL((gemm_stream_kernel<WQ, 2, NB, SB>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W, S,
-                           a.W_stride, a.out, (int)a.N, (int)a.K, ntiles_n);
+        hipLaunchKernelGGL((gemm_stream_kernel<WQ, 2, NB, MT, SB>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E,
+                           W, S, a.W_stride, a.out, (int)a.N, (int)a.K, ntiles_n, a.rows_lo, a.rows_hi);
     return hipGetLastError();
+}
+
+// bf16 weights: 16 MT weight rows per workgroup for 16 MT dispatch rows, so
+// the activation rows (re-read by every workgroup from L2) never outweigh the
+// weights streamed from HBM; the wider tiles stage 128 bytes of each row (the
+// register double buffer stays at 8 loads per lane).  INT4: 32 weight rows.
+hipError_t launch_stream_bf16(const GemmArgs& a, hipStream_t stream) {
+    if (a.stream_mt == 1) return launch_stream_nb<kBF16, MOE_STREAM_NB_BF16, 1, MOE_STREAM_STAGE_BF16>(a, stream);
+    if (a.stream_mt == 2) return launch_stream_nb<kBF16, 2, 2, 128>(a, stream);
+    return launch_stream_nb<kBF16, 4, 4, 128>(a, stream);
+}
+hipError_t launch_stream_int4(const GemmArgs& a, hipStream_t stream) {
+    if (a.stream_mt == 1) return launch_stream_nb<kINT4, MOE_STREAM_NB_INT4, 1, MOE_STREAM_STAGE_INT4>(a, stream);
+    if (a.stream_mt == 2) return launch_stream_nb<kINT4, MOE_STREAM_NB_INT4, 2, MOE_STREAM_STAGE_INT4>(a, stream);
+    return launch_stream_nb<kINT4, MOE_STREAM_NB_INT4, 4, MOE_STREAM_STAGE_INT4>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream) {
     // N is a multiple of 64, so any NB in {1, 2, 4} tiles it exactly.
-    if (a.w_dtype == kBF16) return launch_stream_nb<kBF16, MOE_STREAM_NB_BF16, MOE_STREAM_STAGE_BF16>(a, stream);
-    return launch_stream_nb<kINT4, MOE_STREAM_NB_INT4, MOE_STREAM_STAGE_INT4>(a, stream);
+    if (a.w_dtype == kBF16) return launch_stream_bf16(a, stream);
+    return launch_stream_int4(a, stream);
 }
 
 }  // namespace moe

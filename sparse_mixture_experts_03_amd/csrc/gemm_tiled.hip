@@ -552,12 +552,13 @@ __device__ __forceinline__ void tile_gemm_bf16_bk64(uint8_t* Wl, uint8_t* Xl, co
 }
 
 // W: the experts' weights, W_stride bytes apart (bf16 [N][K] or INT4 codes
-// [N][K/2]); Wsc: INT4 scales bf16 [E][N][K/128] (unused for bf16).
+// [N][K/2]); Wsc: INT4 scales bf16 [E][N][K/128] (unused for bf16).  Only
+// experts holding more than rows_lo rows are multiplied here.
 template <int WQ, int WHICH>
 __global__ void __launch_bounds__(256, 1)
 gemm_tiled_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
                   const int32_t* __restrict__ offsets, int E, const uint8_t* __restrict__ W, int64_t W_stride,
-                  const uint16_t* __restrict__ Wsc, void* __restrict__ out, int N, int K, int ntiles_n) {
+                  const uint16_t* __restrict__ Wsc, void* __restrict__ out, int N, int K, int ntiles_n, int rows_lo) {
     __shared__ __attribute__((aligned(1024))) uint8_t Wt[kStages][kTileBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t Xt[kStages][kTileBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t Ct[WQ == kINT4 ? kStages : 1][4096];  // INT4 code ring
@@ -571,7 +572,7 @@ gemm_tiled_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_
     // handed to the XCDs in turn) share the dispatch-row tiles of one or two
     // m-tiles and stream different weight tiles.  (Grouping 4-16 m-tiles per
     // XCD to share weight tiles in L2 measured no faster.)
-    const MtileScan scan = scan_mtiles(offsets, E, kTBM);
+    const MtileScan scan = scan_mtiles(offsets, E, kTBM, rows_lo, 0x7fffffff);
     const int mt = blockIdx.x / ntiles_n;
     const int nt = blockIdx.x - mt * ntiles_n;
     if (mt >= scan.total) return;
@@ -617,17 +618,17 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
     if (a.w_dtype == kINT4) {
         if (a.which == 1)
             hipLaunchKernelGGL((gemm_tiled_kernel<kINT4, 1>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
-                               a.W_stride, S, a.out, N, K, ntiles_n);
+                               a.W_stride, S, a.out, N, K, ntiles_n, a.rows_lo);
         else
             hipLaunchKernelGGL((gemm_tiled_kernel<kINT4, 2>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
-                               a.W_stride, S, a.out, N, K, ntiles_n);
+                               a.W_stride, S, a.out, N, K, ntiles_n, a.rows_lo);
     } else {
         if (a.which == 1)
             hipLaunchKernelGGL((gemm_tiled_kernel<kBF16, 1>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
-                               a.W_stride, S, a.out, N, K, ntiles_n);
+                               a.W_stride, S, a.out, N, K, ntiles_n, a.rows_lo);
         else
             hipLaunchKernelGGL((gemm_tiled_kernel<kBF16, 2>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
-                               a.W_stride, S, a.out, N, K, ntiles_n);
+                               a.W_stride, S, a.out, N, K, ntiles_n, a.rows_lo);
     }
     return hipGetLastError();
 }

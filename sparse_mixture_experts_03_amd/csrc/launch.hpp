@@ -52,6 +52,8 @@ struct GemmArgs {
     int64_t T, N, K;        // T: tokens (rows = T * k)
     int E, k, w_dtype, act_dtype;
     int path;               // 1 streaming, 2 tiled
+    int rows_lo, rows_hi;   // only experts holding n rows, rows_lo < n <= rows_hi
+    int stream_mt;          // streaming kernel: 16-row dispatch tiles per workgroup (1, 2 or 4)
 };
 hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream);  // BF16 / INT4 weights
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);   // BF16 weights

@@ -92,6 +92,8 @@ Layout layout_of(const moe_config& c) {
 }
 
 // GEMM kernel for a config: 0 (F32 weights), MOE_GEMM_STREAMING or MOE_GEMM_TILED.
+// (Streaming experts of at most 64 rows while tiling the rest measured slower
+// than tiling all of them above 16 tokens.)
 int gemm_path_of(const moe_config& c) {
     if (c.w_dtype == MOE_DTYPE_F32) return 0;
     if (c.gemm_path != MOE_GEMM_AUTO) return c.gemm_path;
@@ -130,6 +132,10 @@ hipError_t run_gemm(const moe_config& c, int which, const void* A, const int32_t
     g.w_dtype = c.w_dtype;
     g.act_dtype = c.act_dtype;
     g.path = gemm_path_of(c);
+    g.rows_lo = 0;
+    g.rows_hi = 0x7fffffff;
+    // a token adds at most one row to an expert, so no expert holds more than T rows
+    g.stream_mt = c.T <= 16 ? 1 : c.T <= 32 ? 2 : 4;
     if (c.w_dtype == MOE_DTYPE_F32) return moe::launch_gemm_f32(g, stream);
     if (g.path == MOE_GEMM_STREAMING) return moe::launch_gemm_stream(g, stream);
     return moe::launch_gemm_tiled(g, stream);

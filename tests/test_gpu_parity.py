@@ -107,6 +107,9 @@ FORWARD_CASES = {
     "bf16-T150-d320-dff576-E6-ntail": (case(150, 320, 576, 6), [moe.GEMM_STREAMING, moe.GEMM_TILED]),
     "bf16-T40-d256-dff256-E256-k8": (case(40, 256, 256, 256, k=8), [moe.GEMM_STREAMING, moe.GEMM_TILED]),
     "bf16-T9-d256-dff512-E1-k1": (case(9, 256, 512, 1, k=1), [moe.GEMM_STREAMING, moe.GEMM_TILED]),
+    # streaming with 32-row (T <= 32) and 64-row dispatch tiles
+    "bf16-T24-d512-dff1024-E4": (case(24, 512, 1024, 4), [moe.GEMM_STREAMING]),
+    "int4-T30-d512-dff1024-E8": (case(30, 512, 1024, 8, w=INT4), [moe.GEMM_STREAMING]),
     "int4-T12-d512-dff1024-E8-gumbel": (case(12, 512, 1024, 8, w=INT4, tau=0.5, gumbel=True), [moe.GEMM_AUTO]),
     "int4-T200-d384-dff768-E8-gumbel": (case(200, 384, 768, 8, w=INT4, tau=0.5, gumbel=True), [moe.GEMM_AUTO]),
     # K = 1024 and 3072: one and three 32-stage scale blocks; skewed rows exercise all three tile heights
