@@ -31,13 +31,13 @@
 #define MOE_STREAM_NB_BF16 1   // 16-row weight tiles per workgroup, bf16 experts
 #endif
 #ifndef MOE_STREAM_NB_INT4
-#define MOE_STREAM_NB_INT4 2   // 16-row weight tiles per workgroup, INT4 experts
+#define MOE_STREAM_NB_INT4 4   // 16-row weight tiles per workgroup, INT4 experts
 #endif
 #ifndef MOE_STREAM_STAGE_BF16
 #define MOE_STREAM_STAGE_BF16 256  // bytes of each weight row per pipeline stage, bf16 experts
 #endif
 #ifndef MOE_STREAM_STAGE_INT4
-#define MOE_STREAM_STAGE_INT4 512  // bytes of each weight row per pipeline stage, INT4 experts
+#define MOE_STREAM_STAGE_INT4 256  // bytes of each weight row per pipeline stage, INT4 experts
 #endif
 #ifndef MOE_STREAM_NT
 #define MOE_STREAM_NT 1        // 1: non-temporal hint on weight loads
@@ -105,11 +105,14 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
     constexpr int SEGS = kStageBytes / 16;     // 16-byte segments per row per stage
     constexpr int LROW = kStageBytes + 16;     // padded LDS row (conflict-free 16-row column reads)
     constexpr int LOADS = ROWS * SEGS / 64;    // 16-byte loads per lane per stage
-    // per-wavefront stage buffers; after the K loop the same LDS holds the partial tiles
-    constexpr int kStageLds = 4 * ROWS * LROW;
+    constexpr int GPS = kStageBytes / 64;      // INT4: 128-column scale groups per stage
+    // per-wavefront stage buffers (INT4: followed by the stage's scales, ROWS x GPS bf16);
+    // after the K loop the same LDS holds the partial tiles
+    constexpr int kWaveLds = ROWS * LROW + (WQ == kINT4 ? ROWS * GPS * 2 : 0);
+    constexpr int kStageLds = 4 * kWaveLds;
     constexpr int kRedBytes = 3 * NB * MT * 64 * 16;
     __shared__ __attribute__((aligned(16))) uint8_t smem[kStageLds > kRedBytes ? kStageLds : kRedBytes];
-    uint8_t (*stage_lds)[ROWS * LROW] = reinterpret_cast<uint8_t (*)[ROWS * LROW]>(smem);
+    uint8_t (*stage_lds)[kWaveLds] = reinterpret_cast<uint8_t (*)[kWaveLds]>(smem);
     f32x4 (*red)[NB * MT][64] = reinterpret_cast<f32x4 (*)[NB * MT][64]>(smem);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -167,16 +170,41 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
 #pragma unroll
         for (int c = 0; c < MT; ++c) acc[b][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    // INT4 scales: this lane's output rows n0 + 16b + 4g + i
+    // INT4 scales: each stage's GPS scales of row `srow` of the block are
+    // loaded by lane srow (one vector load when aligned) with the stage's
+    // codes, parked next to them in LDS, and read back per output row.
     const int groups = K / 128;
-    const uint16_t* sc = (WQ == kINT4) ? Wsc + (int64_t)e * N * groups + (int64_t)(n0 + 4 * g) * groups : nullptr;
+    const int srow = lane % ROWS;
+    const uint16_t* sc_row = (WQ == kINT4) ? Wsc + (int64_t)e * N * groups + (int64_t)(n0 + srow) * groups : nullptr;
+    const bool sc_vec = (WQ == kINT4) && groups % GPS == 0 && ((uintptr_t)Wsc % 16) == 0;
+    uint16_t* sc_lds = reinterpret_cast<uint16_t*>(lds + ROWS * LROW);  // [ROWS][GPS]
+    typedef uint16_t scales_t __attribute__((ext_vector_type(GPS)));
+    auto sload = [&](int st, scales_t& v) {
+        const int gb = st * GPS;
+        if (sc_vec) {
+            v = *reinterpret_cast<const scales_t*>(sc_row + gb);
+        } else {
+#pragma unroll
+            for (int j = 0; j < GPS; ++j) v[j] = gb + j < groups ? sc_row[gb + j] : (uint16_t)0;
+        }
+    };
     const uint4 ones = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
 
     uint4 cur[LOADS], nxt[LOADS];
-    if (st0 < st1) gload(st0, cur);
+    scales_t scur = {}, snxt = {};
+    if (st0 < st1) {
+        gload(st0, cur);
+        if constexpr (WQ == kINT4) sload(st0, scur);
+    }
     for (int st = st0; st < st1; ++st) {
-        if (st + 1 < st1) gload(st + 1, nxt);
+        if (st + 1 < st1) {
+            gload(st + 1, nxt);
+            if constexpr (WQ == kINT4) sload(st + 1, snxt);
+        }
         lstore(cur);
+        if constexpr (WQ == kINT4) {
+            if (lane < ROWS) *reinterpret_cast<scales_t*>(sc_lds + srow * GPS) = scur;
+        }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         const int64_t s0 = (int64_t)st * kStageBytes;
         const int valid = (int)min((int64_t)kStageBytes, row_bytes - s0);
@@ -202,7 +230,15 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
         } else {
             // one 128-column scale group per 64 bytes of each row; lane group g takes columns [32g, 32g+32)
             const int gbase = (int)(s0 / 64);
-            for (int cc = 0; cc < valid / 64; ++cc) {
+            scales_t sv[NB][4];  // this lane's output rows 16 b + 4 g + i
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sv[b][i] = *reinterpret_cast<const scales_t*>(sc_lds + (16 * b + 4 * g + i) * GPS);
+            const int nch = valid / 64;
+#pragma unroll
+            for (int cc = 0; cc < GPS; ++cc) {
+                if (cc >= nch) break;
                 const int grp = gbase + cc;
                 uint4 xv[MT][4];
 #pragma unroll
@@ -235,16 +271,17 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
                 for (int b = 0; b < NB; ++b)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float sv = bf16_bits_to_float(sc[(int64_t)(16 * b + i) * groups + grp]);
+                        const float scale = bf16_bits_to_float(sv[b][i][cc]);
 #pragma unroll
                         for (int c = 0; c < MT; ++c)
-                            acc[b][c][i] = fmaf(sv, fmaf(-136.0f, sx[c][i], t[b][c][i]), acc[b][c][i]);
+                            acc[b][c][i] = fmaf(scale, fmaf(-136.0f, sx[c][i], t[b][c][i]), acc[b][c][i]);
                     }
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) cur[i] = nxt[i];
+        scur = snxt;
     }
 
     // fixed-order reduction of the four K-slices (in the stage buffers, once every wavefront is done with them)
@@ -293,7 +330,7 @@ hipError_t launch_stream_nb(const GemmArgs& a, hipStream_t stream) {
 // bf16 weights: 16 MT weight rows per workgroup for 16 MT dispatch rows, so
 // the activation rows (re-read by every workgroup from L2) never outweigh the
 // weights streamed from HBM; the wider tiles stage 128 bytes of each row (the
-// register double buffer stays at 8 loads per lane).  INT4: 32 weight rows.
+// register double buffer stays at 8 loads per lane).  INT4: 64 weight rows.
 hipError_t launch_stream_bf16(const GemmArgs& a, hipStream_t stream) {
     if (a.stream_mt == 1) return launch_stream_nb<kBF16, MOE_STREAM_NB_BF16, 1, MOE_STREAM_STAGE_BF16>(a, stream);
     if (a.stream_mt == 2) return launch_stream_nb<kBF16, 2, 2, 128>(a, stream);
