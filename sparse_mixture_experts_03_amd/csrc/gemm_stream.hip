@@ -64,17 +64,22 @@ __device__ __forceinline__ uint4 ldw16(const void* p) {
 }
 
 // Eight signed INT4 codes (one 32-bit word, code i in bits 4i..4i+3) to eight
-// bf16 values 136 + q_i, as one MFMA operand.
+// bf16 values 136 + q_i, as one MFMA operand.  bf16(128 + c) = 0x4300 | c for
+// c < 16, and c = q + 8 is the code with bit 3 flipped.  Output dword p holds
+// codes 2p (low nibble of byte p of w) and 2p + 1 (low nibble of byte p of
+// w >> 4): one byte permute places them in the two halves with zero bytes
+// above them, and one three-input bit operation keeps bits 0-2, flips bit 3
+// (a zero becomes one in the 0x43 byte as well) and clears the rest.
+__device__ __forceinline__ uint32_t nibble_pair_to_bf16(uint32_t x) {
+    return (x & 0x00070007u) | (~x & 0x43084308u);
+}
 __device__ __forceinline__ bf16x8 int4x8_to_bf16_offset136(uint32_t w) {
-    const uint32_t v = w ^ 0x88888888u;          // q + 8, offset binary
-    const uint32_t lo = v & 0x0f0f0f0fu;         // codes 0,2,4,6 in bytes 0..3
-    const uint32_t hi = (v >> 4) & 0x0f0f0f0fu;  // codes 1,3,5,7
+    const uint32_t w4 = w >> 4;
     uint4 r;
-    // dword p = bf16(128 + c[2p]) | bf16(128 + c[2p+1]) << 16 ; bf16(128 + c) = 0x4300 | c
-    r.x = __builtin_amdgcn_perm(hi, lo, 0x0c040c00u) | 0x43004300u;
-    r.y = __builtin_amdgcn_perm(hi, lo, 0x0c050c01u) | 0x43004300u;
-    r.z = __builtin_amdgcn_perm(hi, lo, 0x0c060c02u) | 0x43004300u;
-    r.w = __builtin_amdgcn_perm(hi, lo, 0x0c070c03u) | 0x43004300u;
+    r.x = nibble_pair_to_bf16(__builtin_amdgcn_perm(w4, w, 0x0c040c00u));
+    r.y = nibble_pair_to_bf16(__builtin_amdgcn_perm(w4, w, 0x0c050c01u));
+    r.z = nibble_pair_to_bf16(__builtin_amdgcn_perm(w4, w, 0x0c060c02u));
+    r.w = nibble_pair_to_bf16(__builtin_amdgcn_perm(w4, w, 0x0c070c03u));
     return as_bf16x8(r);
 }
 
@@ -124,7 +129,8 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
     const int r = lane & 15;
     const int g = lane >> 4;
     const int n0 = nt * ROWS;
-    // dispatch row 16 c + r of the tile feeds MFMA column tile c
+    // dispatch row 16 c + r of the tile feeds MFMA column tile c; lanes past
+    // the tile's rows load nothing (at decode sizes most of them)
     bool mvalid[MT];
     const uint16_t* xrow[MT];
 #pragma unroll
@@ -190,20 +196,12 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
     };
     const uint4 ones = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
 
-    uint4 cur[LOADS], nxt[LOADS];
-    scales_t scur = {}, snxt = {};
-    if (st0 < st1) {
-        gload(st0, cur);
-        if constexpr (WQ == kINT4) sload(st0, scur);
-    }
-    for (int st = st0; st < st1; ++st) {
-        if (st + 1 < st1) {
-            gload(st + 1, nxt);
-            if constexpr (WQ == kINT4) sload(st + 1, snxt);
-        }
-        lstore(cur);
+    // Two register buffers: stage st + 1 is in flight while stage st is parked
+    // in LDS and multiplied.
+    auto process = [&](int st, const uint4 (&buf)[LOADS], const scales_t& sbuf) {
+        lstore(buf);
         if constexpr (WQ == kINT4) {
-            if (lane < ROWS) *reinterpret_cast<scales_t*>(sc_lds + srow * GPS) = scur;
+            if (lane < ROWS) *reinterpret_cast<scales_t*>(sc_lds + srow * GPS) = sbuf;
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         const int64_t s0 = (int64_t)st * kStageBytes;
@@ -279,9 +277,22 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    };
+    uint4 bufa[LOADS], bufb[LOADS];
+    scales_t sa = {}, sb = {};
+    auto fetch = [&](int st, uint4 (&buf)[LOADS], scales_t& sbuf) {
+        gload(st, buf);
+        if constexpr (WQ == kINT4) sload(st, sbuf);
+    };
+    if (st0 < st1) fetch(st0, bufa, sa);
+    // (using the two buffers in turn instead of copying needs two copies of the
+    // stage code and more registers; measured slower at decode sizes)
+    for (int st = st0; st < st1; ++st) {
+        if (st + 1 < st1) fetch(st + 1, bufb, sb);
+        process(st, bufa, sa);
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) cur[i] = nxt[i];
-        scur = snxt;
+        for (int i = 0; i < LOADS; ++i) bufa[i] = bufb[i];
+        sa = sb;
     }
 
     // fixed-order reduction of the four K-slices (in the stage buffers, once every wavefront is done with them)
