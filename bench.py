@@ -22,6 +22,7 @@ sys.path.insert(0, ROOT)
 DEFAULT_WORKLOAD = "decode-bf16-T8-d8192-E128"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector
 
 
 def parse():
@@ -138,15 +139,19 @@ def main():
     gemm_bytes = active * w_bytes + Tk * d * abytes + Tk * d_ff * hbytes
     gemm_flops = 2.0 * Tk * d * d_ff
     kernel_name = f"moe_grouped_gemm_w1_{path}"
-    decode_like = path == "streaming"
-    if decode_like:
+    # the binding roof: arithmetic intensity against the ridge point of the compute unit the path uses
+    # (bf16 MFMA for bf16/INT4 experts, the fp32 vector ALUs for fp32 experts)
+    compute_peak = FP32_PEAK_TFLOPS if cfg["w"] == moe.F32 else BF16_PEAK_TFLOPS
+    ridge = compute_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if gemm_flops / gemm_bytes < ridge:
         achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=load_traffic(args.workload, kernel_name))
     else:
         achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=load_traffic(args.workload, kernel_name))
+        roof = dict(bound="alu" if cfg["w"] == moe.F32 else "mfma", achieved=round(achieved, 1), peak=compute_peak,
+                    unit="TFLOP/s", frac=round(achieved / compute_peak, 4),
+                    traffic=load_traffic(args.workload, kernel_name))
     roof.update(kernel=kernel_name, avg_launch_ms=round(gemm_ms, 4),
                 algorithmic_bytes=gemm_bytes, algorithmic_flops=gemm_flops)
 
