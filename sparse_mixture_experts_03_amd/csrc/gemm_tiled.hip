@@ -429,15 +429,12 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
 }
 
 // bf16 weights, K-stages of 64: each stage holds 128 bytes (one whole
-// 128-byte line) of every tile row, 32 KB per operand, double-buffered in
-// the same 128 KB of LDS.  Copying whole lines runs the direct-to-LDS loads
+// 128-byte line) of every tile row, 32 KB per operand.  Copying whole lines runs the direct-to-LDS loads
 // about 1.5x faster than half lines (measured on L2-resident data: 16 rows x
 // 64 B per instruction reach 21-24 TB/s, 8 rows x 128 B 33 TB/s).  The
 // eight 16-byte segments of a row sit in slots permuted by (row >> 1) & 7,
 // so 16 consecutive rows read at one logical segment hit 16 distinct bank
-// groups.  Step k waits for its own loads, one barrier publishes stage k and
-// frees the other buffer, stage k+1 is issued into it and stage k is
-// multiplied (four k-substeps of 16).  Logical segment seg of tile row
+// groups.  Stage k is multiplied in four k-substeps of 16.  Logical segment seg of tile row
 // `row` sits at byte row * 128 + 16 * (seg ^ ((row >> 1) & 7)) of a stage.
 
 template <int WHICH, int TI, int TJ, int XROWS>
@@ -469,14 +466,17 @@ __device__ __forceinline__ void tile_gemm_bf16_bk64(uint8_t* Wl, uint8_t* Xl, co
         const uint32_t arow = (WHICH == 1) ? (uint32_t)a_rows[p0 + drow] : (uint32_t)(p0 + drow);
         xoff[i] = arow * rowbytes + 16 * seg;
     }
-    auto issue = [&](int kt, int buf) {
+    auto issue_w = [&](int kt, int slot) {
         const uint32_t kb = (uint32_t)kt * 128;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) copy_rows_to_lds(wbase, woff[i] + kb, Wl + buf * kStage + (64 * wave + 8 * i) * 128);
+        for (int i = 0; i < 8; ++i) copy_rows_to_lds(wbase, woff[i] + kb, Wl + slot * kStage + (64 * wave + 8 * i) * 128);
+    };
+    auto issue_x = [&](int kt, int slot) {
+        const uint32_t kb = (uint32_t)kt * 128;
         if (xload) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                copy_rows_to_lds(xbase, xoff[i] + kb, Xl + buf * kStage + (64 * wave + 8 * i) * 128);
+                copy_rows_to_lds(xbase, xoff[i] + kb, Xl + slot * kStage + (64 * wave + 8 * i) * 128);
         }
     };
 
@@ -538,13 +538,22 @@ __device__ __forceinline__ void tile_gemm_bf16_bk64(uint8_t* Wl, uint8_t* Xl, co
             for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32x32x16(wf[1][i], xf[1][j], acc[i][j]);
     };
 
+    // Weight stages (three slots) are copied two stages ahead, dispatch-row
+    // stages (two slots; shared by the workgroups of one m-tile, mostly L2
+    // hits) one stage ahead, in the order W(0) X(0) W(1) | X(1) W(2) | X(2)
+    // W(3) | ...: at step k everything up to X(k) must have landed and only
+    // W(k+1) (8 loads) may still be in flight.  The barrier publishes stage k
+    // and frees the slots of stage k-1, which the step's copies then reuse.
     const int nk = K / 64;
-    issue(0, 0);
+    issue_w(0, 0);
+    issue_x(0, 0);
+    if (nk > 1) issue_w(1, 1);
     for (int kt = 0; kt < nk; ++kt) {
-        wait_vmcnt<0>();  // stage kt is the only one in flight
+        if (kt + 1 < nk) wait_vmcnt<8>(); else wait_vmcnt<0>();
         barrier();
-        if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
-        const uint32_t wb = lds_addr(Wl + (kt & 1) * kStage), xb = lds_addr(Xl + (kt & 1) * kStage);
+        if (kt + 1 < nk) issue_x(kt + 1, (kt + 1) & 1);
+        if (kt + 2 < nk) issue_w(kt + 2, (kt + 2) % 3);
+        const uint32_t wb = lds_addr(Wl + (kt % 3) * kStage), xb = lds_addr(Xl + (kt & 1) * kStage);
         compute_pair(wb, xb, 0);
         compute_pair(wb, xb, 1);
     }
@@ -559,10 +568,14 @@ __global__ void __launch_bounds__(256, 1)
 gemm_tiled_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
                   const int32_t* __restrict__ offsets, int E, const uint8_t* __restrict__ W, int64_t W_stride,
                   const uint16_t* __restrict__ Wsc, void* __restrict__ out, int N, int K, int ntiles_n, int rows_lo) {
-    __shared__ __attribute__((aligned(1024))) uint8_t Wt[kStages][kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t Xt[kStages][kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t Ct[WQ == kINT4 ? kStages : 1][4096];  // INT4 code ring
-    __shared__ __attribute__((aligned(1024))) uint8_t St[WQ == kINT4 ? 2 : 1][4096];        // INT4 scale ring
+    // bf16: 3 weight + 2 dispatch-row stages of 32 KB (160 KB, all of a CU's LDS).
+    // INT4: 4 + 4 stages of 16 KB, the code ring (4 x 4 KB) and the scale ring (2 x 4 KB).
+    constexpr int kLdsBytes = WQ == kBF16 ? 5 * 32768 : 2 * kStages * kTileBytes + kStages * 4096 + 2 * 4096;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+    uint8_t (*Wt)[kTileBytes] = reinterpret_cast<uint8_t (*)[kTileBytes]>(smem);
+    uint8_t (*Xt)[kTileBytes] = reinterpret_cast<uint8_t (*)[kTileBytes]>(smem + kStages * kTileBytes);
+    uint8_t (*Ct)[4096] = reinterpret_cast<uint8_t (*)[4096]>(smem + 2 * kStages * kTileBytes);     // INT4 code ring
+    uint8_t (*St)[4096] = reinterpret_cast<uint8_t (*)[4096]>(smem + 2 * kStages * kTileBytes + kStages * 4096);  // scales
 
     // An (empty) statement that clobbers an AGPR tells the backend this kernel
     // uses AGPRs, so it gives the MFMAs their AGPR-accumulator form (the
@@ -586,11 +599,11 @@ gemm_tiled_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_
     const void* Wsc_e = (WQ == kINT4) ? (const void*)(Wsc + (int64_t)e * N * (K / 128)) : nullptr;
     if constexpr (WQ == kBF16) {
         if (rows > 128)
-            tile_gemm_bf16_bk64<WHICH, 4, 4, 256>(&Wt[0][0], &Xt[0][0], A, a_rows, Wexp, out, N, K, n0, p0, rows);
+            tile_gemm_bf16_bk64<WHICH, 4, 4, 256>(smem, smem + 3 * 32768, A, a_rows, Wexp, out, N, K, n0, p0, rows);
         else if (rows > 64)
-            tile_gemm_bf16_bk64<WHICH, 2, 4, 128>(&Wt[0][0], &Xt[0][0], A, a_rows, Wexp, out, N, K, n0, p0, rows);
+            tile_gemm_bf16_bk64<WHICH, 2, 4, 128>(smem, smem + 3 * 32768, A, a_rows, Wexp, out, N, K, n0, p0, rows);
         else
-            tile_gemm_bf16_bk64<WHICH, 2, 2, 64>(&Wt[0][0], &Xt[0][0], A, a_rows, Wexp, out, N, K, n0, p0, rows);
+            tile_gemm_bf16_bk64<WHICH, 2, 2, 64>(smem, smem + 3 * 32768, A, a_rows, Wexp, out, N, K, n0, p0, rows);
         return;
     }
     if (rows > 128)
