@@ -135,6 +135,27 @@ moe_status moe_router(const moe_config *cfg, const void *x, const void *Wg, cons
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Router statistics (P1 §3.2 router entropy; P3 §4.2 expert_load, the mean
+ * selection probability; P5 §3.2 balance loss over assignment fractions; P3
+ * §3.2 the same sum over probabilities; P5 §4 spread of expert utilisation).
+ * Routes exactly as moe_router (same expert_ids and gate_weights), then, in
+ * binary64 and in a fixed summation order:
+ *   expert_fraction[e] = #{(t, j): expert_ids[t][j] = e} / (T k)      [E]
+ *   mean_prob[e]       = (1/T) sum_t softmax(z_t)[e]                    [E]
+ *   scalars[0] = (1/T) sum_t -sum_e p ln p  (router entropy, nats; 0 ln 0 = 0)
+ *   scalars[1] = sum_e (expert_fraction[e] - 1/E)^2
+ *   scalars[2] = sum_e (mean_prob[e] - 1/E)^2
+ *   scalars[3] = sqrt(scalars[1] / E)   (standard deviation of expert_fraction)
+ * All outputs are device pointers (double arrays 8-byte aligned).  T == 0
+ * writes zeros.  workspace >= moe_router_stats_workspace_size() bytes,
+ * 256-byte aligned (it holds the T x E softmax rows).
+ */
+moe_status moe_router_stats_workspace_size(const moe_config *cfg, size_t *bytes);
+moe_status moe_router_stats(const moe_config *cfg, const void *x, const void *Wg, const float *router_bias,
+                            int32_t *expert_ids, float *gate_weights, double *expert_fraction, double *mean_prob,
+                            double *scalars, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Dispatch stage (P3 §4.2: per-expert load vector; tokens scattered to
  * experts): counts[e], exclusive offsets[E+1] (offsets[E] = T*k), and the
  * stable expert-major order of the T*k assignments taken in row-major

@@ -108,6 +108,16 @@ def quantize_int4_g128(w):
     return packed.contiguous(), s.contiguous()
 
 
+def generate_router(cfg, device="cpu", seed=0):
+    """The router's inputs alone (the same tensors `generate` returns):
+    dict(x [T, d], Wg [d, E], bias [E] or None)."""
+    T, d, E, act = cfg["T"], cfg["d"], cfg["E"], cfg["act"]
+    x = _store(_normal((T, d), 1.0, device, stream_seed(seed, TAGS["x"])), act)
+    Wg = _store(_normal((d, E), 1.0 / math.sqrt(d), device, stream_seed(seed, TAGS["Wg"])), act)
+    bias = router_bias(E).to(device) if cfg.get("bias") else None
+    return dict(x=x, Wg=Wg, bias=bias)
+
+
 def generate(cfg, device="cpu", seed=0):
     """All inputs of a workload as torch tensors on `device`.
 
@@ -115,11 +125,9 @@ def generate(cfg, device="cpu", seed=0):
     W1 is [E, d_ff, d] (INT4: uint8 [E, d_ff, d/2]); W2 is [E, d, d_ff].
     """
     T, d, d_ff, E = cfg["T"], cfg["d"], cfg["d_ff"], cfg["E"]
-    act, wdt = cfg["act"], cfg["w"]
-    x = _store(_normal((T, d), 1.0, device, stream_seed(seed, TAGS["x"])), act)
-    Wg = _store(_normal((d, E), 1.0 / math.sqrt(d), device, stream_seed(seed, TAGS["Wg"])), act)
-    bias = router_bias(E).to(device) if cfg.get("bias") else None
-    out = dict(x=x, Wg=Wg, bias=bias, S1=None, S2=None)
+    wdt = cfg["w"]
+    out = generate_router(cfg, device, seed)
+    out.update(S1=None, S2=None)
     for name, N, K in (("W1", d_ff, d), ("W2", d, d_ff)):
         std = 1.0 / math.sqrt(K)
         if wdt == INT4_G128:

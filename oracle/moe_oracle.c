@@ -264,6 +264,61 @@ int oracle_permute(int64_t T, int32_t E, int32_t k, const int32_t *ids,
     return 0;
 }
 
+/* ------------------------------------------------------- router statistics */
+
+/*
+ * Batch statistics of the routing (ids [T][k], full softmax rows p [T][E]):
+ *   fraction[e]  = #{(t, j): ids[t][j] = e} / (T k)       share of the assignments,
+ *                  whose target is 1/E                     P5 §3.2 balance loss
+ *   mean_prob[e] = (1/T) sum_t p[t][e]                     P3 §4.2 expert_load buffer
+ *   scalars[0]   = (1/T) sum_t ( -sum_e p[t][e] ln p[t][e] ), with 0 ln 0 = 0
+ *                                                          P1 §3.2 router entropy
+ *   scalars[1]   = sum_e (fraction[e] - 1/E)^2             P5 §3.2 (without lambda)
+ *   scalars[2]   = sum_e (mean_prob[e] - 1/E)^2            P3 §3.2 (without lambda)
+ *   scalars[3]   = sqrt( (1/E) sum_e (fraction[e] - 1/E)^2 ) spread of expert
+ *                  utilisation (population standard deviation) P5 §4 monitoring
+ * Sums run in ascending index order.  Returns 0, or -1 if T < 1 or an id is
+ * out of range.
+ */
+int oracle_router_stats(int64_t T, int32_t E, int32_t k, const int32_t *ids, const double *p,
+                        double *fraction, double *mean_prob, double *scalars)
+{
+    if (T < 1)
+        return -1;
+    for (int32_t e = 0; e < E; ++e) {
+        fraction[e] = 0.0;
+        mean_prob[e] = 0.0;
+    }
+    for (int64_t a = 0; a < T * k; ++a) {
+        if (ids[a] < 0 || ids[a] >= E)
+            return -1;
+        fraction[ids[a]] += 1.0;
+    }
+    double entropy = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+        double h = 0.0;
+        for (int32_t e = 0; e < E; ++e) {
+            const double q = p[t * E + e];
+            mean_prob[e] += q;
+            if (q != 0.0)
+                h -= q * log(q);
+        }
+        entropy += h;
+    }
+    double sf = 0.0, sp = 0.0;
+    for (int32_t e = 0; e < E; ++e) {
+        fraction[e] /= (double)T * (double)k;
+        mean_prob[e] /= (double)T;
+        sf += (fraction[e] - 1.0 / E) * (fraction[e] - 1.0 / E);
+        sp += (mean_prob[e] - 1.0 / E) * (mean_prob[e] - 1.0 / E);
+    }
+    scalars[0] = entropy / (double)T;
+    scalars[1] = sf;
+    scalars[2] = sp;
+    scalars[3] = sqrt(sf / E);
+    return 0;
+}
+
 /* --------------------------------------------------------------- expert FFN */
 
 /*

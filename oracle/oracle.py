@@ -56,6 +56,8 @@ class Oracle:
         lib.oracle_route.restype = ctypes.c_int
         lib.oracle_permute.argtypes = [_I64, _I32, _I32, _P, _P, _P, _P, _P]
         lib.oracle_permute.restype = ctypes.c_int
+        lib.oracle_router_stats.argtypes = [_I64, _I32, _I32, _P, _P, _P, _P, _P]
+        lib.oracle_router_stats.restype = ctypes.c_int
         lib.oracle_expert_ffn.argtypes = [_I64, _I64, _I32, _P, _P, _P, _P, _P, _P]
         lib.oracle_expert_ffn.restype = ctypes.c_int
         lib.oracle_forward_tokens.argtypes = [_I64, _I64, _I64, _I32, _I32, _I32, _I32, _P,
@@ -120,6 +122,23 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_permute: expert id out of range")
         return dict(counts=counts, offsets=offsets, sorted_token=sorted_token, pos=pos)
+
+    def router_stats(self, ids, p):
+        """Routing statistics from ids [T,k] and full softmax rows p [T,E] (binary64):
+        dict(fraction[E], mean_prob[E], entropy, lb_fraction, lb_prob, fraction_std)."""
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        p = np.ascontiguousarray(p, dtype=np.float64)
+        T, k = ids.shape
+        E = p.shape[1]
+        fraction = np.zeros(E, dtype=np.float64)
+        mean_prob = np.zeros(E, dtype=np.float64)
+        scalars = np.zeros(4, dtype=np.float64)
+        rc = self.lib.oracle_router_stats(T, E, k, ids.ctypes.data, p.ctypes.data, fraction.ctypes.data,
+                                          mean_prob.ctypes.data, scalars.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle_router_stats rejected its arguments")
+        return dict(fraction=fraction, mean_prob=mean_prob, entropy=scalars[0], lb_fraction=scalars[1],
+                    lb_prob=scalars[2], fraction_std=scalars[3], scalars=scalars)
 
     # -- experts ------------------------------------------------------------------
     def expert_ffn(self, xr, W1e, W2e, w_dtype, S1e=None, S2e=None):

@@ -6,12 +6,13 @@ allocates outputs and workspace with torch and calls `moe_forward`.
 """
 from . import binding
 from .binding import (BF16, F32, GEMM_AUTO, GEMM_STREAMING, GEMM_TILED, INT4_G128, MoeConfig, MoeError, config,
-                      moe_combine, moe_forward, moe_grouped_gemm, moe_permute, moe_router, moe_router_workspace_size,
-                      moe_workspace_size)
+                      moe_combine, moe_forward, moe_grouped_gemm, moe_permute, moe_router, moe_router_stats,
+                      moe_router_stats_workspace_size, moe_router_workspace_size, moe_workspace_size)
 
 __all__ = ["binding", "BF16", "F32", "INT4_G128", "GEMM_AUTO", "GEMM_STREAMING", "GEMM_TILED", "MoeConfig",
            "MoeError", "config", "moe_forward", "moe_router", "moe_permute", "moe_grouped_gemm", "moe_combine",
-           "moe_workspace_size", "moe_router_workspace_size", "MoELayerForward"]
+           "moe_workspace_size", "moe_router_workspace_size", "moe_router_stats", "moe_router_stats_workspace_size",
+           "MoELayerForward"]
 
 
 class MoELayerForward:

@@ -16,7 +16,8 @@ F32, BF16, INT4_G128 = 0, 1, 2
 GEMM_AUTO, GEMM_STREAMING, GEMM_TILED = 0, 1, 2
 
 EXPORTS = ("moe_workspace_size", "moe_router_workspace_size", "moe_forward", "moe_router", "moe_permute",
-           "moe_grouped_gemm", "moe_combine", "moe_status_string", "moe_last_hip_error")
+           "moe_grouped_gemm", "moe_combine", "moe_router_stats_workspace_size", "moe_router_stats",
+           "moe_status_string", "moe_last_hip_error")
 
 
 class MoeConfig(ctypes.Structure):
@@ -65,8 +66,10 @@ def load(path=LIB_PATH):
     lib.moe_permute.argtypes = [CFG, P, P, P, P, P, P]
     lib.moe_grouped_gemm.argtypes = [CFG, I32, P, P, P, P, P, I64, P, P]
     lib.moe_combine.argtypes = [CFG, P, P, P, P, P]
+    lib.moe_router_stats_workspace_size.argtypes = [CFG, ctypes.POINTER(SZ)]
+    lib.moe_router_stats.argtypes = [CFG, P, P, P, P, P, P, P, P, P, SZ, P]
     for name in ("moe_workspace_size", "moe_router_workspace_size", "moe_forward", "moe_router", "moe_permute",
-                 "moe_grouped_gemm", "moe_combine"):
+                 "moe_grouped_gemm", "moe_combine", "moe_router_stats_workspace_size", "moe_router_stats"):
         getattr(lib, name).restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -136,6 +139,21 @@ def moe_router(cfg, x, Wg, bias, expert_ids, gate_weights, workspace, stream=Non
     st = load().moe_router(ctypes.byref(cfg), _ptr(x), _ptr(Wg), _ptr(bias), _ptr(expert_ids), _ptr(gate_weights),
                            _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "moe_router")
+
+
+def moe_router_stats_workspace_size(cfg):
+    n = ctypes.c_size_t()
+    _check(load().moe_router_stats_workspace_size(ctypes.byref(cfg), ctypes.byref(n)), "moe_router_stats_workspace_size")
+    return n.value
+
+
+def moe_router_stats(cfg, x, Wg, bias, expert_ids, gate_weights, expert_fraction, mean_prob, scalars, workspace,
+                     stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().moe_router_stats(ctypes.byref(cfg), _ptr(x), _ptr(Wg), _ptr(bias), _ptr(expert_ids),
+                                 _ptr(gate_weights), _ptr(expert_fraction), _ptr(mean_prob), _ptr(scalars),
+                                 _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "moe_router_stats")
 
 
 def moe_permute(cfg, expert_ids, counts, offsets, sorted_token, pos, stream=None):

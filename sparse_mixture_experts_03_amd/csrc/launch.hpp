@@ -30,8 +30,22 @@ struct RouterArgs {
     double* partial;  // workspace, >= router_plan().partial_bytes
     int32_t* ids;
     float* gates;
+    double* prob_rows = nullptr;     // optional [T][E]: every token's softmax row (router statistics)
+    double* entropy_rows = nullptr;  // optional [T]: every token's -sum p ln p
 };
 hipError_t launch_router(const RouterArgs& a, hipStream_t stream);
+
+// ------------------------------------------------------ router statistics
+// From prob_rows [T][E], entropy_rows [T] and ids [T][k]: fraction[E] =
+// count_e / (T k), mean_prob[E] = sum_t p[t][e] / T and scalars[4] = { mean
+// entropy, sum_e (fraction_e - 1/E)^2, sum_e (mean_prob_e - 1/E)^2, std of
+// fraction }.  scratch: >= stats_scratch_bytes(E).  T >= 1.
+size_t stats_scratch_bytes(int E);
+hipError_t launch_router_stats(const double* prob_rows, const double* entropy_rows, const int32_t* ids, int64_t T,
+                               int E, int k, void* scratch, double* fraction, double* mean_prob, double* scalars,
+                               hipStream_t stream);
+// fraction[E] = mean_prob[E] = scalars[4] = 0 (empty batch)
+hipError_t launch_zero_stats(int E, double* fraction, double* mean_prob, double* scalars, hipStream_t stream);
 
 // --------------------------------------------------------------- permute
 hipError_t launch_permute(const int32_t* ids, int64_t T, int E, int k, int32_t* counts, int32_t* offsets,

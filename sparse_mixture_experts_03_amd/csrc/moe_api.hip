@@ -244,6 +244,65 @@ moe_status moe_router(const moe_config* cfg, const void* x, const void* Wg, cons
     return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
+// Router-statistics workspace: router partials, then [T][E] softmax rows,
+// [T] entropies and the reduction scratch.
+struct StatsLayout {
+    size_t partial, prob_rows, entropy_rows, scratch, total;
+};
+StatsLayout stats_layout_of(const moe_config& c) {
+    StatsLayout L;
+    size_t off = 0;
+    L.partial = off;
+    off = round_up(off + moe::router_plan(c.T, c.d, c.E).partial_bytes, 256);
+    L.prob_rows = off;
+    off = round_up(off + sizeof(double) * (size_t)c.T * (size_t)c.E, 256);
+    L.entropy_rows = off;
+    off = round_up(off + sizeof(double) * (size_t)c.T, 256);
+    L.scratch = off;
+    off = round_up(off + moe::stats_scratch_bytes(c.E), 256);
+    L.total = c.T == 0 ? 0 : off;
+    return L;
+}
+
+moe_status moe_router_stats_workspace_size(const moe_config* cfg, size_t* bytes) {
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+    *bytes = stats_layout_of(*cfg).total;
+    return MOE_OK;
+}
+
+moe_status moe_router_stats(const moe_config* cfg, const void* x, const void* Wg, const float* router_bias,
+                            int32_t* expert_ids, float* gate_weights, double* expert_fraction, double* mean_prob,
+                            double* scalars, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    const moe_config& c = *cfg;
+    if (!expert_fraction || !aligned(expert_fraction, 8) || !mean_prob || !aligned(mean_prob, 8) || !scalars ||
+        !aligned(scalars, 8))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (c.T == 0) {
+        hipError_t e = moe::launch_zero_stats(c.E, expert_fraction, mean_prob, scalars, stream);
+        return e == hipSuccess ? MOE_OK : hip_fail(e);
+    }
+    if (!x || !aligned(x, 16) || !Wg || !aligned(Wg, 16)) return MOE_ERR_INVALID_ARGUMENT;
+    if (!expert_ids || !aligned(expert_ids, 4) || !gate_weights || !aligned(gate_weights, 4))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (router_bias && !aligned(router_bias, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    const StatsLayout L = stats_layout_of(c);
+    if (!workspace || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    char* ws = static_cast<char*>(workspace);
+    moe::RouterArgs r = router_args(c, x, Wg, router_bias, expert_ids, gate_weights, ws + L.partial);
+    r.prob_rows = reinterpret_cast<double*>(ws + L.prob_rows);
+    r.entropy_rows = reinterpret_cast<double*>(ws + L.entropy_rows);
+    hipError_t e = moe::launch_router(r, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    e = moe::launch_router_stats(r.prob_rows, r.entropy_rows, expert_ids, c.T, c.E, c.k, ws + L.scratch,
+                                 expert_fraction, mean_prob, scalars, stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
 moe_status moe_permute(const moe_config* cfg, const int32_t* expert_ids, int32_t* counts, int32_t* offsets,
                        int32_t* sorted_token, int32_t* pos, hipStream_t stream) {
     moe_status s = check_config(cfg);

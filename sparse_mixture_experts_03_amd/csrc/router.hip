@@ -185,7 +185,8 @@ constexpr int kNoExpert = 0x7fffffff;
 __global__ void __launch_bounds__(256)
 router_finalize_kernel(const double* __restrict__ partial, int nsplit, int T, int E, int k,
                        const float* __restrict__ bias, double tau, int use_gumbel, uint64_t seed,
-                       uint64_t token_offset, int32_t* __restrict__ ids, float* __restrict__ gates) {
+                       uint64_t token_offset, int32_t* __restrict__ ids, float* __restrict__ gates,
+                       double* __restrict__ prob_rows, double* __restrict__ entropy_rows) {
     __shared__ double zs[256];
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
@@ -231,6 +232,19 @@ router_finalize_kernel(const double* __restrict__ partial, int nsplit, int T, in
     for (int j = 0; j < 4; ++j)
         if (live[j]) s += exp(z[j] - m);
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (prob_rows) {
+        // router statistics: this token's full softmax row and its entropy -sum p ln p (0 ln 0 = 0)
+        double h = 0.0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (live[j]) {
+                const double p = any_nan ? (double)NAN : exp(z[j] - m) / s;
+                prob_rows[(int64_t)t * E + lane + 64 * j] = p;
+                if (!(p == 0.0)) h -= p * log(p);
+            }
+        for (int off = 32; off >= 1; off >>= 1) h += __shfl_xor(h, off, 64);
+        if (lane == 0) entropy_rows[t] = h;
+    }
     // top-k by repeated wavefront argmax
     bool taken[4] = {false, false, false, false};
     for (int r = 0; r < k; ++r) {
@@ -301,7 +315,7 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t stream) {
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(router_finalize_kernel, dim3((unsigned)a.T), dim3(256), 0, stream, a.partial, p.splits,
                        (int)a.T, a.E, a.k, a.bias, (double)a.tau, a.use_gumbel, a.seed, a.token_offset, a.ids,
-                       a.gates);
+                       a.gates, a.prob_rows, a.entropy_rows);
     return hipGetLastError();
 }
 

@@ -448,4 +448,70 @@ def pin_invariants_at_tiny_workload(orc):
     assert np.all(np.isfinite(out["y"]))
 
 
+# ---------------------------------------------------------- router statistics
+
+def pin_router_stats_closed_forms(orc):
+    """Uniform logits: every p is 1/E (mean-probability balance term 0,
+    entropy ln E) and ties send every token to experts 0..k-1, so the
+    assignment fractions are 1/k there and 0 elsewhere.  A dominating bias
+    makes p one-hot: entropy exactly 0 and that expert's mean probability 1.
+    Two experts, two tokens with logit gaps +ln 3 and -ln 3: p = (3/4, 1/4)
+    and (1/4, 3/4), mean probabilities 1/2, entropy = the binary entropy of
+    1/4 (scipy), and top-1 fractions 1/2 each."""
+    T, d, E, k = 10, 8, 6, 2
+    uni = orc.route(np.zeros((T, d), np.float32), np.zeros((d, E), np.float32), k, F32, want_zp=True)
+    st = orc.router_stats(uni["ids"], uni["p"])
+    want_f = np.array([1.0 / k] * k + [0.0] * (E - k))
+    assert np.array_equal(uni["ids"], np.tile(np.arange(k, dtype=np.int32), (T, 1)))
+    assert np.allclose(st["fraction"], want_f, rtol=0, atol=1e-15)
+    assert np.allclose(st["mean_prob"], 1.0 / E, rtol=0, atol=1e-15)
+    assert abs(st["lb_prob"]) <= 1e-30
+    assert abs(st["entropy"] - math.log(E)) <= 1e-14
+    lb_f = k * (1.0 / k - 1.0 / E) ** 2 + (E - k) * (1.0 / E) ** 2
+    assert abs(st["lb_fraction"] - lb_f) <= 1e-15
+    assert abs(st["fraction_std"] - math.sqrt(lb_f / E)) <= 1e-15
+
+    bias = np.zeros(E, np.float32)
+    bias[3] = 1000.0
+    hot = orc.route(np.zeros((T, d), np.float32), np.zeros((d, E), np.float32), k, F32, bias=bias, want_zp=True)
+    st = orc.router_stats(hot["ids"], hot["p"])
+    assert st["entropy"] == 0.0 and st["mean_prob"][3] == 1.0
+    assert np.all(hot["ids"][:, 0] == 3)
+
+    # two tokens x = +1 and -1 against Wg = (q, -q), q = fp32(ln 3 / 2): logit gaps +-2q
+    q = float(np.float32(math.log(3.0) / 2))
+    two = orc.route(np.array([[1.0], [-1.0]], np.float32), np.array([[q, -q]], np.float32), 1, F32, want_zp=True)
+    st = orc.router_stats(two["ids"], two["p"])
+    pa = math.exp(2 * q) / (math.exp(2 * q) + 1.0)  # ~3/4
+    assert abs(pa - 0.75) < 1e-7
+    assert np.array_equal(two["ids"].ravel(), [0, 1])
+    assert np.allclose(st["mean_prob"], [0.5, 0.5], rtol=0, atol=1e-15)
+    assert np.array_equal(st["fraction"], [0.5, 0.5])
+    assert abs(st["entropy"] - stats.entropy([pa, 1.0 - pa])) <= 1e-15
+    assert st["lb_fraction"] == 0.0 and st["fraction_std"] == 0.0
+
+
+def pin_router_stats_invariants(orc):
+    """On random routings: the fractions and mean probabilities each sum to
+    one, 0 <= entropy <= ln E, the balance terms are >= 0 with std^2 * E equal
+    to the fraction term; relabelling the experts (permuting Wg's columns)
+    permutes the per-expert results and leaves the scalars unchanged; the
+    fractions equal numpy's bincount of the ids over T k."""
+    (x, Wg, _, _), _ = _tiny(31, T=40, E=7, dtype=BF16)
+    out = orc.route(x, Wg, 2, BF16, want_zp=True)
+    st = orc.router_stats(out["ids"], out["p"])
+    assert abs(st["fraction"].sum() - 1.0) <= 1e-15 and abs(st["mean_prob"].sum() - 1.0) <= 1e-14
+    assert 0.0 <= st["entropy"] <= math.log(7) + 1e-15
+    assert st["lb_fraction"] >= 0 and st["lb_prob"] >= 0
+    assert abs(st["fraction_std"] ** 2 * 7 - st["lb_fraction"]) <= 1e-15
+    assert np.array_equal(st["fraction"], np.bincount(out["ids"].ravel(), minlength=7) / (40 * 2))
+    perm = np.array([3, 6, 0, 5, 1, 2, 4])
+    outp = orc.route(x, np.ascontiguousarray(Wg[:, perm]), 2, BF16, want_zp=True)
+    sp = orc.router_stats(outp["ids"], outp["p"])
+    assert np.allclose(sp["fraction"], st["fraction"][perm], rtol=0, atol=0)
+    assert np.allclose(sp["mean_prob"], st["mean_prob"][perm], rtol=0, atol=1e-15)
+    for key in ("entropy", "lb_fraction", "lb_prob", "fraction_std"):
+        assert abs(sp[key] - st[key]) <= 1e-14 * max(1.0, abs(st[key]))
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

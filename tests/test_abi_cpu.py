@@ -175,6 +175,23 @@ def test_stage_entry_points_check_arguments(lib):
                            P(0)) == binding.MOE_ERR_INVALID_ARGUMENT
 
 
+def test_router_stats_checks_arguments(lib):
+    P = ctypes.c_void_p
+    c = _cfg()
+    n = ctypes.c_size_t()
+    assert lib.moe_router_stats_workspace_size(ctypes.byref(c), ctypes.byref(n)) == 0
+    assert n.value >= 8 * 8 * 8 + 8 * 8  # softmax rows [T][E] and entropies [T] in binary64
+    good = dict(x=0x1000, Wg=0x2000, ids=0x3000, gates=0x4000, frac=0x5000, mp=0x6000, sc=0x7000, ws=0x10000)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return lib.moe_router_stats(ctypes.byref(c), P(a["x"]), P(a["Wg"]), None, P(a["ids"]), P(a["gates"]),
+                                    P(a["frac"]), P(a["mp"]), P(a["sc"]), P(a["ws"]), kw.get("wsb", 1 << 30), P(0))
+    for bad in (dict(frac=None), dict(mp=0x6004), dict(sc=None), dict(x=None), dict(ids=0x3002), dict(ws=0x10008)):
+        assert call(**bad) == binding.MOE_ERR_INVALID_ARGUMENT, bad
+    assert call(wsb=64) == binding.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_workloads_are_valid_configs(lib):
     n = ctypes.c_size_t()
     for name in moe_synth.WORKLOADS:

@@ -52,6 +52,13 @@ MUTANTS = [
     ("bf16 widened wrongly", "uint32_t w = (uint32_t)bits << 16;", "uint32_t w = ((uint32_t)bits << 16) | 0x8000u;"),
     ("logits skip last input", "for (int64_t i = 0; i < d; ++i) {\n            double xi",
      "for (int64_t i = 0; i + 1 < d; ++i) {\n            double xi"),
+    ("fraction over tokens only", "fraction[e] /= (double)T * (double)k;", "fraction[e] /= (double)T;"),
+    ("entropy in bits", "h -= q * log(q);", "h -= q * log2(q);"),
+    ("entropy sign", "h -= q * log(q);", "h += q * log(q);"),
+    ("balance term on fractions uses probs", "sf += (fraction[e] - 1.0 / E) * (fraction[e] - 1.0 / E);",
+     "sf += (mean_prob[e] - 1.0 / E) * (mean_prob[e] - 1.0 / E);"),
+    ("std without 1/E", "scalars[3] = sqrt(sf / E);", "scalars[3] = sqrt(sf);"),
+    ("mean prob not averaged", "mean_prob[e] /= (double)T;", "mean_prob[e] /= (double)E;"),
 ]
 
 
