@@ -234,7 +234,9 @@ int oracle_route(int64_t T, int64_t d, int32_t E, int32_t k, int32_t act_dtype,
  * the T*k assignments taken in row-major (token, slot) order:
  *   sorted_token[offsets[e] + r] = token of the r-th assignment to e,
  *   pos[t*k + j] = the position of assignment (t, j) in that order.
- * Returns 0, or -1 if an id is out of range.
+ * An id of -1 marks an assignment dropped by capacity-limited dispatch: it
+ * is not counted and gets pos = -1.  Returns 0, or -1 if an id is otherwise
+ * out of range.
  */
 int oracle_permute(int64_t T, int32_t E, int32_t k, const int32_t *ids,
                    int32_t *counts, int32_t *offsets, int32_t *sorted_token, int32_t *pos)
@@ -242,6 +244,8 @@ int oracle_permute(int64_t T, int32_t E, int32_t k, const int32_t *ids,
     for (int32_t e = 0; e < E; ++e)
         counts[e] = 0;
     for (int64_t a = 0; a < T * k; ++a) {
+        if (ids[a] == -1)
+            continue;
         if (ids[a] < 0 || ids[a] >= E)
             return -1;
         counts[ids[a]] += 1;
@@ -255,12 +259,107 @@ int oracle_permute(int64_t T, int32_t E, int32_t k, const int32_t *ids,
     for (int64_t t = 0; t < T; ++t)
         for (int32_t j = 0; j < k; ++j) {
             int32_t e = ids[t * k + j];
+            if (e == -1) {
+                pos[t * k + j] = -1;
+                continue;
+            }
             int32_t slot = offsets[e] + fill[e];
             fill[e] += 1;
             sorted_token[slot] = (int32_t)t;
             pos[t * k + j] = slot;
         }
     free(fill);
+    return 0;
+}
+
+/* ------------------------------------------------ capacity-limited dispatch */
+
+/*
+ * Expert capacity: ceil(T k / E * capacity_factor), evaluated in binary64 in
+ * that order (P5 §3.2 prints the formula and the value 64 for T = 2048,
+ * k = 2, E = 128, factor 2).
+ */
+int64_t oracle_capacity(int64_t T, int32_t E, int32_t k, double capacity_factor)
+{
+    return (int64_t)ceil((double)T * (double)k / (double)E * capacity_factor);
+}
+
+/*
+ * Capacity-limited dispatch of a routing (P5 §3.2: an expert whose queue is
+ * full sends further tokens to their next-best expert; P2 §3.2: the capacity
+ * factor trades drops against idle capacity, and dropped requests are
+ * retried at the next-best expert).  Read as two passes over the T k
+ * assignments in row-major (token, slot) order, the order in which they
+ * queue:
+ *   1. an assignment keeps its expert while that expert holds fewer than
+ *      cap assignments; otherwise it overflows;
+ *   2. (policy 1, reroute) each overflowed assignment, in the same order,
+ *      moves to the best-ranked expert (larger z first, NaN last, ties to the
+ *      lower index) that its token does not already use and that holds fewer
+ *      than cap assignments; with no such expert, or under policy 0 (drop),
+ *      it is dropped: id -1.
+ * ids [T][k] is read (the top-k routing) and rewritten; z and p are the
+ * routing's [T][E] logits-over-tau and softmax rows.  gates/gate_p receive
+ * p[t][id] (0 for a dropped assignment), not renormalised.  counts[E]
+ * receives the per-expert totals.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_capacity_dispatch(int64_t T, int32_t E, int32_t k, int64_t cap, int32_t policy,
+                             const double *z, const double *p, int32_t *ids, float *gates,
+                             double *gate_p, int32_t *counts)
+{
+    if (T < 0 || E < 1 || k < 1 || cap < 0 || (policy != 0 && policy != 1))
+        return -1;
+    uint8_t *overflow = (uint8_t *)calloc((size_t)(T * k > 0 ? T * k : 1), 1);
+    if (!overflow)
+        return -1;
+    for (int32_t e = 0; e < E; ++e)
+        counts[e] = 0;
+    /* pass 1 */
+    for (int64_t a = 0; a < T * k; ++a) {
+        int32_t e = ids[a];
+        if (e < 0 || e >= E) {
+            free(overflow);
+            return -1;
+        }
+        if (counts[e] < cap) {
+            counts[e] += 1;
+        } else {
+            overflow[a] = 1;
+            ids[a] = -1;
+        }
+    }
+    /* pass 2 */
+    if (policy == 1) {
+        for (int64_t t = 0; t < T; ++t)
+            for (int32_t j = 0; j < k; ++j) {
+                if (!overflow[t * k + j])
+                    continue;
+                int32_t best = -1;
+                for (int32_t e = 0; e < E; ++e) {
+                    if (counts[e] >= cap)
+                        continue;
+                    int used = 0;
+                    for (int32_t jj = 0; jj < k; ++jj)
+                        if (ids[t * k + jj] == e)
+                            used = 1;
+                    if (used)
+                        continue;
+                    if (best < 0 || ranks_before(z + t * E, e, best))
+                        best = e;
+                }
+                if (best >= 0) {
+                    ids[t * k + j] = best;
+                    counts[best] += 1;
+                }
+            }
+    }
+    for (int64_t a = 0; a < T * k; ++a) {
+        double g = ids[a] >= 0 ? p[(a / k) * E + ids[a]] : 0.0;
+        gates[a] = (float)g;
+        if (gate_p)
+            gate_p[a] = g;
+    }
+    free(overflow);
     return 0;
 }
 
@@ -383,6 +482,8 @@ int oracle_forward_tokens(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t
             y[r * d + c] = 0.0;
         for (int32_t j = 0; j < k; ++j) {
             int32_t e = ids[t * k + j];
+            if (e == -1)
+                continue; /* dropped by capacity-limited dispatch */
             if (e < 0 || e >= E || !W1[e] || !W2[e]) {
                 rc = -1;
                 break;

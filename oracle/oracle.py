@@ -58,6 +58,10 @@ class Oracle:
         lib.oracle_permute.restype = ctypes.c_int
         lib.oracle_router_stats.argtypes = [_I64, _I32, _I32, _P, _P, _P, _P, _P]
         lib.oracle_router_stats.restype = ctypes.c_int
+        lib.oracle_capacity.argtypes = [_I64, _I32, _I32, ctypes.c_double]
+        lib.oracle_capacity.restype = ctypes.c_int64
+        lib.oracle_capacity_dispatch.argtypes = [_I64, _I32, _I32, _I64, _I32, _P, _P, _P, _P, _P, _P]
+        lib.oracle_capacity_dispatch.restype = ctypes.c_int
         lib.oracle_expert_ffn.argtypes = [_I64, _I64, _I32, _P, _P, _P, _P, _P, _P]
         lib.oracle_expert_ffn.restype = ctypes.c_int
         lib.oracle_forward_tokens.argtypes = [_I64, _I64, _I64, _I32, _I32, _I32, _I32, _P,
@@ -122,6 +126,28 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_permute: expert id out of range")
         return dict(counts=counts, offsets=offsets, sorted_token=sorted_token, pos=pos)
+
+    def capacity(self, T, E, k, capacity_factor):
+        """ceil(T k / E * capacity_factor) in binary64."""
+        return int(self.lib.oracle_capacity(T, E, k, float(capacity_factor)))
+
+    def capacity_dispatch(self, route, capacity_factor, policy):
+        """Capacity-limited dispatch of a routing made with want_zp=True.  policy 0 drops
+        overflow, 1 reroutes it.  Returns dict(ids (-1 = dropped), gates, gate_p, counts, cap)."""
+        ids = np.ascontiguousarray(route["ids"], dtype=np.int32).copy()
+        z = np.ascontiguousarray(route["z"], dtype=np.float64)
+        p = np.ascontiguousarray(route["p"], dtype=np.float64)
+        T, k = ids.shape
+        E = z.shape[1]
+        cap = self.capacity(T, E, k, capacity_factor)
+        gates = np.zeros((T, k), dtype=np.float32)
+        gate_p = np.zeros((T, k), dtype=np.float64)
+        counts = np.zeros(E, dtype=np.int32)
+        rc = self.lib.oracle_capacity_dispatch(T, E, k, cap, policy, z.ctypes.data, p.ctypes.data, ids.ctypes.data,
+                                               gates.ctypes.data, gate_p.ctypes.data, counts.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle_capacity_dispatch rejected its arguments")
+        return dict(ids=ids, gates=gates, gate_p=gate_p, counts=counts, cap=cap)
 
     def router_stats(self, ids, p):
         """Routing statistics from ids [T,k] and full softmax rows p [T,E] (binary64):

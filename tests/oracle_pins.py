@@ -448,6 +448,91 @@ def pin_invariants_at_tiny_workload(orc):
     assert np.all(np.isfinite(out["y"]))
 
 
+# --------------------------------------------------- capacity-limited dispatch
+
+def pin_capacity_formula(orc):
+    """P5 §3.2 prints ceil(2048 * 2 / 128 * 2) = 64; two more values by hand."""
+    assert orc.capacity(2048, 128, 2, 2.0) == 64
+    assert orc.capacity(4096, 16, 2, 1.25) == 640
+    assert orc.capacity(10, 3, 2, 1.0) == 7          # ceil(6.67)
+    assert orc.capacity(8, 128, 2, 1.0) == 1         # ceil(0.125)
+
+
+def _ranked_routing(orc, T, E, k, order_bias):
+    """Every token ranks the experts alike: bias alone sets the logits."""
+    return orc.route(np.zeros((T, 4), np.float32), np.zeros((4, E), np.float32), k, F32,
+                     bias=np.asarray(order_bias, np.float32), want_zp=True)
+
+
+def pin_capacity_by_hand(orc):
+    """All 10 tokens rank experts 0 > 1 > 2 > 3 (k = 1) and the capacity is 3
+    (factor 1.2: ceil(10/4*1.2) = 3).  Drop: tokens 0-2 keep expert 0, the
+    rest are dropped (id -1, gate 0).  Reroute: tokens 3-5 move to expert 1,
+    6-8 to expert 2, token 9 to expert 3, each gated by its own probability.
+    With k = 2 (every token's top-2 = {0, 1}) and capacity 2 (factor 0.4:
+    ceil(10*2/4*0.4) = 2): tokens 0 and 1 keep both; token 2's two slots move
+    to experts 2 and then 3 (not 2 again: the token already uses it); token 3
+    fills the second places of experts 2 and 3; every later slot is dropped."""
+    r = _ranked_routing(orc, 10, 4, 1, [3.0, 2.0, 1.0, 0.0])
+    drop = orc.capacity_dispatch(r, 1.2, 0)
+    assert drop["cap"] == 3
+    assert drop["ids"].ravel().tolist() == [0, 0, 0] + [-1] * 7
+    assert drop["counts"].tolist() == [3, 0, 0, 0]
+    assert np.all(drop["gates"].ravel()[3:] == 0) and np.all(drop["gates"].ravel()[:3] == r["gates"].ravel()[:3])
+    rr = orc.capacity_dispatch(r, 1.2, 1)
+    assert rr["ids"].ravel().tolist() == [0, 0, 0, 1, 1, 1, 2, 2, 2, 3]
+    assert rr["counts"].tolist() == [3, 3, 3, 1]
+    want = np.array([r["p"][t, e] for t, e in enumerate(rr["ids"].ravel())])
+    assert np.array_equal(rr["gate_p"].ravel(), want)
+
+    r2 = _ranked_routing(orc, 10, 4, 2, [3.0, 2.0, 1.0, 0.0])
+    assert np.all(r2["ids"] == [0, 1])
+    rr2 = orc.capacity_dispatch(r2, 0.4, 1)
+    assert rr2["cap"] == 2
+    assert rr2["ids"].tolist() == [[0, 1], [0, 1], [2, 3], [2, 3]] + [[-1, -1]] * 6
+    assert rr2["counts"].tolist() == [2, 2, 2, 2]
+    dr2 = orc.capacity_dispatch(r2, 0.4, 0)
+    assert dr2["ids"].tolist() == [[0, 1], [0, 1]] + [[-1, -1]] * 8
+
+
+def pin_capacity_invariants(orc):
+    """Random skewed routing: no expert exceeds the capacity; a token never
+    uses an expert twice; under drop the kept assignments are exactly the
+    first `cap` of each expert in row-major order (numpy's stable argsort
+    rank); kept gates equal the uncapped ones; a capacity of at least T k
+    changes nothing; reroute with factor 2 drops nothing here; counts equal
+    numpy's bincount of the surviving ids."""
+    (x, Wg, _, _), _ = _tiny(41, T=60, E=6, dtype=BF16)
+    bias = np.array([2.0, 1.0, 0.5, 0.0, -0.5, -1.0], np.float32)
+    r = orc.route(x, Wg, 2, BF16, bias=bias, want_zp=True)
+    T, k, E = 60, 2, 6
+    flat = r["ids"].ravel()
+    order = np.argsort(flat, kind="stable")
+    rank = np.empty_like(order)
+    for e in range(E):
+        sel = order[flat[order] == e]
+        rank[sel] = np.arange(len(sel))
+    for cf in (0.5, 0.9, 1.3):
+        dr = orc.capacity_dispatch(r, cf, 0)
+        cap = dr["cap"]
+        keep = rank < cap
+        assert np.array_equal(dr["ids"].ravel(), np.where(keep, flat, -1))
+        assert np.array_equal(dr["gates"].ravel(), np.where(keep, r["gates"].ravel(), 0.0))
+        assert np.array_equal(dr["counts"], np.bincount(flat[keep], minlength=E))
+        for pol in (0, 1):
+            out = orc.capacity_dispatch(r, cf, pol)
+            assert out["counts"].max() <= out["cap"]
+            for row in out["ids"]:
+                live = row[row >= 0]
+                assert len(set(live.tolist())) == len(live)
+            live = out["ids"].ravel()
+            assert np.array_equal(out["counts"], np.bincount(live[live >= 0], minlength=E))
+    big = orc.capacity_dispatch(r, 100.0, 1)
+    assert np.array_equal(big["ids"], r["ids"]) and np.array_equal(big["gates"], r["gates"])
+    rr = orc.capacity_dispatch(r, 2.0, 1)
+    assert np.all(rr["ids"] >= 0) and rr["counts"].sum() == T * k
+
+
 # ---------------------------------------------------------- router statistics
 
 def pin_router_stats_closed_forms(orc):

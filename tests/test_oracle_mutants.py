@@ -59,6 +59,20 @@ MUTANTS = [
      "sf += (mean_prob[e] - 1.0 / E) * (mean_prob[e] - 1.0 / E);"),
     ("std without 1/E", "scalars[3] = sqrt(sf / E);", "scalars[3] = sqrt(sf);"),
     ("mean prob not averaged", "mean_prob[e] /= (double)T;", "mean_prob[e] /= (double)E;"),
+    ("capacity rounds down", "return (int64_t)ceil((double)T * (double)k / (double)E * capacity_factor);",
+     "return (int64_t)floor((double)T * (double)k / (double)E * capacity_factor);"),
+    ("capacity off by one", "if (counts[e] < cap) {", "if (counts[e] <= cap) {"),
+    ("reroute to the worst expert", "if (best < 0 || ranks_before(z + t * E, e, best))",
+     "if (best < 0 || ranks_before(z + t * E, best, e))"),
+    ("reroute reuses the token's expert", "if (ids[t * k + jj] == e)\n                            used = 1;",
+     "if (ids[t * k + jj] == e)\n                            used = 0;"),
+    ("reroute ignores capacity", "if (counts[e] >= cap)\n                        continue;",
+     "if (counts[e] > cap + 100)\n                        continue;"),
+    ("dropped slot keeps its gate", "double g = ids[a] >= 0 ? p[(a / k) * E + ids[a]] : 0.0;",
+     "double g = ids[a] >= 0 ? p[(a / k) * E + ids[a]] : p[(a / k) * E];"),
+    ("reroute in reverse token order",
+     "for (int64_t t = 0; t < T; ++t)\n            for (int32_t j = 0; j < k; ++j) {\n                if (!overflow",
+     "for (int64_t t = T - 1; t >= 0; --t)\n            for (int32_t j = 0; j < k; ++j) {\n                if (!overflow"),
 ]
 
 
