@@ -92,9 +92,27 @@ typedef struct moe_config {
     uint64_t token_offset; /* absolute index of token 0, so successive calls draw fresh noise */
     int32_t gemm_path;     /* moe_gemm_path */
     int32_t reserved;      /* must be 0 */
+    float capacity_factor; /* 0: dropless (every token gets k experts); > 0 (finite): expert capacity
+                              cap = ceil(T k / E * capacity_factor) in binary64 (P5 §3.2; P2 §3.2),
+                              which only moe_forward applies; a cap >= T changes nothing */
+    int32_t capacity_policy; /* moe_capacity_policy (must be valid even when capacity_factor == 0) */
 } moe_config;
 
-/* Bytes of device workspace moe_forward needs for `cfg` (0 when T == 0). */
+/* What happens to an assignment whose expert is full (P5 §3.2; P2 §3.2).  The
+ * T k assignments queue in row-major (token, slot) order; each keeps its
+ * expert while that expert holds fewer than cap.  DROP: an overflowing
+ * assignment is dropped.  REROUTE: then, in the same order, each overflowing
+ * assignment moves to the best-ranked expert (larger z first, NaN last, ties
+ * to the lower index) that its token does not already use and that holds
+ * fewer than cap; with none left it is dropped.  A dropped assignment has
+ * expert id -1 and gate 0 and adds nothing to y; gates are never renormalised. */
+typedef enum moe_capacity_policy {
+    MOE_CAPACITY_DROP = 0,
+    MOE_CAPACITY_REROUTE = 1
+} moe_capacity_policy;
+
+/* Bytes of device workspace moe_forward needs for `cfg` (0 when T == 0); capacity-limited
+ * dispatch adds the [T][E] logit and probability rows. */
 moe_status moe_workspace_size(const moe_config *cfg, size_t *bytes);
 
 /* Bytes of device workspace moe_router needs for `cfg`. */
@@ -113,6 +131,10 @@ moe_status moe_router_workspace_size(const moe_config *cfg, size_t *bytes);
  *   gate_weights [T][k]   float, softmax(z)[ids]         (device, out)
  *   counts       [E]      int32, tokens routed per expert (sum = T*k)  (device, out)
  *   workspace    >= moe_workspace_size() bytes, 256-byte aligned       (device, scratch)
+ * With a capacity (capacity_factor > 0) expert_ids and gate_weights hold the
+ * dispatched routing: a rerouted slot names its new expert (no longer in z
+ * order), a dropped slot has id -1 and gate 0, and counts sum to the
+ * assignments kept.
  * T == 0 is a valid no-op that writes counts = 0.
  */
 moe_status moe_forward(const moe_config *cfg, const void *x, const void *Wg, const float *router_bias,
@@ -161,7 +183,8 @@ moe_status moe_router_stats(const moe_config *cfg, const void *x, const void *Wg
  * stable expert-major order of the T*k assignments taken in row-major
  * (token, slot) order: sorted_token[offsets[e] + r] is the token of the r-th
  * assignment to e, pos[t][j] is the position of assignment (t, j).
- * Bit-exact and deterministic.
+ * Bit-exact and deterministic.  An id outside [0, E) (a dropped slot, -1)
+ * is left out: its pos is -1 and offsets[E] counts only the others.
  *   expert_ids [T][k] (device, in); counts [E], offsets [E+1],
  *   sorted_token [T*k], pos [T][k]: int32 (device, out)
  */
@@ -190,7 +213,8 @@ moe_status moe_grouped_gemm(const moe_config *cfg, int32_t which, const void *A,
 
 /*
  * Combine stage (P2 §2.2 step 4; P5 §3.2): y[t][c] = sum_{j<k} gate_weights[t][j] * Y[pos[t][j]][c],
- * summed in ascending j in fp32, stored in act_dtype (round to nearest even).
+ * summed in ascending j in fp32 over the slots with pos >= 0, stored in
+ * act_dtype (round to nearest even).
  *   Y [T*k][d] float, pos [T][k] int32, gate_weights [T][k] float (device, in);
  *   y [T][d] act_dtype (device, out)
  */

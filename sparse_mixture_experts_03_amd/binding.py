@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
 F32, BF16, INT4_G128 = 0, 1, 2
 GEMM_AUTO, GEMM_STREAMING, GEMM_TILED = 0, 1, 2
+CAPACITY_DROP, CAPACITY_REROUTE = 0, 1
 
 EXPORTS = ("moe_workspace_size", "moe_router_workspace_size", "moe_forward", "moe_router", "moe_permute",
            "moe_grouped_gemm", "moe_combine", "moe_router_stats_workspace_size", "moe_router_stats",
@@ -35,6 +36,8 @@ class MoeConfig(ctypes.Structure):
         ("token_offset", ctypes.c_uint64),
         ("gemm_path", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
+        ("capacity_factor", ctypes.c_float),
+        ("capacity_policy", ctypes.c_int32),
     ]
 
 
@@ -84,9 +87,9 @@ def status_string(status):
 
 
 def config(T, d, d_ff, E, k, act_dtype, w_dtype, tau=1.0, use_gumbel=False, seed=0, token_offset=0,
-           gemm_path=GEMM_AUTO):
+           gemm_path=GEMM_AUTO, capacity_factor=0.0, capacity_policy=CAPACITY_DROP):
     return MoeConfig(T, d, d_ff, E, k, act_dtype, w_dtype, tau, int(bool(use_gumbel)), seed, token_offset,
-                     gemm_path, 0)
+                     gemm_path, 0, capacity_factor, capacity_policy)
 
 
 def _ptr(t):

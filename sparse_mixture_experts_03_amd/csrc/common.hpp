@@ -56,6 +56,17 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Expert ranking of the router and of capacity rerouting: is (za, ea) ranked
+// before (zb, eb)?  Larger z first, NaN last, ties to the lower expert index.
+__device__ __forceinline__ bool ranks_before(double za, int ea, double zb, int eb) {
+    bool na = isnan(za), nb = isnan(zb);
+    if (na != nb) return nb;
+    if (!na && za != zb) return za > zb;
+    return ea < eb;
+}
+
+constexpr int kNoExpert = 0x7fffffff;
+
 __device__ __forceinline__ float gelu_erf(float h) {
     return 0.5f * h * (1.0f + erff(h * 0.70710678118654752440f));
 }

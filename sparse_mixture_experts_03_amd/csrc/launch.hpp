@@ -32,6 +32,7 @@ struct RouterArgs {
     float* gates;
     double* prob_rows = nullptr;     // optional [T][E]: every token's softmax row (router statistics)
     double* entropy_rows = nullptr;  // optional [T]: every token's -sum p ln p
+    double* z_rows = nullptr;        // optional [T][E]: every token's (l + g) / tau
 };
 hipError_t launch_router(const RouterArgs& a, hipStream_t stream);
 
@@ -44,6 +45,16 @@ size_t stats_scratch_bytes(int E);
 hipError_t launch_router_stats(const double* prob_rows, const double* entropy_rows, const int32_t* ids, int64_t T,
                                int E, int k, void* scratch, double* fraction, double* mean_prob, double* scalars,
                                hipStream_t stream);
+// ------------------------------------------------ capacity-limited dispatch
+// In place on ids/gates [T][k] (the top-k routing), given the stable
+// permutation of that routing (pos, offsets, counts from launch_permute), the
+// [T][E] rows z (ranking) and p (gates), the capacity 1 <= cap <= T and the
+// policy (0 drop, 1 reroute).  Overflowing assignments end with id -1 and
+// gate 0, or with their rerouted expert and its probability.
+hipError_t launch_capacity(int32_t* ids, float* gates, const int32_t* pos, const int32_t* offsets,
+                           const int32_t* counts, const double* z_rows, const double* prob_rows, int64_t T, int E,
+                           int k, int cap, int policy, hipStream_t stream);
+
 // fraction[E] = mean_prob[E] = scalars[4] = 0 (empty batch)
 hipError_t launch_zero_stats(int E, double* fraction, double* mean_prob, double* scalars, hipStream_t stream);
 

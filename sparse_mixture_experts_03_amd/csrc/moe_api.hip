@@ -1,6 +1,8 @@
 // C ABI of the MoE-layer forward: argument checks, workspace carve-up and the
 // stream-ordered launch sequence
-//   router (partial logits, finalize) -> permute -> GEMM1 (+GeLU) -> GEMM2 -> combine.
+//   router (partial logits, finalize) -> permute -> GEMM1 (+GeLU) -> GEMM2 -> combine,
+// with capacity-limited dispatch
+//   router (+ z and p rows) -> permute -> capacity -> permute -> GEMM1 -> GEMM2 -> combine.
 // No host synchronisation and no host<->device copy happens inside a call;
 // counts and the dispatch order stay on the device and every kernel finds its
 // work from them.
@@ -48,6 +50,10 @@ moe_status check_config(const moe_config* c) {
     if (c->use_gumbel != 0 && c->use_gumbel != 1) return MOE_ERR_INVALID_ARGUMENT;
     if (c->gemm_path < MOE_GEMM_AUTO || c->gemm_path > MOE_GEMM_TILED) return MOE_ERR_INVALID_ARGUMENT;
     if (c->reserved != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (!(c->capacity_factor == 0.0f || (c->capacity_factor > 0.0f && isfinite(c->capacity_factor))))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (c->capacity_policy != MOE_CAPACITY_DROP && c->capacity_policy != MOE_CAPACITY_REROUTE)
+        return MOE_ERR_INVALID_ARGUMENT;
     if (c->act_dtype != MOE_DTYPE_F32 && c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARGUMENT;
     if (c->w_dtype < MOE_DTYPE_F32 || c->w_dtype > MOE_DTYPE_INT4_G128) return MOE_ERR_INVALID_ARGUMENT;
     if (c->w_dtype == MOE_DTYPE_INT4_G128 && (c->d % 128 != 0 || c->d_ff % 128 != 0))
@@ -66,8 +72,20 @@ moe_status check_config(const moe_config* c) {
     return MOE_OK;
 }
 
+// Expert capacity ceil(T k / E * capacity_factor), evaluated in binary64 and
+// clamped to T (no expert can receive more than T assignments, since a
+// token's k experts are distinct); 0 means dropless dispatch.
+int64_t capacity_of(const moe_config& c) {
+    if (c.capacity_factor == 0.0f || c.T == 0) return 0;
+    const double v = ceil((double)c.T * (double)c.k / (double)c.E * (double)c.capacity_factor);
+    return v >= (double)c.T ? c.T : (int64_t)v;
+}
+
+// Capacity can change the routing only when it is below T.
+bool capacity_active(const moe_config& c) { return capacity_of(c) > 0 && capacity_of(c) < c.T; }
+
 struct Layout {
-    size_t partial, offsets, sorted_token, pos, H, Y, total;
+    size_t partial, offsets, sorted_token, pos, H, Y, z_rows, prob_rows, total;
 };
 
 Layout layout_of(const moe_config& c) {
@@ -87,6 +105,13 @@ Layout layout_of(const moe_config& c) {
     off = round_up(off + hbytes * Tk * (size_t)c.d_ff, 256);
     L.Y = off;
     off = round_up(off + sizeof(float) * Tk * (size_t)c.d, 256);
+    L.z_rows = L.prob_rows = 0;
+    if (capacity_active(c)) {
+        L.z_rows = off;
+        off = round_up(off + sizeof(double) * (size_t)c.T * (size_t)c.E, 256);
+        L.prob_rows = off;
+        off = round_up(off + sizeof(double) * (size_t)c.T * (size_t)c.E, 256);
+    }
     L.total = c.T == 0 ? 0 : off;
     return L;
 }
@@ -212,11 +237,24 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
     void* H = ws + L.H;
     float* Y = reinterpret_cast<float*>(ws + L.Y);
 
-    hipError_t e = moe::launch_router(router_args(c, x, Wg, router_bias, expert_ids, gate_weights, ws + L.partial),
-                                      stream);
+    moe::RouterArgs r = router_args(c, x, Wg, router_bias, expert_ids, gate_weights, ws + L.partial);
+    const bool limited = capacity_active(c);
+    if (limited) {
+        r.z_rows = reinterpret_cast<double*>(ws + L.z_rows);
+        r.prob_rows = reinterpret_cast<double*>(ws + L.prob_rows);
+    }
+    hipError_t e = moe::launch_router(r, stream);
     if (e != hipSuccess) return hip_fail(e);
     e = moe::launch_permute(expert_ids, c.T, c.E, c.k, counts, offsets, sorted_token, pos, stream);
     if (e != hipSuccess) return hip_fail(e);
+    if (limited) {
+        // queue ranks come from the top-k dispatch order; the GEMMs use the dispatch of the final ids
+        e = moe::launch_capacity(expert_ids, gate_weights, pos, offsets, counts, r.z_rows, r.prob_rows, c.T, c.E,
+                                 c.k, (int)capacity_of(c), c.capacity_policy, stream);
+        if (e != hipSuccess) return hip_fail(e);
+        e = moe::launch_permute(expert_ids, c.T, c.E, c.k, counts, offsets, sorted_token, pos, stream);
+        if (e != hipSuccess) return hip_fail(e);
+    }
     e = run_gemm(c, 1, x, sorted_token, offsets, W1, W1_scales, W1_expert_stride, H, stream);
     if (e != hipSuccess) return hip_fail(e);
     e = run_gemm(c, 2, H, nullptr, offsets, W2, W2_scales, W2_expert_stride, Y, stream);

@@ -167,17 +167,6 @@ __device__ __forceinline__ double gumbel_draw(uint64_t seed, uint64_t token, uin
     return -log(-log(u));
 }
 
-// Is (za, ea) ranked before (zb, eb)?  Larger z first, NaN last, ties to the
-// lower expert index.
-__device__ __forceinline__ bool ranks_before(double za, int ea, double zb, int eb) {
-    bool na = isnan(za), nb = isnan(zb);
-    if (na != nb) return nb;
-    if (!na && za != zb) return za > zb;
-    return ea < eb;
-}
-
-constexpr int kNoExpert = 0x7fffffff;
-
 // One workgroup per token.  Thread e sums the split partials of expert e (all
 // loads issued before the adds, summed in split order), adds bias and noise
 // and applies the temperature; wavefront 0 then picks the top-k and forms the
@@ -186,7 +175,8 @@ __global__ void __launch_bounds__(256)
 router_finalize_kernel(const double* __restrict__ partial, int nsplit, int T, int E, int k,
                        const float* __restrict__ bias, double tau, int use_gumbel, uint64_t seed,
                        uint64_t token_offset, int32_t* __restrict__ ids, float* __restrict__ gates,
-                       double* __restrict__ prob_rows, double* __restrict__ entropy_rows) {
+                       double* __restrict__ prob_rows, double* __restrict__ entropy_rows,
+                       double* __restrict__ z_rows) {
     __shared__ double zs[256];
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
@@ -232,8 +222,13 @@ router_finalize_kernel(const double* __restrict__ partial, int nsplit, int T, in
     for (int j = 0; j < 4; ++j)
         if (live[j]) s += exp(z[j] - m);
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (z_rows) {  // capacity-limited dispatch reranks overflowing tokens
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (live[j]) z_rows[(int64_t)t * E + lane + 64 * j] = z[j];
+    }
     if (prob_rows) {
-        // router statistics: this token's full softmax row and its entropy -sum p ln p (0 ln 0 = 0)
+        // this token's full softmax row, and (router statistics) its entropy -sum p ln p (0 ln 0 = 0)
         double h = 0.0;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -243,7 +238,7 @@ router_finalize_kernel(const double* __restrict__ partial, int nsplit, int T, in
                 if (!(p == 0.0)) h -= p * log(p);
             }
         for (int off = 32; off >= 1; off >>= 1) h += __shfl_xor(h, off, 64);
-        if (lane == 0) entropy_rows[t] = h;
+        if (lane == 0 && entropy_rows) entropy_rows[t] = h;
     }
     // top-k by repeated wavefront argmax
     bool taken[4] = {false, false, false, false};
@@ -315,7 +310,7 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t stream) {
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(router_finalize_kernel, dim3((unsigned)a.T), dim3(256), 0, stream, a.partial, p.splits,
                        (int)a.T, a.E, a.k, a.bias, (double)a.tau, a.use_gumbel, a.seed, a.token_offset, a.ids,
-                       a.gates, a.prob_rows, a.entropy_rows);
+                       a.gates, a.prob_rows, a.entropy_rows, a.z_rows);
     return hipGetLastError();
 }
 

@@ -116,7 +116,7 @@ def sample_tokens(ids, E, max_tokens, exclude=(), rng_seed=0):
 def oracle_y(orc, cfg, inp, ref, tokens):
     """Oracle y rows for `tokens`, copying back only the experts they use."""
     E = cfg["E"]
-    used = sorted(set(ref["ids"][tokens].reshape(-1).tolist()))
+    used = sorted(e for e in set(ref["ids"][tokens].reshape(-1).tolist()) if e >= 0)  # -1: dropped slot
     W1 = [None] * E
     W2 = [None] * E
     S1 = [None] * E if inp["S1"] is not None else None

@@ -63,7 +63,7 @@ def _cfg(**kw):
     base = dict(T=8, d=256, d_ff=512, E=8, k=2, act_dtype=moe.BF16, w_dtype=moe.BF16)
     base.update(kw)
     c = moe.config(base["T"], base["d"], base["d_ff"], base["E"], base["k"], base["act_dtype"], base["w_dtype"])
-    for key in ("tau", "use_gumbel", "gemm_path", "reserved"):
+    for key in ("tau", "use_gumbel", "gemm_path", "reserved", "capacity_factor", "capacity_policy"):
         if key in kw:
             setattr(c, key, kw[key])
     return c
@@ -74,6 +74,9 @@ BAD = [
     dict(d=100), dict(d_ff=96), dict(d=0), dict(d=1 << 18), dict(tau=0.0), dict(tau=-1.0), dict(tau=float("nan")),
     dict(tau=float("inf")), dict(use_gumbel=2), dict(gemm_path=3), dict(reserved=1), dict(act_dtype=2),
     dict(w_dtype=3), dict(w_dtype=moe.INT4_G128, d=192), dict(w_dtype=moe.INT4_G128, d_ff=320),
+    dict(capacity_factor=-1.0), dict(capacity_factor=float("nan")), dict(capacity_factor=float("inf")),
+    dict(capacity_factor=-0.0 - 1e-30), dict(capacity_policy=2), dict(capacity_policy=-1),
+    dict(capacity_factor=1.25, capacity_policy=7),
 ]
 
 
@@ -129,6 +132,25 @@ def test_workspace_size_accounts_for_buffers(lib):
     assert lib.moe_workspace_size(ctypes.byref(_cfg(T=0)), ctypes.byref(n)) == 0 and n.value == 0
     assert lib.moe_workspace_size(ctypes.byref(c), None) == binding.MOE_ERR_INVALID_ARGUMENT
     assert lib.moe_workspace_size(None, ctypes.byref(n)) == binding.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_capacity_workspace(lib):
+    """A capacity below T adds the [T][E] binary64 logit and probability rows
+    to the workspace; a capacity of at least T (ceil(T k / E * cf) >= T)
+    cannot drop anything and adds nothing."""
+    n0, n1 = ctypes.c_size_t(), ctypes.c_size_t()
+    T, E = 2048, 128
+    base = _cfg(T=T, d=512, d_ff=512, E=E)
+    assert lib.moe_workspace_size(ctypes.byref(base), ctypes.byref(n0)) == 0
+    for cf, policy, extra in [(1.25, moe.CAPACITY_DROP, True), (2.0, moe.CAPACITY_REROUTE, True),
+                              (64.0, moe.CAPACITY_DROP, False), (1e30, moe.CAPACITY_REROUTE, False),
+                              (0.0, moe.CAPACITY_REROUTE, False)]:
+        c = _cfg(T=T, d=512, d_ff=512, E=E, capacity_factor=cf, capacity_policy=policy)
+        assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n1)) == 0
+        if extra:
+            assert n1.value >= n0.value + 2 * T * E * 8, cf
+        else:
+            assert n1.value == n0.value, cf
 
 
 def _forward(lib, c, **ptr):
