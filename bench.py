@@ -1,12 +1,17 @@
 """Benchmark of the MoE-layer forward on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                [--capacity-factor CF --capacity-policy drop|reroute]
 
 One step = the whole layer (router, dispatch, W1 GEMM + GeLU, W2 GEMM,
 combine) over one batch of seeded synthetic input already resident in HBM.
 Prints one JSON line: tokens/s over the timed steps, the roofline of the
 dominant kernel (the W1 grouped GEMM) measured with HIP events on the stream
 it runs on, and the CPU oracle timed on a bounded sample of the same workload.
+With a capacity factor the step is the capacity-limited layer (expert
+capacity ceil(T k / E * CF), overflow dropped or rerouted).  The line also
+carries the router alone and the router with its batch statistics, each timed
+with HIP events.
 """
 import argparse
 import hashlib
@@ -33,6 +38,8 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="0: automatic")
+    ap.add_argument("--capacity-factor", type=float, default=0.0, help="0: dropless dispatch")
+    ap.add_argument("--capacity-policy", choices=["drop", "reroute"], default="drop")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy first (reference kernel for HBM byte counters)")
     return ap.parse_args()
@@ -80,7 +87,9 @@ def main():
     print(f"[bench] generating {args.workload} on {dev}", file=sys.stderr, flush=True)
     inp = moe_synth.generate(cfg, device=dev, seed=0)
     torch.cuda.synchronize()
-    c = moe.config(T, d, d_ff, E, k, cfg["act"], cfg["w"], tau=cfg["tau"], use_gumbel=cfg["gumbel"], seed=0)
+    policy = moe.CAPACITY_REROUTE if args.capacity_policy == "reroute" else moe.CAPACITY_DROP
+    c = moe.config(T, d, d_ff, E, k, cfg["act"], cfg["w"], tau=cfg["tau"], use_gumbel=cfg["gumbel"], seed=0,
+                   capacity_factor=args.capacity_factor, capacity_policy=policy)
     layer = moe.MoELayerForward(c, device=dev)
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -103,11 +112,12 @@ def main():
     tokens_per_s = T * args.steps / wall
 
     counts = layer.counts.cpu().numpy()
+    kept = int(counts.sum())
     active = int((counts > 0).sum())
     wbits = {moe.F32: 32, moe.BF16: 16, moe.INT4_G128: 4}[cfg["w"]]
     abytes = 4 if cfg["act"] == moe.F32 else 2
     w_bytes = d * d_ff * wbits // 8 + (d * d_ff // 128 * 2 if cfg["w"] == moe.INT4_G128 else 0)
-    Tk = T * k
+    Tk = kept  # dispatched rows (T k without a capacity)
     hbytes = 4 if cfg["w"] == moe.F32 else 2
 
     # dominant kernel: the W1 grouped GEMM (+GeLU), timed alone with HIP events on its stream
@@ -120,16 +130,21 @@ def main():
     cnt = torch.empty(E, dtype=torch.int32, device=dev)
     moe.moe_permute(c, layer.expert_ids, cnt, offsets, sorted_token, pos)
     gemm = lambda: moe.moe_grouped_gemm(c, 1, inp["x"], sorted_token, offsets, inp["W1"], inp["S1"], H)
-    for _ in range(3):
-        gemm()
     reps = max(10, args.steps)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(reps):
-        gemm()
-    ev1.record(stream)
-    ev1.synchronize()
-    gemm_ms = ev0.elapsed_time(ev1) / reps
+    gemm_ms = time_on_stream(torch, stream, gemm, reps)
+
+    # the router alone, and with its batch statistics (expert fractions, mean probabilities, entropy, balance terms)
+    r_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    r_gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    r_ws = torch.empty(max(256, moe.moe_router_workspace_size(c)), dtype=torch.uint8, device=dev)
+    s_ws = torch.empty(max(256, moe.moe_router_stats_workspace_size(c)), dtype=torch.uint8, device=dev)
+    frac = torch.empty(E, dtype=torch.float64, device=dev)
+    mprob = torch.empty(E, dtype=torch.float64, device=dev)
+    scal = torch.empty(4, dtype=torch.float64, device=dev)
+    router_ms = time_on_stream(torch, stream, lambda: moe.moe_router(c, inp["x"], inp["Wg"], inp["bias"], r_ids,
+                                                                     r_gates, r_ws), reps)
+    stats_ms = time_on_stream(torch, stream, lambda: moe.moe_router_stats(c, inp["x"], inp["Wg"], inp["bias"], r_ids,
+                                                                          r_gates, frac, mprob, scal, s_ws), reps)
     if cfg["w"] == moe.F32:
         path = "f32"
     elif T <= 16 or (cfg["w"] == moe.INT4_G128 and (d % 1024 or d_ff % 1024)):
@@ -155,7 +170,7 @@ def main():
     roof.update(kernel=kernel_name, avg_launch_ms=round(gemm_ms, 4),
                 algorithmic_bytes=gemm_bytes, algorithmic_flops=gemm_flops)
 
-    step_bytes = (T * d * abytes + d * E * abytes + active * 2 * w_bytes + T * d * abytes + Tk * 8 + E * 4)
+    step_bytes = (T * d * abytes + d * E * abytes + active * 2 * w_bytes + T * d * abytes + T * k * 8 + E * 4)
     out = {
         "metric": "MoE-layer tokens/s",
         "value": round(tokens_per_s, 1),
@@ -170,17 +185,35 @@ def main():
         "dtype": {moe.F32: "f32", moe.BF16: "bf16", moe.INT4_G128: "bf16 (int4 g128 experts)"}[cfg["w"]],
         "data": "synthetic (seeded N(0,1/fan_in) weights, N(0,1) tokens)",
         "config": {"workload": args.workload, "T": T, "d": d, "d_ff": d_ff, "E": E, "k": k,
-                   "router_bias": bool(cfg["bias"]), "tau": cfg["tau"], "gumbel": bool(cfg["gumbel"])},
+                   "router_bias": bool(cfg["bias"]), "tau": cfg["tau"], "gumbel": bool(cfg["gumbel"]),
+                   "capacity_factor": args.capacity_factor,
+                   "capacity_policy": args.capacity_policy if args.capacity_factor > 0 else None},
         "layer_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "layer_mfma_frac": round(2 * gemm_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "active_experts": active,
         "counts_var": float(np.var(counts)),
+        "assignments_kept": kept,
+        "router_ms": round(router_ms, 4),
+        "router_stats_ms": round(stats_ms, 4),
         "roofline": roof,
     }
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, layer, args)
     print(json.dumps(out))
+
+
+def time_on_stream(torch, stream, fn, reps):
+    """Average milliseconds of fn() (which enqueues work on `stream`), from HIP events on that stream."""
+    for _ in range(3):
+        fn()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(reps):
+        fn()
+    ev1.record(stream)
+    ev1.synchronize()
+    return ev0.elapsed_time(ev1) / reps
 
 
 def cpu_baseline(cfg, inp, layer, args):
@@ -201,10 +234,14 @@ def cpu_baseline(cfg, inp, layer, args):
     tokens = np.linspace(0, T - 1, n).round().astype(np.int64)
     tokens = np.unique(tokens)
     t0 = time.perf_counter()
+    limited = args.capacity_factor > 0
     ref = orc.route(xb, wgb, cfg["k"], cfg["act"], bias=bias, tau=float(np.float32(cfg["tau"])),
-                    use_gumbel=cfg["gumbel"], seed=0)
+                    use_gumbel=cfg["gumbel"], seed=0, want_zp=limited)
+    if limited:
+        ref = orc.capacity_dispatch(ref, float(np.float32(args.capacity_factor)),
+                                    1 if args.capacity_policy == "reroute" else 0)
     t_route = time.perf_counter() - t0
-    used = sorted(set(ref["ids"][tokens].reshape(-1).tolist()))
+    used = sorted(e for e in set(ref["ids"][tokens].reshape(-1).tolist()) if e >= 0)
     E = cfg["E"]
     W1 = [None] * E
     W2 = [None] * E
@@ -227,7 +264,8 @@ def cpu_baseline(cfg, inp, layer, args):
     t_ffn = (time.perf_counter() - t0) / reps
     secs = t_route * len(tokens) / T + t_ffn
     return {"value": round(len(tokens) / secs, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(tokens)} of {T} tokens (routing of all {T} tokens, prorated; expert FFNs and combine "
+            "sample": f"{len(tokens)} of {T} tokens (routing{' and capacity dispatch' if limited else ''} of all "
+                      f"{T} tokens, prorated; expert FFNs and combine "
                       f"of the sample, repeated {reps}x), single-threaded fp64 C oracle; "
                       f"{t_route + t_ffn * reps:.1f} s measured"}
 

@@ -18,12 +18,21 @@
 // Pass 1 is parallel over the assignments.  Pass 2 is a sequential greedy
 // fill (each choice depends on every earlier one through the expert counts),
 // so it runs on one workgroup: the assignments stream through in chunks of
-// whole tokens, the chunk's overflowing assignments are listed in order with
-// a block scan, every wavefront stages their tokens' z rows in LDS, and one
-// wavefront then walks the list, each step a 64-lane argmax over the experts
-// with the per-expert counts and the chunk's current ids in LDS.
+// whole tokens and the chunk's overflowing assignments are listed in order
+// with a block scan.  Wavefront 0 then walks the list while the other
+// fifteen stage, one batch ahead in a double-buffered LDS ring, each listed
+// token's experts as 64-bit keys that order like z (the token's kept experts
+// get the lowest key).  Wavefront 0 holds every expert's count in registers
+// (lane l owns experts l, l + 64, ...), so one step is: mask full experts and
+// those the token took earlier in the walk, a DPP max-reduction of the keys,
+// a DPP min-reduction of the expert index among the lanes holding the
+// maximum (ties go to the lower index), and a register increment.
 #include "common.hpp"
 #include "launch.hpp"
+
+// Wavefront reductions of ROCm's device library (DPP based).
+extern "C" __device__ uint32_t __ockl_wfred_max_u32(uint32_t);
+extern "C" __device__ uint32_t __ockl_wfred_min_u32(uint32_t);
 
 namespace moe {
 
@@ -34,30 +43,44 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kPerThread = 4;
 constexpr int kChunk = kThreads * kPerThread;  // assignments per chunk (rounded down to whole tokens)
 constexpr int kMaxE = 256;
-constexpr int kStageDoubles = 8192;            // 64 KB of staged z rows
+constexpr int kRingKeys = 4096;                // keys per ring buffer (32 KB)
 constexpr int kMaxK = 8;
+
+// A 64-bit key that orders like the router's ranking: larger z larger key,
+// any NaN below every number, and 0 reserved for "not a candidate".  -0 is
+// folded into +0 (they compare equal, so the lower index must decide).
+__device__ __forceinline__ uint64_t rank_key(double z) {
+    if (isnan(z)) return 1;
+    const uint64_t b = (uint64_t)__double_as_longlong(z + 0.0);
+    return (b >> 63) ? ~b : (b | (1ull << 63));
+}
 
 __global__ void __launch_bounds__(kThreads)
 capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int32_t* __restrict__ pos,
                 const int32_t* __restrict__ offsets, const int32_t* __restrict__ counts,
                 const double* __restrict__ z_rows, const double* __restrict__ prob_rows, int64_t Tk, int E, int k,
                 int cap, int reroute) {
-    __shared__ int cnt[kMaxE];        // assignments each expert holds
     __shared__ int offs[kMaxE];       // first dispatch position of each expert in the top-k routing
-    __shared__ int cur[kChunk];       // the chunk's current expert per assignment (-1: none)
+    __shared__ int cur[kChunk];       // the chunk's expert per assignment after pass 1 (-1: overflow)
     __shared__ int list[kChunk];      // the chunk's overflowing assignments, row-major
+    __shared__ int res[kChunk];       // their final experts (-1: dropped)
+    __shared__ int ltok[kChunk];      // their tokens (chunk-local)
     __shared__ int wsum[kWaves];
-    __shared__ double zs[kStageDoubles];
+    __shared__ uint64_t ring[2][kRingKeys];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
-    if (tid < E) {
-        cnt[tid] = min(counts[tid], cap);  // what pass 1 keeps
-        offs[tid] = offsets[tid];
+    if (tid < E) offs[tid] = offsets[tid];
+    // wavefront 0: the count of expert lane + 64 j after pass 1, then after each reroute
+    int held[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = lane + 64 * j;
+        held[j] = (w == 0 && e < E) ? min(counts[e], cap) : cap;  // absent experts count as full
     }
     __syncthreads();
     const int chunk = (kChunk / k) * k;
-    const int rows = min(256, kStageDoubles / E);
+    const int rows = min(256, kRingKeys / E);  // listed assignments per ring buffer
 
     for (int64_t base = 0; base < Tk; base += chunk) {
         const int n_here = (int)min((int64_t)chunk, Tk - base);
@@ -93,57 +116,83 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
         int at = before + incl - c;
 #pragma unroll
         for (int r = 0; r < kPerThread; ++r)
-            if ((over >> r) & 1) list[at++] = kPerThread * tid + r;
+            if ((over >> r) & 1) {
+                const int i = kPerThread * tid + r;
+                res[at] = -1;
+                ltok[at] = i / k;
+                list[at++] = i;
+            }
         __syncthreads();
 
-        // pass 2 (reroute), in batches of staged z rows
-        if (reroute) {
-            for (int q0 = 0; q0 < total; q0 += rows) {
-                const int nr = min(rows, total - q0);
-                for (int idx = tid; idx < nr * E; idx += kThreads) {
+        // pass 2 (reroute)
+        if (reroute && total > 0) {
+            const int nb = (total + rows - 1) / rows;
+            // keys of listed assignments [q0, q0 + nr) into ring[buf], by threads t0, t0 + stride, ...
+            auto stage = [&](int q0, int nr, uint64_t* buf, int t0, int stride) {
+                for (int idx = t0; idx < nr * E; idx += stride) {
                     const int r = idx / E;
                     const int e = idx - r * E;
-                    const int64_t t = (base + list[q0 + r]) / k;
-                    zs[idx] = z_rows[t * E + e];
+                    const int i = list[q0 + r];
+                    const int first = i - i % k;  // the token's slot 0 (chunks hold whole tokens)
+                    bool kept = false;
+                    for (int jj = 0; jj < k; ++jj) kept |= cur[first + jj] == e;
+                    buf[idx] = kept ? 0ull : rank_key(z_rows[((base + i) / k) * E + e]);
                 }
-                __syncthreads();
+            };
+            stage(0, min(rows, total), ring[0], tid, kThreads);
+            __syncthreads();
+            int tok = -1;  // wavefront 0: the token being rerouted, and the experts it took so far
+            int took = 0;
+            for (int b = 0; b < nb; ++b) {
+                const int q0 = b * rows;
+                const int nr = min(rows, total - q0);
                 if (w == 0) {
-                    for (int r = 0; r < nr; ++r) {
-                        const int i = list[q0 + r];
-                        const int first = i - i % k;  // the token's slot 0 (chunks hold whole tokens)
-                        int tok[kMaxK];
+                    const uint64_t* buf = ring[b & 1];
+                    uint64_t key[4];
 #pragma unroll
-                        for (int jj = 0; jj < kMaxK; ++jj) tok[jj] = jj < k ? cur[first + jj] : -1;
-                        double bz = 0.0;
-                        int be = kNoExpert;
+                    for (int j = 0; j < 4; ++j) key[j] = lane + 64 * j < E ? buf[lane + 64 * j] : 0ull;
+                    for (int r = 0; r < nr; ++r) {
+                        const int t = ltok[q0 + r];
+                        if (t != tok) {
+                            tok = t;
+                            took = 0;
+                        }
+                        uint64_t bk = 0;
+                        int bj = 0;
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            const int e = lane + 64 * j;
-                            if (e < E && cnt[e] < cap) {
-                                bool used = false;
+                            uint64_t kj = key[j];
+                            if (held[j] >= cap || ((took >> j) & 1)) kj = 0;
+                            if (kj > bk) {  // strict: the lower index keeps a tie
+                                bk = kj;
+                                bj = j;
+                            }
+                        }
+                        if (r + 1 < nr) {  // the next step's keys load under this step's reductions
 #pragma unroll
-                                for (int jj = 0; jj < kMaxK; ++jj) used |= tok[jj] == e;
-                                const double z = zs[r * E + e];
-                                if (!used && (be == kNoExpert || ranks_before(z, e, bz, be))) {
-                                    bz = z;
-                                    be = e;
-                                }
-                            }
+                            for (int j = 0; j < 4; ++j)
+                                key[j] = lane + 64 * j < E ? buf[(r + 1) * E + lane + 64 * j] : 0ull;
                         }
-                        for (int off = 32; off >= 1; off >>= 1) {
-                            const double oz = __shfl_xor(bz, off, 64);
-                            const int oe = __shfl_xor(be, off, 64);
-                            if (oe != kNoExpert && (be == kNoExpert || ranks_before(oz, oe, bz, be))) {
-                                bz = oz;
-                                be = oe;
+                        // max over the wavefront: high halves, then low halves among the lanes that tie
+                        const uint32_t hi = (uint32_t)(bk >> 32);
+                        const uint32_t mhi = __ockl_wfred_max_u32(hi);
+                        const uint32_t mlo = __ockl_wfred_max_u32(hi == mhi ? (uint32_t)bk : 0u);
+                        if (mhi != 0 || mlo != 0) {
+                            const bool top = hi == mhi && (uint32_t)bk == mlo;
+                            const uint32_t be = __ockl_wfred_min_u32(top ? (uint32_t)(lane + 64 * bj) : 0xffffffffu);
+                            if (lane == (int)(be & 63)) {
+#pragma unroll
+                                for (int j = 0; j < 4; ++j)
+                                    if (j == (int)(be >> 6)) {
+                                        held[j] += 1;
+                                        took |= 1 << j;
+                                    }
                             }
-                        }
-                        // every lane holds the same be; LDS operations of one wavefront complete in order
-                        if (be != kNoExpert && lane == 0) {
-                            cur[i] = be;
-                            cnt[be] += 1;
+                            if (lane == 0) res[q0 + r] = (int)be;
                         }
                     }
+                } else if (b + 1 < nb) {
+                    stage(q0 + rows, min(rows, total - q0 - rows), ring[(b + 1) & 1], tid - 64, kThreads - 64);
                 }
                 __syncthreads();
             }
@@ -151,13 +200,12 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
 
         // the overflowing assignments' final ids and gates
         for (int q = tid; q < total; q += kThreads) {
-            const int i = list[q];
-            const int64_t a = base + i;
-            const int e = cur[i];
+            const int64_t a = base + list[q];
+            const int e = res[q];
             ids[a] = e;
             gates[a] = e >= 0 ? (float)prob_rows[(a / k) * E + e] : 0.0f;
         }
-        __syncthreads();  // cur, list and wsum are reused by the next chunk
+        __syncthreads();  // cur, list, res and wsum are reused by the next chunk
     }
 }
 
