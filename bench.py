@@ -140,7 +140,7 @@ def main():
     s_ws = torch.empty(max(256, moe.moe_router_stats_workspace_size(c)), dtype=torch.uint8, device=dev)
     frac = torch.empty(E, dtype=torch.float64, device=dev)
     mprob = torch.empty(E, dtype=torch.float64, device=dev)
-    scal = torch.empty(4, dtype=torch.float64, device=dev)
+    scal = torch.empty(5, dtype=torch.float64, device=dev)
     router_ms = time_on_stream(torch, stream, lambda: moe.moe_router(c, inp["x"], inp["Wg"], inp["bias"], r_ids,
                                                                      r_gates, r_ws), reps)
     stats_ms = time_on_stream(torch, stream, lambda: moe.moe_router_stats(c, inp["x"], inp["Wg"], inp["bias"], r_ids,

@@ -168,6 +168,8 @@ moe_status moe_router(const moe_config *cfg, const void *x, const void *Wg, cons
  *   scalars[1] = sum_e (expert_fraction[e] - 1/E)^2
  *   scalars[2] = sum_e (mean_prob[e] - 1/E)^2
  *   scalars[3] = sqrt(scalars[1] / E)   (standard deviation of expert_fraction)
+ *   scalars[4] = E sum_e expert_fraction[e] * mean_prob[e]   (product form of the
+ *                balance term; 1 when both are uniform)
  * All outputs are device pointers (double arrays 8-byte aligned).  T == 0
  * writes zeros.  workspace >= moe_router_stats_workspace_size() bytes,
  * 256-byte aligned (it holds the T x E softmax rows).

@@ -376,6 +376,9 @@ int oracle_capacity_dispatch(int64_t T, int32_t E, int32_t k, int64_t cap, int32
  *   scalars[2]   = sum_e (mean_prob[e] - 1/E)^2            P3 §3.2 (without lambda)
  *   scalars[3]   = sqrt( (1/E) sum_e (fraction[e] - 1/E)^2 ) spread of expert
  *                  utilisation (population standard deviation) P5 §4 monitoring
+ *   scalars[4]   = E sum_e fraction[e] * mean_prob[e]       the product form of the
+ *                  balance term, pairing P5 §3.2's assignment fractions with
+ *                  P3 §4.2's mean probabilities (1 when both are uniform)
  * Sums run in ascending index order.  Returns 0, or -1 if T < 1 or an id is
  * out of range.
  */
@@ -404,17 +407,19 @@ int oracle_router_stats(int64_t T, int32_t E, int32_t k, const int32_t *ids, con
         }
         entropy += h;
     }
-    double sf = 0.0, sp = 0.0;
+    double sf = 0.0, sp = 0.0, fp = 0.0;
     for (int32_t e = 0; e < E; ++e) {
         fraction[e] /= (double)T * (double)k;
         mean_prob[e] /= (double)T;
         sf += (fraction[e] - 1.0 / E) * (fraction[e] - 1.0 / E);
         sp += (mean_prob[e] - 1.0 / E) * (mean_prob[e] - 1.0 / E);
+        fp += fraction[e] * mean_prob[e];
     }
     scalars[0] = entropy / (double)T;
     scalars[1] = sf;
     scalars[2] = sp;
     scalars[3] = sqrt(sf / E);
+    scalars[4] = (double)E * fp;
     return 0;
 }
 

@@ -151,20 +151,20 @@ class Oracle:
 
     def router_stats(self, ids, p):
         """Routing statistics from ids [T,k] and full softmax rows p [T,E] (binary64):
-        dict(fraction[E], mean_prob[E], entropy, lb_fraction, lb_prob, fraction_std)."""
+        dict(fraction[E], mean_prob[E], entropy, lb_fraction, lb_prob, fraction_std, lb_product)."""
         ids = np.ascontiguousarray(ids, dtype=np.int32)
         p = np.ascontiguousarray(p, dtype=np.float64)
         T, k = ids.shape
         E = p.shape[1]
         fraction = np.zeros(E, dtype=np.float64)
         mean_prob = np.zeros(E, dtype=np.float64)
-        scalars = np.zeros(4, dtype=np.float64)
+        scalars = np.zeros(5, dtype=np.float64)
         rc = self.lib.oracle_router_stats(T, E, k, ids.ctypes.data, p.ctypes.data, fraction.ctypes.data,
                                           mean_prob.ctypes.data, scalars.ctypes.data)
         if rc != 0:
             raise ValueError("oracle_router_stats rejected its arguments")
         return dict(fraction=fraction, mean_prob=mean_prob, entropy=scalars[0], lb_fraction=scalars[1],
-                    lb_prob=scalars[2], fraction_std=scalars[3], scalars=scalars)
+                    lb_prob=scalars[2], fraction_std=scalars[3], lb_product=scalars[4], scalars=scalars)
 
     # -- experts ------------------------------------------------------------------
     def expert_ffn(self, xr, W1e, W2e, w_dtype, S1e=None, S2e=None):

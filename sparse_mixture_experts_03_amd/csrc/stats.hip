@@ -5,7 +5,8 @@
 //     P_e = sum_t p[t][e] / T over the full softmax rows;
 //   P5 §3.2 balance loss: sum_e (f_e - 1/E)^2 with f_e the fraction of the
 //     T k assignments routed to e; P3 §3.2 writes the same sum over P_e;
-//   P5 §4 monitoring: the spread (standard deviation) of f_e across experts.
+//   P5 §4 monitoring: the spread (standard deviation) of f_e across experts;
+//   the product form E sum_e f_e P_e of the balance term (1 when uniform).
 // The router's finalize step writes each token's softmax row and entropy;
 // here one workgroup per expert sums its column (and counts its assignments)
 // in a fixed order, and one workgroup forms the per-expert and scalar
@@ -68,7 +69,7 @@ stats_final_kernel(const double* __restrict__ colsum, const int64_t* __restrict_
     __shared__ double red[kThreads];
     const int e = threadIdx.x;
     const double inv_e = 1.0 / (double)E;
-    double df2 = 0.0, dp2 = 0.0;
+    double df2 = 0.0, dp2 = 0.0, fp = 0.0;
     if (e < E) {
         const double f = (double)count[e] / ((double)T * (double)k);
         const double pm = colsum[e] / (double)T;
@@ -76,14 +77,17 @@ stats_final_kernel(const double* __restrict__ colsum, const int64_t* __restrict_
         mean_prob[e] = pm;
         df2 = (f - inv_e) * (f - inv_e);
         dp2 = (pm - inv_e) * (pm - inv_e);
+        fp = f * pm;
     }
     const double sf = block_sum(df2, red);
     const double sp = block_sum(dp2, red);
+    const double sfp = block_sum(fp, red);
     if (e == 0) {
         scalars[0] = colsum[E] / (double)T;
         scalars[1] = sf;
         scalars[2] = sp;
         scalars[3] = sqrt(sf / (double)E);
+        scalars[4] = (double)E * sfp;
     }
 }
 
@@ -93,7 +97,7 @@ __global__ void zero_stats_kernel(int E, double* fraction, double* mean_prob, do
         fraction[i] = 0.0;
         mean_prob[i] = 0.0;
     }
-    if (i < 4) scalars[i] = 0.0;
+    if (i < 5) scalars[i] = 0.0;
 }
 
 }  // namespace

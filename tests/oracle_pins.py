@@ -542,7 +542,10 @@ def pin_router_stats_closed_forms(orc):
     makes p one-hot: entropy exactly 0 and that expert's mean probability 1.
     Two experts, two tokens with logit gaps +ln 3 and -ln 3: p = (3/4, 1/4)
     and (1/4, 3/4), mean probabilities 1/2, entropy = the binary entropy of
-    1/4 (scipy), and top-1 fractions 1/2 each."""
+    1/4 (scipy), and top-1 fractions 1/2 each.  The product term
+    E sum_e f_e P_e is 1 whenever the mean probabilities are uniform, and
+    E * (1/2) * 1 = E/2 for the one-hot case (half the assignments on the
+    expert that holds all the probability)."""
     T, d, E, k = 10, 8, 6, 2
     uni = orc.route(np.zeros((T, d), np.float32), np.zeros((d, E), np.float32), k, F32, want_zp=True)
     st = orc.router_stats(uni["ids"], uni["p"])
@@ -555,6 +558,7 @@ def pin_router_stats_closed_forms(orc):
     lb_f = k * (1.0 / k - 1.0 / E) ** 2 + (E - k) * (1.0 / E) ** 2
     assert abs(st["lb_fraction"] - lb_f) <= 1e-15
     assert abs(st["fraction_std"] - math.sqrt(lb_f / E)) <= 1e-15
+    assert abs(st["lb_product"] - 1.0) <= 1e-15
 
     bias = np.zeros(E, np.float32)
     bias[3] = 1000.0
@@ -562,6 +566,7 @@ def pin_router_stats_closed_forms(orc):
     st = orc.router_stats(hot["ids"], hot["p"])
     assert st["entropy"] == 0.0 and st["mean_prob"][3] == 1.0
     assert np.all(hot["ids"][:, 0] == 3)
+    assert st["lb_product"] == E / 2
 
     # two tokens x = +1 and -1 against Wg = (q, -q), q = fp32(ln 3 / 2): logit gaps +-2q
     q = float(np.float32(math.log(3.0) / 2))
@@ -574,6 +579,7 @@ def pin_router_stats_closed_forms(orc):
     assert np.array_equal(st["fraction"], [0.5, 0.5])
     assert abs(st["entropy"] - stats.entropy([pa, 1.0 - pa])) <= 1e-15
     assert st["lb_fraction"] == 0.0 and st["fraction_std"] == 0.0
+    assert abs(st["lb_product"] - 1.0) <= 1e-15
 
 
 def pin_router_stats_invariants(orc):
@@ -595,7 +601,8 @@ def pin_router_stats_invariants(orc):
     sp = orc.router_stats(outp["ids"], outp["p"])
     assert np.allclose(sp["fraction"], st["fraction"][perm], rtol=0, atol=0)
     assert np.allclose(sp["mean_prob"], st["mean_prob"][perm], rtol=0, atol=1e-15)
-    for key in ("entropy", "lb_fraction", "lb_prob", "fraction_std"):
+    assert st["lb_product"] > 0
+    for key in ("entropy", "lb_fraction", "lb_prob", "fraction_std", "lb_product"):
         assert abs(sp[key] - st[key]) <= 1e-14 * max(1.0, abs(st[key]))
 
 

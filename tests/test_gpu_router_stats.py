@@ -44,7 +44,7 @@ def _run_stats(cfg, inp, dev, noise_seed=9):
     gates = torch.zeros((T, k), dtype=torch.float32, device=dev)
     frac = torch.full((E,), -1.0, dtype=torch.float64, device=dev)
     mprob = torch.full((E,), -1.0, dtype=torch.float64, device=dev)
-    scal = torch.full((4,), -1.0, dtype=torch.float64, device=dev)
+    scal = torch.full((5,), -1.0, dtype=torch.float64, device=dev)
     ws = torch.empty(max(256, moe.moe_router_stats_workspace_size(c)), dtype=torch.uint8, device=dev)
     moe.moe_router_stats(c, inp["x"], inp["Wg"], inp["bias"], ids, gates, frac, mprob, scal, ws)
     # the plain router for comparison
@@ -78,7 +78,7 @@ def test_router_stats_parity(dev, oracle, name):
     assert np.array_equal(frac, st["fraction"]), np.max(np.abs(frac - st["fraction"]))
     assert np.max(np.abs(out["mprob"].cpu().numpy() - st["mean_prob"])) <= 1e-12
     scal = out["scal"].cpu().numpy()
-    for i, key in enumerate(("entropy", "lb_fraction", "lb_prob", "fraction_std")):
+    for i, key in enumerate(("entropy", "lb_fraction", "lb_prob", "fraction_std", "lb_product")):
         assert abs(scal[i] - st[key]) <= 1e-12 * max(1.0, abs(st[key])), (key, scal[i], st[key])
 
 
@@ -87,7 +87,7 @@ def test_router_stats_empty_batch(dev):
     c = H.abi_config(cfg)
     frac = torch.full((8,), 7.0, dtype=torch.float64, device=dev)
     mprob = torch.full((8,), 7.0, dtype=torch.float64, device=dev)
-    scal = torch.full((4,), 7.0, dtype=torch.float64, device=dev)
+    scal = torch.full((5,), 7.0, dtype=torch.float64, device=dev)
     moe.moe_router_stats(c, None, None, None, None, None, frac, mprob, scal, None)
     torch.cuda.synchronize()
     assert frac.abs().sum().item() == 0 and mprob.abs().sum().item() == 0 and scal.abs().sum().item() == 0

@@ -58,6 +58,9 @@ MUTANTS = [
     ("balance term on fractions uses probs", "sf += (fraction[e] - 1.0 / E) * (fraction[e] - 1.0 / E);",
      "sf += (mean_prob[e] - 1.0 / E) * (mean_prob[e] - 1.0 / E);"),
     ("std without 1/E", "scalars[3] = sqrt(sf / E);", "scalars[3] = sqrt(sf);"),
+    ("product term without E", "scalars[4] = (double)E * fp;", "scalars[4] = fp;"),
+    ("product term pairs fraction with itself", "fp += fraction[e] * mean_prob[e];",
+     "fp += fraction[e] * fraction[e];"),
     ("mean prob not averaged", "mean_prob[e] /= (double)T;", "mean_prob[e] /= (double)E;"),
     ("capacity rounds down", "return (int64_t)ceil((double)T * (double)k / (double)E * capacity_factor);",
      "return (int64_t)floor((double)T * (double)k / (double)E * capacity_factor);"),
