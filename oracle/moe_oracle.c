@@ -31,6 +31,11 @@
  *      Selecting on z equals selecting on softmax(z) (softmax is monotone). P1 §3.1 step 4; P2 §2.2 step 3
  *   5. p = softmax(z) over all E, max-subtracted; gate[j] = p[ids[j]] (not
  *      renormalised over the k chosen).                              P2 §2.2 step 4; P5 §3.1 worked example
+ *   Variants (oracle_route_ex):
+ *   2'. Gaussian noise sigma * n[e] added to the logits, n standard normal by
+ *      Box-Muller from the same Philox block: z = (l + g + sigma n) / tau   P5 §3.3 (router noise injection)
+ *   5'. renormalised gates: gate[j] = softmax over the k chosen z values
+ *      (= p[ids[j]] / sum_j' p[ids[j']])                                   P4 §4.3 (softmax over the top-k)
  *   6. expert FFN  o = W2_e * GeLU(W1_e * x),  GeLU(h) = h * Phi(h)
  *                  = 0.5 h (1 + erf(h / sqrt 2)), no bias.           P3 §3.2 (d -> 4d -> d MLP, GELU)
  *      W1_e is d_ff x d, W2_e is d x d_ff (out x in, input dim contiguous).
@@ -132,6 +137,20 @@ double oracle_gumbel(uint64_t seed, uint64_t token, uint64_t expert)
     return -log(-log(u));
 }
 
+/* Standard normal draw for (seed, token, expert): the Box-Muller transform
+ * (Box & Muller, 1958) sqrt(-2 ln u1) cos(2 pi u2) of two uniforms built like
+ * oracle_uniform from words 2 and 3 of the same Philox block (word 0 feeds
+ * the Gumbel draw).   P5 §3.3 (Gaussian noise on the router logits). */
+double oracle_normal(uint64_t seed, uint64_t token, uint64_t expert)
+{
+    uint64_t ctr[4] = {token, expert, 0, 0}, key[2] = {seed, 0}, r[4];
+    oracle_philox4x64_10(ctr, key, r);
+    const double two_pi = 6.283185307179586; /* 2 pi rounded to binary64 */
+    double u1 = ((double)(r[2] >> 11) + 0.5) * (1.0 / 9007199254740992.0);
+    double u2 = ((double)(r[3] >> 11) + 0.5) * (1.0 / 9007199254740992.0);
+    return sqrt(-2.0 * log(u1)) * cos(two_pi * u2);
+}
+
 /* GeLU in its exact form h * Phi(h). */
 double oracle_gelu(double h)
 {
@@ -154,16 +173,21 @@ static int ranks_before(const double *z, int32_t a, int32_t b)
 
 /*
  * Router for all T tokens.  Writes ids[T][k] (best first), gates[T][k] =
- * (float) p[ids], and optionally gate_p[T][k] (the same probabilities in
- * binary64), z_out[T][E] and p_out[T][E].  bias may be NULL.
- * Returns 0, or -1 on a bad argument.
+ * (float) gate, and optionally gate_p[T][k] (the same gates in binary64),
+ * z_out[T][E] and p_out[T][E] (the full softmax rows).  bias may be NULL.
+ * noise_std: sigma of the Gaussian logit noise (0: none).  gate_norm: 0 gives
+ * gate = p[id]; 1 gives the softmax over the k chosen z, max-subtracted at the
+ * best one and summed in slot order.  Returns 0, or -1 on a bad argument.
  */
-int oracle_route(int64_t T, int64_t d, int32_t E, int32_t k, int32_t act_dtype,
-                 const void *x, const void *Wg, const float *bias,
-                 double tau, int32_t use_gumbel, uint64_t seed, uint64_t token_offset,
-                 int32_t *ids, float *gates, double *gate_p, double *z_out, double *p_out)
+int oracle_route_ex(int64_t T, int64_t d, int32_t E, int32_t k, int32_t act_dtype,
+                    const void *x, const void *Wg, const float *bias,
+                    double tau, int32_t use_gumbel, double noise_std, int32_t gate_norm,
+                    uint64_t seed, uint64_t token_offset,
+                    int32_t *ids, float *gates, double *gate_p, double *z_out, double *p_out)
 {
     if (T < 0 || d < 1 || E < 1 || k < 1 || k > E || !(tau > 0.0))
+        return -1;
+    if (!(noise_std >= 0.0) || (gate_norm != 0 && gate_norm != 1))
         return -1;
     if (act_dtype != ORACLE_F32 && act_dtype != ORACLE_BF16)
         return -1;
@@ -190,7 +214,10 @@ int oracle_route(int64_t T, int64_t d, int32_t E, int32_t k, int32_t act_dtype,
         /* 2-3. noise and temperature. */
         for (int32_t e = 0; e < E; ++e) {
             double g = use_gumbel ? oracle_gumbel(seed, token_offset + (uint64_t)t, (uint64_t)e) : 0.0;
-            z[e] = (l[e] + g) / tau;
+            double v = l[e] + g;
+            if (noise_std > 0.0)
+                v += noise_std * oracle_normal(seed, token_offset + (uint64_t)t, (uint64_t)e);
+            z[e] = v / tau;
         }
         /* 5. softmax over all experts. */
         double m = z[0];
@@ -218,6 +245,18 @@ int oracle_route(int64_t T, int64_t d, int32_t E, int32_t k, int32_t act_dtype,
             if (gate_p)
                 gate_p[t * k + j] = p[best];
         }
+        if (gate_norm) {
+            /* 5'. softmax over the chosen z (z[ids[0]] is their maximum) */
+            double top = z[ids[t * k]], den = 0.0;
+            for (int32_t j = 0; j < k; ++j)
+                den += exp(z[ids[t * k + j]] - top);
+            for (int32_t j = 0; j < k; ++j) {
+                double gj = exp(z[ids[t * k + j]] - top) / den;
+                gates[t * k + j] = (float)gj;
+                if (gate_p)
+                    gate_p[t * k + j] = gj;
+            }
+        }
         if (z_out)
             memcpy(z_out + t * E, z, sizeof(double) * (size_t)E);
         if (p_out)
@@ -225,6 +264,16 @@ int oracle_route(int64_t T, int64_t d, int32_t E, int32_t k, int32_t act_dtype,
     }
     free(l); free(z); free(p); free(taken);
     return 0;
+}
+
+/* The router of steps 1-5 (no Gaussian noise, gates not renormalised). */
+int oracle_route(int64_t T, int64_t d, int32_t E, int32_t k, int32_t act_dtype,
+                 const void *x, const void *Wg, const float *bias,
+                 double tau, int32_t use_gumbel, uint64_t seed, uint64_t token_offset,
+                 int32_t *ids, float *gates, double *gate_p, double *z_out, double *p_out)
+{
+    return oracle_route_ex(T, d, E, k, act_dtype, x, Wg, bias, tau, use_gumbel, 0.0, 0, seed, token_offset,
+                           ids, gates, gate_p, z_out, p_out);
 }
 
 /* ----------------------------------------------------------------- dispatch */

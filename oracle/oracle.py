@@ -49,11 +49,16 @@ class Oracle:
         lib.oracle_uniform.restype = ctypes.c_double
         lib.oracle_gumbel.argtypes = [_U64, _U64, _U64]
         lib.oracle_gumbel.restype = ctypes.c_double
+        lib.oracle_normal.argtypes = [_U64, _U64, _U64]
+        lib.oracle_normal.restype = ctypes.c_double
         lib.oracle_gelu.argtypes = [ctypes.c_double]
         lib.oracle_gelu.restype = ctypes.c_double
         lib.oracle_route.argtypes = [_I64, _I64, _I32, _I32, _I32, _P, _P, _P,
                                      ctypes.c_double, _I32, _U64, _U64, _P, _P, _P, _P, _P]
         lib.oracle_route.restype = ctypes.c_int
+        lib.oracle_route_ex.argtypes = [_I64, _I64, _I32, _I32, _I32, _P, _P, _P, ctypes.c_double, _I32,
+                                        ctypes.c_double, _I32, _U64, _U64, _P, _P, _P, _P, _P]
+        lib.oracle_route_ex.restype = ctypes.c_int
         lib.oracle_permute.argtypes = [_I64, _I32, _I32, _P, _P, _P, _P, _P]
         lib.oracle_permute.restype = ctypes.c_int
         lib.oracle_router_stats.argtypes = [_I64, _I32, _I32, _P, _P, _P, _P, _P]
@@ -83,13 +88,17 @@ class Oracle:
     def gumbel(self, seed, token, expert):
         return self.lib.oracle_gumbel(seed, token, expert)
 
+    def normal(self, seed, token, expert):
+        return self.lib.oracle_normal(seed, token, expert)
+
     def gelu(self, h):
         return self.lib.oracle_gelu(float(h))
 
     # -- routing ----------------------------------------------------------------
     def route(self, x, Wg, k, act_dtype, bias=None, tau=1.0, use_gumbel=False, seed=0,
-              token_offset=0, want_zp=False):
-        """Returns dict(ids[T,k] int32, gates[T,k] float32, gate_p[T,k] float64 [, z, p])."""
+              token_offset=0, want_zp=False, noise_std=0.0, gate_norm=0):
+        """Returns dict(ids[T,k] int32, gates[T,k] float32, gate_p[T,k] float64 [, z, p]).
+        noise_std: sigma of the Gaussian logit noise; gate_norm=1: gates renormalised over the k chosen."""
         x = np.ascontiguousarray(x)
         Wg = np.ascontiguousarray(Wg)
         T, d = x.shape
@@ -101,12 +110,12 @@ class Oracle:
         gate_p = np.zeros((T, k), dtype=np.float64)
         z = np.zeros((T, E), dtype=np.float64) if want_zp else None
         p = np.zeros((T, E), dtype=np.float64) if want_zp else None
-        rc = self.lib.oracle_route(T, d, E, k, act_dtype, x.ctypes.data, Wg.ctypes.data,
-                                   None if b is None else b.ctypes.data, float(tau),
-                                   int(bool(use_gumbel)), seed, token_offset,
-                                   ids.ctypes.data, gates.ctypes.data, gate_p.ctypes.data,
-                                   None if z is None else z.ctypes.data,
-                                   None if p is None else p.ctypes.data)
+        rc = self.lib.oracle_route_ex(T, d, E, k, act_dtype, x.ctypes.data, Wg.ctypes.data,
+                                      None if b is None else b.ctypes.data, float(tau),
+                                      int(bool(use_gumbel)), float(noise_std), int(gate_norm), seed, token_offset,
+                                      ids.ctypes.data, gates.ctypes.data, gate_p.ctypes.data,
+                                      None if z is None else z.ctypes.data,
+                                      None if p is None else p.ctypes.data)
         if rc != 0:
             raise ValueError("oracle_route rejected its arguments")
         out = dict(ids=ids, gates=gates, gate_p=gate_p)

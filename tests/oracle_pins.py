@@ -275,6 +275,64 @@ def pin_router_worked_example(orc):
     assert np.all(np.sort(out["p"][0])[:-4] < 0.01)
 
 
+def pin_renormalised_gates(orc):
+    """P4 §4.3 takes the softmax over the k chosen values.  On P5 §3.1's worked
+    example this turns 0.42 and 0.38 into 0.42/0.80 = 0.525 and 0.475.  In
+    general: the same experts as without renormalisation; the gates sum to 1;
+    their ratio is exp(z_a - z_b); they equal p[ids] / sum p[ids] of the plain
+    router; with k = 1 the gate is exactly 1."""
+    with open(os.path.join(GOLDEN, "p5_router_example.json")) as f:
+        ex = json.load(f)
+    E = ex["num_experts"]
+    p = np.full(E, ex["rest_mass"] / (E - len(ex["listed"])))
+    for e, pe in ex["listed"].items():
+        p[int(e)] = pe
+    logits = np.log(p).astype(np.float32)
+    out = orc.route(np.zeros((1, 8), np.float32), np.zeros((8, E), np.float32), 2, F32, bias=logits,
+                    gate_norm=1)
+    assert out["ids"].tolist() == [ex["top2_ids"]]
+    assert np.allclose(out["gates"][0], [0.42 / 0.80, 0.38 / 0.80], rtol=0, atol=1e-6)
+
+    (x, Wg, _, _), _ = _tiny(21, T=30, E=9, dtype=BF16)
+    for k in (1, 2, 3):
+        plain = orc.route(x, Wg, k, BF16, use_gumbel=True, seed=4, tau=0.5, want_zp=True)
+        ren = orc.route(x, Wg, k, BF16, use_gumbel=True, seed=4, tau=0.5, want_zp=True, gate_norm=1)
+        assert np.array_equal(ren["ids"], plain["ids"]) and np.array_equal(ren["z"], plain["z"])
+        g = ren["gate_p"]
+        assert np.all(np.abs(g.sum(axis=1) - 1.0) <= 1e-15)
+        want = plain["gate_p"] / plain["gate_p"].sum(axis=1, keepdims=True)
+        assert np.max(np.abs(g - want) / want) <= 1e-14
+        if k == 1:
+            assert np.all(ren["gates"] == 1.0)
+        else:
+            zs = np.take_along_axis(ren["z"], ren["ids"].astype(np.int64), 1)
+            assert np.max(np.abs(g[:, 0] / g[:, 1] / np.exp(zs[:, 0] - zs[:, 1]) - 1.0)) <= 1e-14
+
+
+def pin_gaussian_noise(orc):
+    """P5 §3.3 adds Gaussian noise to the router logits.  The draws are standard
+    normal (KS test against scipy over 20,000 (token, expert) keys; sample mean
+    and variance), independent of the Gumbel draw of the same key (neither n
+    nor n^2 correlates with it); the noise
+    enters as z = (l + sigma n)/tau, keyed on the absolute token (routing a
+    slice with its token offset reproduces the rows of the whole batch)."""
+    n = np.array([orc.normal(17, t, e) for t in range(2000) for e in range(10)])
+    g = np.array([orc.gumbel(17, t, e) for t in range(2000) for e in range(10)])
+    assert stats.kstest(n, "norm").pvalue > 1e-3
+    assert abs(n.mean()) < 4.0 / math.sqrt(len(n)) and abs(n.var() - 1.0) < 0.05
+    assert abs(np.corrcoef(n, g)[0, 1]) < 4.0 / math.sqrt(len(n))
+    assert abs(np.corrcoef(n * n, g)[0, 1]) < 4.0 / math.sqrt(len(n))  # magnitudes independent too
+    (x, Wg, _, _), _ = _tiny(22, T=8, E=6, dtype=F32)
+    a = orc.route(x, Wg, 2, F32, tau=0.5, want_zp=True)
+    b = orc.route(x, Wg, 2, F32, tau=0.5, seed=3, token_offset=40, noise_std=0.1, want_zp=True)
+    for t in range(8):
+        for e in range(6):
+            dn = 0.1 * orc.normal(3, 40 + t, e) / 0.5
+            assert abs((b["z"][t, e] - a["z"][t, e]) - dn) <= 1e-14 * (abs(a["z"][t, e]) + abs(dn) + 1)
+    part = orc.route(x[3:], Wg, 2, F32, tau=0.5, seed=3, token_offset=43, noise_std=0.1, want_zp=True)
+    assert np.array_equal(part["z"], b["z"][3:]) and np.array_equal(part["ids"], b["ids"][3:])
+
+
 def pin_gumbel_max_theorem(orc):
     """Gumbel-max: with noise and tau=1, the first choice is distributed as
     softmax(l), and the ordered pair (a, b) of the top-2 as p_a p_b / (1 - p_a)

@@ -15,8 +15,8 @@ SRC = os.path.join(os.path.dirname(oracle_mod.__file__), "moe_oracle.c")
 MUTANTS = [
     ("bias dropped", "l[e] += (double)bias[e];", "l[e] += 0.0 * (double)bias[e];"),
     ("gumbel sign", "return -log(-log(u));", "return log(-log(u));"),
-    ("tau multiplies", "z[e] = (l[e] + g) / tau;", "z[e] = (l[e] + g) * tau;"),
-    ("noise not tempered", "z[e] = (l[e] + g) / tau;", "z[e] = l[e] / tau + g;"),
+    ("tau multiplies", "z[e] = v / tau;", "z[e] = v * tau;"),
+    ("noise not tempered", "z[e] = v / tau;", "z[e] = (v - g) / tau + g;"),
     ("ties to higher index", "return a < b;", "return a > b;"),
     ("NaN ranks first", "return nb; /* the non-NaN one wins */", "return na;"),
     ("ascending selection", "return z[a] > z[b];", "return z[a] < z[b];"),
@@ -59,6 +59,13 @@ MUTANTS = [
      "sf += (mean_prob[e] - 1.0 / E) * (mean_prob[e] - 1.0 / E);"),
     ("std without 1/E", "scalars[3] = sqrt(sf / E);", "scalars[3] = sqrt(sf);"),
     ("product term without E", "scalars[4] = (double)E * fp;", "scalars[4] = fp;"),
+    ("renormalisation drops the last chosen", "for (int32_t j = 0; j < k; ++j)\n                den +=",
+     "for (int32_t j = 0; j + 1 < k; ++j)\n                den +="),
+    ("gaussian noise not scaled by sigma", "v += noise_std * oracle_normal(", "v += oracle_normal("),
+    ("box-muller without the factor 2", "return sqrt(-2.0 * log(u1)) * cos(two_pi * u2);",
+     "return sqrt(-log(u1)) * cos(two_pi * u2);"),
+    ("gaussian reuses the gumbel word", "double u1 = ((double)(r[2] >> 11) + 0.5)",
+     "double u1 = ((double)(r[0] >> 11) + 0.5)"),
     ("product term pairs fraction with itself", "fp += fraction[e] * mean_prob[e];",
      "fp += fraction[e] * fraction[e];"),
     ("mean prob not averaged", "mean_prob[e] /= (double)T;", "mean_prob[e] /= (double)E;"),
