@@ -1,7 +1,7 @@
 """Benchmark of the MoE-layer forward on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                [--capacity-factor CF --capacity-policy drop|reroute]
+                [--capacity-factor CF --capacity-policy drop|reroute] [--gate-norm] [--noise-std SIGMA]
 
 One step = the whole layer (router, dispatch, W1 GEMM + GeLU, W2 GEMM,
 combine) over one batch of seeded synthetic input already resident in HBM.
@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="0: automatic")
     ap.add_argument("--capacity-factor", type=float, default=0.0, help="0: dropless dispatch")
     ap.add_argument("--capacity-policy", choices=["drop", "reroute"], default="drop")
+    ap.add_argument("--gate-norm", action="store_true", help="gates renormalised over the k chosen experts")
+    ap.add_argument("--noise-std", type=float, default=0.0, help="sigma of Gaussian router-logit noise")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy first (reference kernel for HBM byte counters)")
     return ap.parse_args()
@@ -89,7 +91,8 @@ def main():
     torch.cuda.synchronize()
     policy = moe.CAPACITY_REROUTE if args.capacity_policy == "reroute" else moe.CAPACITY_DROP
     c = moe.config(T, d, d_ff, E, k, cfg["act"], cfg["w"], tau=cfg["tau"], use_gumbel=cfg["gumbel"], seed=0,
-                   capacity_factor=args.capacity_factor, capacity_policy=policy)
+                   capacity_factor=args.capacity_factor, capacity_policy=policy, gate_norm=int(args.gate_norm),
+                   noise_std=args.noise_std)
     layer = moe.MoELayerForward(c, device=dev)
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -187,7 +190,8 @@ def main():
         "config": {"workload": args.workload, "T": T, "d": d, "d_ff": d_ff, "E": E, "k": k,
                    "router_bias": bool(cfg["bias"]), "tau": cfg["tau"], "gumbel": bool(cfg["gumbel"]),
                    "capacity_factor": args.capacity_factor,
-                   "capacity_policy": args.capacity_policy if args.capacity_factor > 0 else None},
+                   "capacity_policy": args.capacity_policy if args.capacity_factor > 0 else None,
+                   "gate_norm": int(args.gate_norm), "noise_std": args.noise_std},
         "layer_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "layer_mfma_frac": round(2 * gemm_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "active_experts": active,
@@ -236,7 +240,8 @@ def cpu_baseline(cfg, inp, layer, args):
     t0 = time.perf_counter()
     limited = args.capacity_factor > 0
     ref = orc.route(xb, wgb, cfg["k"], cfg["act"], bias=bias, tau=float(np.float32(cfg["tau"])),
-                    use_gumbel=cfg["gumbel"], seed=0, want_zp=limited)
+                    use_gumbel=cfg["gumbel"], seed=0, want_zp=limited, gate_norm=int(args.gate_norm),
+                    noise_std=float(np.float32(args.noise_std)))
     if limited:
         ref = orc.capacity_dispatch(ref, float(np.float32(args.capacity_factor)),
                                     1 if args.capacity_policy == "reroute" else 0)

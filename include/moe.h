@@ -96,6 +96,11 @@ typedef struct moe_config {
                               cap = ceil(T k / E * capacity_factor) in binary64 (P5 §3.2; P2 §3.2),
                               which only moe_forward applies; a cap >= T changes nothing */
     int32_t capacity_policy; /* moe_capacity_policy (must be valid even when capacity_factor == 0) */
+    int32_t gate_norm;     /* 0: gate = softmax over all E experts at the chosen ids (not renormalised);
+                              1: softmax over the k chosen z only (P4 §4.3); not combinable with a capacity */
+    float noise_std;       /* sigma >= 0 (finite) of Gaussian router noise (P5 §3.3): z = (l + g + sigma n) / tau,
+                              n standard normal by Box-Muller from words 2 and 3 of the (seed, token, expert)
+                              Philox block; 0: none */
 } moe_config;
 
 /* What happens to an assignment whose expert is full (P5 §3.2; P2 §3.2).  The

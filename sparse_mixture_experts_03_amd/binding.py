@@ -38,6 +38,8 @@ class MoeConfig(ctypes.Structure):
         ("reserved", ctypes.c_int32),
         ("capacity_factor", ctypes.c_float),
         ("capacity_policy", ctypes.c_int32),
+        ("gate_norm", ctypes.c_int32),
+        ("noise_std", ctypes.c_float),
     ]
 
 
@@ -87,9 +89,9 @@ def status_string(status):
 
 
 def config(T, d, d_ff, E, k, act_dtype, w_dtype, tau=1.0, use_gumbel=False, seed=0, token_offset=0,
-           gemm_path=GEMM_AUTO, capacity_factor=0.0, capacity_policy=CAPACITY_DROP):
+           gemm_path=GEMM_AUTO, capacity_factor=0.0, capacity_policy=CAPACITY_DROP, gate_norm=0, noise_std=0.0):
     return MoeConfig(T, d, d_ff, E, k, act_dtype, w_dtype, tau, int(bool(use_gumbel)), seed, token_offset,
-                     gemm_path, 0, capacity_factor, capacity_policy)
+                     gemm_path, 0, capacity_factor, capacity_policy, int(gate_norm), noise_std)
 
 
 def _ptr(t):

@@ -26,6 +26,8 @@ struct RouterArgs {
     int E, k, act_dtype;
     float tau;
     int use_gumbel;
+    float noise_std;     // Gaussian logit noise sigma (0: none)
+    int gate_norm;       // 1: gates renormalised over the k chosen
     uint64_t seed, token_offset;
     double* partial;  // workspace, >= router_plan().partial_bytes
     int32_t* ids;

@@ -54,6 +54,10 @@ moe_status check_config(const moe_config* c) {
         return MOE_ERR_INVALID_ARGUMENT;
     if (c->capacity_policy != MOE_CAPACITY_DROP && c->capacity_policy != MOE_CAPACITY_REROUTE)
         return MOE_ERR_INVALID_ARGUMENT;
+    if (c->gate_norm != 0 && c->gate_norm != 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (!(c->noise_std >= 0.0f) || !isfinite(c->noise_std)) return MOE_ERR_INVALID_ARGUMENT;
+    // a rerouted or dropped slot has no renormalised gate defined
+    if (c->gate_norm == 1 && c->capacity_factor > 0.0f) return MOE_ERR_UNSUPPORTED;
     if (c->act_dtype != MOE_DTYPE_F32 && c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARGUMENT;
     if (c->w_dtype < MOE_DTYPE_F32 || c->w_dtype > MOE_DTYPE_INT4_G128) return MOE_ERR_INVALID_ARGUMENT;
     if (c->w_dtype == MOE_DTYPE_INT4_G128 && (c->d % 128 != 0 || c->d_ff % 128 != 0))
@@ -179,6 +183,8 @@ moe::RouterArgs router_args(const moe_config& c, const void* x, const void* Wg, 
     r.act_dtype = c.act_dtype;
     r.tau = c.tau;
     r.use_gumbel = c.use_gumbel;
+    r.noise_std = c.noise_std;
+    r.gate_norm = c.gate_norm;
     r.seed = c.seed;
     r.token_offset = c.token_offset;
     r.partial = static_cast<double*>(partial);

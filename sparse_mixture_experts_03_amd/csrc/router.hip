@@ -142,8 +142,12 @@ router_partial_kernel(const void* __restrict__ x, const void* __restrict__ Wg, i
 }
 
 // Philox4x64-10 (Salmon et al., SC'11): two 64x64->128 products per round,
-// key bumped by the Weyl constants between rounds.
-__device__ __forceinline__ uint64_t philox_word0(uint64_t c0, uint64_t c1, uint64_t k0, uint64_t k1) {
+// key bumped by the Weyl constants between rounds.  Counter (c0, c1, 0, 0),
+// key (k0, k1); all four output words.
+struct PhiloxBlock {
+    uint64_t w[4];
+};
+__device__ __forceinline__ PhiloxBlock philox_block(uint64_t c0, uint64_t c1, uint64_t k0, uint64_t k1) {
     uint64_t x0 = c0, x1 = c1, x2 = 0, x3 = 0;
     const uint64_t M0 = 0xD2E7470EE14C6C93ULL, M1 = 0xCA5A826395121157ULL;
 #pragma unroll
@@ -158,13 +162,29 @@ __device__ __forceinline__ uint64_t philox_word0(uint64_t c0, uint64_t c1, uint6
         k0 += 0x9E3779B97F4A7C15ULL;
         k1 += 0xBB67AE8584CAA73BULL;
     }
-    return x0;
+    PhiloxBlock b;
+    b.w[0] = x0;
+    b.w[1] = x1;
+    b.w[2] = x2;
+    b.w[3] = x3;
+    return b;
 }
 
-__device__ __forceinline__ double gumbel_draw(uint64_t seed, uint64_t token, uint64_t expert) {
-    uint64_t r0 = philox_word0(token, expert, seed, 0);
-    double u = ((double)(r0 >> 11) + 0.5) * 0x1.0p-53;
-    return -log(-log(u));
+// A uniform strictly inside (0, 1) from the top 53 bits of a word plus half an ulp.
+__device__ __forceinline__ double open_uniform(uint64_t w) { return ((double)(w >> 11) + 0.5) * 0x1.0p-53; }
+
+// Router noise of one (token, expert) key, before the temperature: the Gumbel
+// draw -ln(-ln u) from word 0 (P1 §3.1) and sigma times a standard normal by
+// Box-Muller, sqrt(-2 ln u1) cos(2 pi u2), from words 2 and 3 (P5 §3.3).
+__device__ __forceinline__ double router_noise(double l, int use_gumbel, double noise_std, uint64_t seed,
+                                               uint64_t token, uint64_t expert) {
+    const PhiloxBlock b = philox_block(token, expert, seed, 0);
+    double v = l + (use_gumbel ? -log(-log(open_uniform(b.w[0]))) : 0.0);
+    if (noise_std > 0.0) {
+        const double two_pi = 6.283185307179586;  // 2 pi rounded to binary64
+        v += noise_std * (sqrt(-2.0 * log(open_uniform(b.w[2]))) * cos(two_pi * open_uniform(b.w[3])));
+    }
+    return v;
 }
 
 // One workgroup per token.  Thread e sums the split partials of expert e (all
@@ -173,11 +193,13 @@ __device__ __forceinline__ double gumbel_draw(uint64_t seed, uint64_t token, uin
 // softmax gates from the E values in LDS.
 __global__ void __launch_bounds__(256)
 router_finalize_kernel(const double* __restrict__ partial, int nsplit, int T, int E, int k,
-                       const float* __restrict__ bias, double tau, int use_gumbel, uint64_t seed,
-                       uint64_t token_offset, int32_t* __restrict__ ids, float* __restrict__ gates,
+                       const float* __restrict__ bias, double tau, int use_gumbel, double noise_std,
+                       int gate_norm, uint64_t seed, uint64_t token_offset, int32_t* __restrict__ ids,
+                       float* __restrict__ gates,
                        double* __restrict__ prob_rows, double* __restrict__ entropy_rows,
                        double* __restrict__ z_rows) {
     __shared__ double zs[256];
+    __shared__ int sel[8];  // the chosen experts, best first
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
     if (tid < E) {
@@ -192,8 +214,9 @@ router_finalize_kernel(const double* __restrict__ partial, int nsplit, int T, in
         for (int s = 0; s < kMaxSplits; ++s)
             if (s < nsplit) l += v[s];
         if (bias) l += (double)bias[tid];
-        const double g = use_gumbel ? gumbel_draw(seed, token_offset + (uint64_t)t, (uint64_t)tid) : 0.0;
-        zs[tid] = (l + g) / tau;
+        if (use_gumbel || noise_std > 0.0)
+            l = router_noise(l, use_gumbel, noise_std, seed, token_offset + (uint64_t)t, (uint64_t)tid);
+        zs[tid] = l / tau;
     }
     __syncthreads();
     if (tid >= 64) return;
@@ -266,9 +289,17 @@ router_finalize_kernel(const double* __restrict__ partial, int nsplit, int T, in
             if (lane + 64 * j == be) taken[j] = true;
         if (lane == 0) {
             ids[(int64_t)t * k + r] = be;
+            sel[r] = be;
             const double p = any_nan ? (double)NAN : exp(bz - m) / s;
             gates[(int64_t)t * k + r] = (float)p;
         }
+    }
+    if (gate_norm && lane == 0) {
+        // softmax over the chosen z (P4 §4.3), max-subtracted at the best, summed in slot order
+        const double top = zs[sel[0]];
+        double den = 0.0;
+        for (int r = 0; r < k; ++r) den += exp(zs[sel[r]] - top);
+        for (int r = 0; r < k; ++r) gates[(int64_t)t * k + r] = (float)(exp(zs[sel[r]] - top) / den);
     }
 }
 
@@ -309,7 +340,8 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t stream) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(router_finalize_kernel, dim3((unsigned)a.T), dim3(256), 0, stream, a.partial, p.splits,
-                       (int)a.T, a.E, a.k, a.bias, (double)a.tau, a.use_gumbel, a.seed, a.token_offset, a.ids,
+                       (int)a.T, a.E, a.k, a.bias, (double)a.tau, a.use_gumbel, (double)a.noise_std, a.gate_norm,
+                       a.seed, a.token_offset, a.ids,
                        a.gates, a.prob_rows, a.entropy_rows, a.z_rows);
     return hipGetLastError();
 }

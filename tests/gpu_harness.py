@@ -29,7 +29,8 @@ def tau32(tau):
 
 def abi_config(cfg, gemm_path=moe.GEMM_AUTO, seed=0, token_offset=0):
     return moe.config(cfg["T"], cfg["d"], cfg["d_ff"], cfg["E"], cfg["k"], cfg["act"], cfg["w"], tau=cfg["tau"],
-                      use_gumbel=cfg["gumbel"], seed=seed, token_offset=token_offset, gemm_path=gemm_path)
+                      use_gumbel=cfg["gumbel"], seed=seed, token_offset=token_offset, gemm_path=gemm_path,
+                      gate_norm=cfg.get("gate_norm", 0), noise_std=cfg.get("noise", 0.0))
 
 
 def run_forward(cfg, inp, gemm_path=moe.GEMM_AUTO, noise_seed=0, token_offset=0, device="cuda"):
@@ -44,7 +45,7 @@ def oracle_route(orc, cfg, inp, noise_seed=0, token_offset=0):
     bias = None if inp["bias"] is None else inp["bias"].cpu().numpy()
     return orc.route(moe_synth.to_bits(inp["x"]), moe_synth.to_bits(inp["Wg"]), cfg["k"], cfg["act"], bias=bias,
                      tau=tau32(cfg["tau"]), use_gumbel=cfg["gumbel"], seed=noise_seed, token_offset=token_offset,
-                     want_zp=True)
+                     want_zp=True, noise_std=tau32(cfg.get("noise", 0.0)), gate_norm=cfg.get("gate_norm", 0))
 
 
 def ambiguous_tokens(z, k):

@@ -63,7 +63,8 @@ def _cfg(**kw):
     base = dict(T=8, d=256, d_ff=512, E=8, k=2, act_dtype=moe.BF16, w_dtype=moe.BF16)
     base.update(kw)
     c = moe.config(base["T"], base["d"], base["d_ff"], base["E"], base["k"], base["act_dtype"], base["w_dtype"])
-    for key in ("tau", "use_gumbel", "gemm_path", "reserved", "capacity_factor", "capacity_policy"):
+    for key in ("tau", "use_gumbel", "gemm_path", "reserved", "capacity_factor", "capacity_policy", "gate_norm",
+                "noise_std"):
         if key in kw:
             setattr(c, key, kw[key])
     return c
@@ -77,6 +78,8 @@ BAD = [
     dict(capacity_factor=-1.0), dict(capacity_factor=float("nan")), dict(capacity_factor=float("inf")),
     dict(capacity_factor=-0.0 - 1e-30), dict(capacity_policy=2), dict(capacity_policy=-1),
     dict(capacity_factor=1.25, capacity_policy=7),
+    dict(gate_norm=2), dict(gate_norm=-1), dict(noise_std=-0.1), dict(noise_std=float("nan")),
+    dict(noise_std=float("inf")),
 ]
 
 
@@ -89,6 +92,10 @@ def test_invalid_config_rejected(lib, kw):
 
 def test_unsupported_pairings(lib):
     n = ctypes.c_size_t()
+    # renormalised gates are defined over the router's k choices, not over a capacity-limited dispatch
+    assert lib.moe_workspace_size(ctypes.byref(_cfg(gate_norm=1, capacity_factor=1.25)), ctypes.byref(n)) == \
+        binding.MOE_ERR_UNSUPPORTED
+    assert lib.moe_workspace_size(ctypes.byref(_cfg(gate_norm=1, noise_std=0.1)), ctypes.byref(n)) == 0
     for a, w in [(moe.F32, moe.BF16), (moe.BF16, moe.F32), (moe.F32, moe.INT4_G128)]:
         assert lib.moe_workspace_size(ctypes.byref(_cfg(act_dtype=a, w_dtype=w)), ctypes.byref(n)) == \
             binding.MOE_ERR_UNSUPPORTED

@@ -14,8 +14,9 @@ pytestmark = pytest.mark.gpu
 F32, BF16, INT4 = moe.F32, moe.BF16, moe.INT4_G128
 
 
-def case(T, d, d_ff, E, k=2, act=BF16, w=BF16, bias=False, tau=1.0, gumbel=False):
-    return dict(T=T, d=d, d_ff=d_ff, E=E, k=k, act=act, w=w, bias=bias, tau=tau, gumbel=gumbel, name="case")
+def case(T, d, d_ff, E, k=2, act=BF16, w=BF16, bias=False, tau=1.0, gumbel=False, gate_norm=0, noise=0.0):
+    return dict(T=T, d=d, d_ff=d_ff, E=E, k=k, act=act, w=w, bias=bias, tau=tau, gumbel=gumbel, gate_norm=gate_norm,
+                noise=noise, name="case")
 
 
 ROUTER_CASES = {
@@ -27,6 +28,12 @@ ROUTER_CASES = {
     "bf16-T31-d192-E5-k3": case(31, 192, 64, 5, k=3),
     "f32-T40-d64-E1-k1": case(40, 64, 64, 1, k=1, act=F32, w=F32),
     "bf16-T1-d8192-E128": case(1, 8192, 64, 128),
+    # variants: Gaussian logit noise, renormalised gates, both with Gumbel noise and a temperature
+    "bf16-T200-d512-E64-gaussian0.1": case(200, 512, 64, 64, noise=0.1),
+    "bf16-T77-d768-E16-gumbel-gaussian0.3-tau0.5-renorm": case(77, 768, 128, 16, tau=0.5, gumbel=True, noise=0.3,
+                                                                gate_norm=1),
+    "bf16-T50-d256-E256-k8-renorm": case(50, 256, 64, 256, k=8, gate_norm=1),
+    "f32-T40-d64-E1-k1-renorm": case(40, 64, 64, 1, k=1, act=F32, w=F32, gate_norm=1),
 }
 
 
@@ -117,6 +124,12 @@ FORWARD_CASES = {
                                           [moe.GEMM_STREAMING, moe.GEMM_TILED]),
     "int4-T40-d1024-dff1024-E64-k8": (case(40, 1024, 1024, 64, k=8, w=INT4), [moe.GEMM_TILED]),
     "f32-T130-d192-dff320-E5-k3": (case(130, 192, 320, 5, k=3, act=F32, w=F32, bias=True), [moe.GEMM_AUTO]),
+    # router variants through the whole layer
+    "bf16-T300-d512-dff1024-E8-renorm-gaussian0.1": (case(300, 512, 1024, 8, bias=True, gate_norm=1, noise=0.1),
+                                                     [moe.GEMM_STREAMING, moe.GEMM_TILED]),
+    "int4-T12-d512-dff1024-E8-renorm-gumbel": (case(12, 512, 1024, 8, w=INT4, tau=0.5, gumbel=True, gate_norm=1),
+                                               [moe.GEMM_AUTO]),
+    "f32-T64-d128-dff256-E6-k3-renorm": (case(64, 128, 256, 6, k=3, act=F32, w=F32, gate_norm=1), [moe.GEMM_AUTO]),
 }
 FORWARD_PARAMS = [(n, p) for n, (_, paths) in FORWARD_CASES.items() for p in paths]
 
