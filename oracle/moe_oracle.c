@@ -41,6 +41,10 @@
  *      W1_e is d_ff x d, W2_e is d x d_ff (out x in, input dim contiguous).
  *      INT4 experts: w[n,c] = q[n,c] * s[n, c/128] exactly, q in [-8,7]
  *      (symmetric group-128 codes with bf16 scales).                 P1 §5.4; P2 §2.3 (dequantize step)
+ *   6'. expert activations (expert_act): 1 = SiLU, o = W2_e * SiLU(W1_e * x)
+ *      with SiLU(a) = a / (1 + e^-a); 2 = SwiGLU, o = W2_e * (SiLU(G x) * (U x))
+ *      where W1_e holds 2 d_ff rows: the gate row of hidden unit n is
+ *      32 (n / 16) + n % 16 and its up row is 16 rows further.        P1 §3.3, §4.2 (SwiGLU experts)
  *   7. y[t] = sum_j p[ids[j]] * o_{ids[j]}                           P2 §2.2 step 4; P5 §3.2 "合并"
  * Dispatch bookkeeping (per-expert counts, exclusive offsets, a stable
  * counting sort of the (token, slot) assignments) follows P3 §4.2's per-expert
@@ -149,6 +153,12 @@ double oracle_normal(uint64_t seed, uint64_t token, uint64_t expert)
     double u1 = ((double)(r[2] >> 11) + 0.5) * (1.0 / 9007199254740992.0);
     double u2 = ((double)(r[3] >> 11) + 0.5) * (1.0 / 9007199254740992.0);
     return sqrt(-2.0 * log(u1)) * cos(two_pi * u2);
+}
+
+/* SiLU (swish with beta = 1): a * sigmoid(a) = a / (1 + e^-a). */
+double oracle_silu(double a)
+{
+    return a / (1.0 + exp(-a));
 }
 
 /* GeLU in its exact form h * Phi(h). */
@@ -475,24 +485,42 @@ int oracle_router_stats(int64_t T, int32_t E, int32_t k, const int32_t *ids, con
 /* --------------------------------------------------------------- expert FFN */
 
 /*
- * o[0..d) = W2_e * GeLU(W1_e * xr) for one token row xr (binary64, length d).
- * W1e is d_ff x d, W2e is d x d_ff, both in w_dtype; S1e/S2e are the bf16 group
- * scales for INT4 (ignored otherwise).  Returns 0, or -1 on a bad argument.
+ * o[0..d) = W2_e * act(W1_e * xr) for one token row xr (binary64, length d).
+ * act 0 = GeLU, 1 = SiLU: W1e is d_ff x d.  act 2 = SwiGLU: W1e is 2 d_ff x d
+ * with the gate/up rows of step 6' and a[n] = SiLU(gate . x) * (up . x).
+ * W2e is d x d_ff; all in w_dtype; S1e/S2e are the bf16 group scales for INT4
+ * (ignored otherwise).  Returns 0, or -1 on a bad argument.
  */
-int oracle_expert_ffn(int64_t d, int64_t d_ff, int32_t w_dtype,
+int oracle_expert_ffn(int64_t d, int64_t d_ff, int32_t w_dtype, int32_t act,
                       const double *xr, const void *W1e, const void *S1e,
                       const void *W2e, const void *S2e, double *o)
 {
     if (w_dtype == ORACLE_INT4_G128 && (d % 128 != 0 || d_ff % 128 != 0 || !S1e || !S2e))
         return -1;
+    if (act < 0 || act > 2 || (act == 2 && d_ff % 16 != 0))
+        return -1;
     double *a = (double *)malloc(sizeof(double) * (size_t)d_ff);
     if (!a)
         return -1;
     for (int64_t n = 0; n < d_ff; ++n) {
+        if (act == 2) {
+            /* SwiGLU: the unit's gate and up rows of the 2 d_ff-row W1 */
+            int64_t rg = 32 * (n / 16) + n % 16, ru = rg + 16;
+            double g = 0.0, u = 0.0;
+            for (int64_t i = 0; i < d; ++i)
+                g += load_w(W1e, S1e, w_dtype, d, rg, i) * xr[i];
+            for (int64_t i = 0; i < d; ++i)
+                u += load_w(W1e, S1e, w_dtype, d, ru, i) * xr[i];
+            a[n] = oracle_silu(g) * u;
+            continue;
+        }
         double h = 0.0;
         for (int64_t i = 0; i < d; ++i)
             h += load_w(W1e, S1e, w_dtype, d, n, i) * xr[i];
-        a[n] = oracle_gelu(h);
+        if (act == 1)
+            a[n] = oracle_silu(h);
+        else
+            a[n] = oracle_gelu(h);
     }
     for (int64_t c = 0; c < d; ++c) {
         double acc = 0.0;
@@ -511,7 +539,7 @@ int oracle_expert_ffn(int64_t d, int64_t d_ff, int32_t w_dtype,
  * Returns 0, or -1 on a bad argument or a missing expert.
  */
 int oracle_forward_tokens(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k,
-                          int32_t act_dtype, int32_t w_dtype, const void *x,
+                          int32_t act_dtype, int32_t w_dtype, int32_t act, const void *x,
                           const int32_t *ids, const double *gate_p,
                           const void *const *W1, const void *const *S1,
                           const void *const *W2, const void *const *S2,
@@ -542,7 +570,7 @@ int oracle_forward_tokens(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t
                 rc = -1;
                 break;
             }
-            rc = oracle_expert_ffn(d, d_ff, w_dtype, xr, W1[e], S1 ? S1[e] : NULL,
+            rc = oracle_expert_ffn(d, d_ff, w_dtype, act, xr, W1[e], S1 ? S1[e] : NULL,
                                    W2[e], S2 ? S2[e] : NULL, o);
             if (rc != 0)
                 break;

@@ -51,6 +51,8 @@ class Oracle:
         lib.oracle_gumbel.restype = ctypes.c_double
         lib.oracle_normal.argtypes = [_U64, _U64, _U64]
         lib.oracle_normal.restype = ctypes.c_double
+        lib.oracle_silu.argtypes = [ctypes.c_double]
+        lib.oracle_silu.restype = ctypes.c_double
         lib.oracle_gelu.argtypes = [ctypes.c_double]
         lib.oracle_gelu.restype = ctypes.c_double
         lib.oracle_route.argtypes = [_I64, _I64, _I32, _I32, _I32, _P, _P, _P,
@@ -67,9 +69,9 @@ class Oracle:
         lib.oracle_capacity.restype = ctypes.c_int64
         lib.oracle_capacity_dispatch.argtypes = [_I64, _I32, _I32, _I64, _I32, _P, _P, _P, _P, _P, _P]
         lib.oracle_capacity_dispatch.restype = ctypes.c_int
-        lib.oracle_expert_ffn.argtypes = [_I64, _I64, _I32, _P, _P, _P, _P, _P, _P]
+        lib.oracle_expert_ffn.argtypes = [_I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P]
         lib.oracle_expert_ffn.restype = ctypes.c_int
-        lib.oracle_forward_tokens.argtypes = [_I64, _I64, _I64, _I32, _I32, _I32, _I32, _P,
+        lib.oracle_forward_tokens.argtypes = [_I64, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _P,
                                               _P, _P, _P, _P, _P, _P, _I64, _P, _P]
         lib.oracle_forward_tokens.restype = ctypes.c_int
         self.lib = lib
@@ -90,6 +92,9 @@ class Oracle:
 
     def normal(self, seed, token, expert):
         return self.lib.oracle_normal(seed, token, expert)
+
+    def silu(self, a):
+        return self.lib.oracle_silu(float(a))
 
     def gelu(self, h):
         return self.lib.oracle_gelu(float(h))
@@ -176,17 +181,18 @@ class Oracle:
                     lb_prob=scalars[2], fraction_std=scalars[3], lb_product=scalars[4], scalars=scalars)
 
     # -- experts ------------------------------------------------------------------
-    def expert_ffn(self, xr, W1e, W2e, w_dtype, S1e=None, S2e=None):
-        """o = W2e . GeLU(W1e . xr) in binary64 for one float64 row xr."""
+    def expert_ffn(self, xr, W1e, W2e, w_dtype, S1e=None, S2e=None, act=0):
+        """o = W2e . act(W1e . xr) in binary64 for one float64 row xr (act 0 GeLU, 1 SiLU,
+        2 SwiGLU with W1e's 2 d_ff rows interleaved in blocks of 16: gate, then up)."""
         xr = np.ascontiguousarray(xr, dtype=np.float64)
         d = xr.shape[0]
-        d_ff = W1e.shape[0]
+        d_ff = W1e.shape[0] // (2 if act == 2 else 1)
         W1e = np.ascontiguousarray(W1e)
         W2e = np.ascontiguousarray(W2e)
         S1e = None if S1e is None else np.ascontiguousarray(S1e)
         S2e = None if S2e is None else np.ascontiguousarray(S2e)
         o = np.zeros(d, dtype=np.float64)
-        rc = self.lib.oracle_expert_ffn(d, d_ff, w_dtype, xr.ctypes.data, W1e.ctypes.data,
+        rc = self.lib.oracle_expert_ffn(d, d_ff, w_dtype, act, xr.ctypes.data, W1e.ctypes.data,
                                         None if S1e is None else S1e.ctypes.data,
                                         W2e.ctypes.data,
                                         None if S2e is None else S2e.ctypes.data, o.ctypes.data)
@@ -195,7 +201,7 @@ class Oracle:
         return o
 
     def forward_tokens(self, x, ids, gate_p, W1, W2, act_dtype, w_dtype, d_ff, tokens,
-                       S1=None, S2=None):
+                       S1=None, S2=None, act=0):
         """y rows (float64) for the listed tokens.  W1/W2/S1/S2 map expert -> numpy
         array (a list of length E, entries may be None for untouched experts)."""
         x = np.ascontiguousarray(x)
@@ -221,7 +227,7 @@ class Oracle:
 
         p1, p2, s1, s2 = ptrs(W1), ptrs(W2), ptrs(S1), ptrs(S2)
         y = np.zeros((len(tokens), d), dtype=np.float64)
-        rc = self.lib.oracle_forward_tokens(T, d, d_ff, E, k, act_dtype, w_dtype, x.ctypes.data,
+        rc = self.lib.oracle_forward_tokens(T, d, d_ff, E, k, act_dtype, w_dtype, act, x.ctypes.data,
                                             ids.ctypes.data, gate_p.ctypes.data, p1, s1, p2, s2,
                                             len(tokens), tokens.ctypes.data, y.ctypes.data)
         if rc != 0:
@@ -229,7 +235,7 @@ class Oracle:
         return y
 
     def forward(self, x, Wg, W1, W2, k, act_dtype, w_dtype, bias=None, tau=1.0,
-                use_gumbel=False, seed=0, token_offset=0, S1=None, S2=None, tokens=None):
+                use_gumbel=False, seed=0, token_offset=0, S1=None, S2=None, tokens=None, act=0):
         """Whole layer: routing for every token, dispatch arrays, and y for the
         listed tokens (all tokens by default).  W1/W2 are [E, N, K] arrays or
         per-expert lists."""
@@ -240,11 +246,11 @@ class Oracle:
         T = x.shape[0]
         if tokens is None:
             tokens = np.arange(T)
-        d_ff = W1[0].shape[0] if not isinstance(W1, np.ndarray) else W1.shape[1]
+        d_ff = (W1[0].shape[0] if not isinstance(W1, np.ndarray) else W1.shape[1]) // (2 if act == 2 else 1)
         as_list = (lambda a: None if a is None else [a[e] for e in range(E)])
         r["y"] = self.forward_tokens(x, r["ids"], r["gate_p"], as_list(W1), as_list(W2),
                                      act_dtype, w_dtype, d_ff, tokens,
-                                     S1=as_list(S1), S2=as_list(S2))
+                                     S1=as_list(S1), S2=as_list(S2), act=act)
         r["tokens"] = np.asarray(tokens)
         return r
 

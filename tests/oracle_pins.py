@@ -404,6 +404,75 @@ def pin_single_expert_equals_dense(orc):
         assert np.max(np.abs(out["y"] - want)) <= 1e-13 * np.max(np.abs(want))
 
 
+def _swiglu_split(W1):
+    """Gate and up matrices of a SwiGLU W1 whose 2 d_ff rows alternate in
+    blocks of 16 (16 gate rows, then the same 16 units' up rows)."""
+    rows, d = W1.shape
+    blocks = W1.reshape(rows // 32, 2, 16, d)
+    return blocks[:, 0].reshape(rows // 2, d), blocks[:, 1].reshape(rows // 2, d)
+
+
+def pin_silu_and_swiglu_experts(orc):
+    """P1 §3.3/§4.2 give the experts SiLU-gated (SwiGLU) FFNs.  SiLU: 0 at 0,
+    silu(x) - silu(-x) = x, and x * scipy's expit(x).  SwiGLU with 0/1
+    selection matrices: unit n's gate row picks x[a(n)], its up row x[b(n)],
+    so o[c] = silu(x[a]) * x[b] by index arithmetic (two 16-unit blocks, so
+    the block interleave is exercised).  Single-expert layers equal numpy/scipy
+    dense FFNs: W2 silu(W1 x) and W2 (silu(G x) * U x) with G and U unpacked by
+    a reshape, in fp32, bf16 and INT4 storage."""
+    from scipy import special
+    xs = np.array([0.0, 1e-3, 0.5, -0.5, 2.0, -3.0, 20.0, -40.0, 700.0, -700.0])
+    assert orc.silu(0.0) == 0.0
+    for v in xs:
+        assert abs(orc.silu(v) - orc.silu(-v) - v) <= 1e-15 * max(1.0, abs(v))
+        assert abs(orc.silu(v) - v * special.expit(v)) <= 1e-15 * max(1.0, abs(v))
+
+    d, d_ff = 8, 32
+    r = _rng(23)
+    a_src, b_src = r.integers(0, d, d_ff), r.integers(0, d, d_ff)
+    W1 = np.zeros((2 * d_ff, d), np.float32)
+    for n in range(d_ff):
+        rg = 32 * (n // 16) + n % 16
+        W1[rg, a_src[n]] = 1.0
+        W1[rg + 16, b_src[n]] = 1.0
+    pick = r.permutation(d_ff)[:d]
+    W2 = np.zeros((d, d_ff), np.float32)
+    W2[np.arange(d), pick] = 1.0
+    x = r.standard_normal(d)
+    o = orc.expert_ffn(x, W1, W2, F32, act=2)
+    want = x[a_src[pick]] * special.expit(x[a_src[pick]]) * x[b_src[pick]]
+    assert np.max(np.abs(o - want)) <= 1e-15
+
+    for dtype in (F32, BF16):
+        (x, Wg, W1, W2), (xf, _, W1f, W2f) = _tiny(24, T=9, d=32, d_ff=64, E=1, dtype=dtype)
+        out = orc.forward(x, Wg, W1, W2, 1, dtype, dtype, act=1)
+        h = xf @ W1f[0].T
+        want = (h * special.expit(h)) @ W2f[0].T
+        assert np.max(np.abs(out["y"] - want)) <= 1e-13 * np.max(np.abs(want))
+        (x, Wg, W1, W2), (xf, _, W1f, W2f) = _tiny(25, T=9, d=32, d_ff=128, E=1, dtype=dtype)
+        W2h, W2hf = W2[:, :, :64], W2f[:, :, :64]     # d x d_ff with d_ff = 64 hidden units
+        out = orc.forward(x, Wg, W1, np.ascontiguousarray(W2h), 1, dtype, dtype, act=2)
+        G, U = _swiglu_split(W1f[0])
+        g, u = xf @ G.T, xf @ U.T
+        want = (g * special.expit(g) * u) @ W2hf[0].T
+        assert np.max(np.abs(out["y"] - want)) <= 1e-13 * np.max(np.abs(want))
+
+    # INT4 SwiGLU expert against the dense formula on the decoded q * s weights
+    r = _rng(26)
+    d, d_ff = 128, 128
+    q1 = r.integers(-8, 8, (2 * d_ff, d))
+    q2 = r.integers(-8, 8, (d, d_ff))
+    s1 = _bf16(r.uniform(0.01, 0.05, (2 * d_ff, d // 128)))
+    s2 = _bf16(r.uniform(0.01, 0.05, (d, d_ff // 128)))
+    c1, c2 = npref.pack_int4(q1), npref.pack_int4(q2)
+    x = r.standard_normal(d)
+    o = orc.expert_ffn(x, c1, c2, INT4_G128, S1e=s1, S2e=s2, act=2)
+    G, U = _swiglu_split(npref.dequant_int4(c1, s1))
+    g, u = G @ x, U @ x
+    want = npref.dequant_int4(c2, s2) @ (g * special.expit(g) * u)
+    assert np.max(np.abs(o - want)) <= 1e-13 * np.max(np.abs(want))
+
+
 def pin_int4_decode(orc):
     """All sixteen signed codes decode (two's complement nibbles, even column in
     the low nibble), each 128-column group takes its own scale, and an INT4

@@ -33,6 +33,11 @@ MUTANTS = [
     ("W1 reads x reversed", "h += load_w(W1e, S1e, w_dtype, d, n, i) * xr[i];",
      "h += load_w(W1e, S1e, w_dtype, d, n, i) * xr[d - 1 - i];"),
     ("GeLU skipped", "a[n] = oracle_gelu(h);", "a[n] = h;"),
+    ("SwiGLU gate and up swapped", "a[n] = oracle_silu(g) * u;", "a[n] = oracle_silu(u) * g;"),
+    ("SwiGLU interleaved in blocks of 8", "int64_t rg = 32 * (n / 16) + n % 16, ru = rg + 16;",
+     "int64_t rg = 16 * (n / 8) + n % 8, ru = rg + 8;"),
+    ("SiLU sign", "return a / (1.0 + exp(-a));", "return a / (1.0 + exp(a));"),
+    ("SiLU expert computes GeLU", "a[n] = oracle_silu(h);", "a[n] = oracle_gelu(h);"),
     ("W2 reads hidden reversed", "acc += load_w(W2e, S2e, w_dtype, d_ff, c, n) * a[n];",
      "acc += load_w(W2e, S2e, w_dtype, d_ff, c, n) * a[d_ff - 1 - n];"),
     ("int4 nibble order", "int nib = (c % 2 == 0) ? (byte & 0x0F) : (byte >> 4);",
