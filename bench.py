@@ -2,6 +2,7 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                 [--capacity-factor CF --capacity-policy drop|reroute] [--gate-norm] [--noise-std SIGMA]
+                [--expert-act gelu|silu|swiglu]
 
 One step = the whole layer (router, dispatch, W1 GEMM + GeLU, W2 GEMM,
 combine) over one batch of seeded synthetic input already resident in HBM.
@@ -42,6 +43,8 @@ def parse():
     ap.add_argument("--capacity-policy", choices=["drop", "reroute"], default="drop")
     ap.add_argument("--gate-norm", action="store_true", help="gates renormalised over the k chosen experts")
     ap.add_argument("--noise-std", type=float, default=0.0, help="sigma of Gaussian router-logit noise")
+    ap.add_argument("--expert-act", choices=["gelu", "silu", "swiglu"], default="gelu",
+                    help="expert activation (swiglu: W1 holds 2 d_ff gate/up rows)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy first (reference kernel for HBM byte counters)")
     return ap.parse_args()
@@ -85,14 +88,17 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = moe_synth.workload(args.workload)
+    act_code = {"gelu": moe.ACT_GELU, "silu": moe.ACT_SILU, "swiglu": moe.ACT_SWIGLU}[args.expert_act]
+    cfg["ffn"] = act_code
     T, d, d_ff, E, k = cfg["T"], cfg["d"], cfg["d_ff"], cfg["E"], cfg["k"]
+    n1 = 2 * d_ff if act_code == moe.ACT_SWIGLU else d_ff  # W1 rows
     print(f"[bench] generating {args.workload} on {dev}", file=sys.stderr, flush=True)
     inp = moe_synth.generate(cfg, device=dev, seed=0)
     torch.cuda.synchronize()
     policy = moe.CAPACITY_REROUTE if args.capacity_policy == "reroute" else moe.CAPACITY_DROP
     c = moe.config(T, d, d_ff, E, k, cfg["act"], cfg["w"], tau=cfg["tau"], use_gumbel=cfg["gumbel"], seed=0,
                    capacity_factor=args.capacity_factor, capacity_policy=policy, gate_norm=int(args.gate_norm),
-                   noise_std=args.noise_std)
+                   noise_std=args.noise_std, expert_act=act_code)
     layer = moe.MoELayerForward(c, device=dev)
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -119,7 +125,8 @@ def main():
     active = int((counts > 0).sum())
     wbits = {moe.F32: 32, moe.BF16: 16, moe.INT4_G128: 4}[cfg["w"]]
     abytes = 4 if cfg["act"] == moe.F32 else 2
-    w_bytes = d * d_ff * wbits // 8 + (d * d_ff // 128 * 2 if cfg["w"] == moe.INT4_G128 else 0)
+    w_bytes = d * d_ff * wbits // 8 + (d * d_ff // 128 * 2 if cfg["w"] == moe.INT4_G128 else 0)  # one W2
+    w1_bytes = w_bytes * n1 // d_ff
     Tk = kept  # dispatched rows (T k without a capacity)
     hbytes = 4 if cfg["w"] == moe.F32 else 2
 
@@ -154,8 +161,8 @@ def main():
         path = "streaming"  # the automatic choice of the library
     else:
         path = "tiled"
-    gemm_bytes = active * w_bytes + Tk * d * abytes + Tk * d_ff * hbytes
-    gemm_flops = 2.0 * Tk * d * d_ff
+    gemm_bytes = active * w1_bytes + Tk * d * abytes + Tk * d_ff * hbytes
+    gemm_flops = 2.0 * Tk * d * n1
     kernel_name = f"moe_grouped_gemm_w1_{path}"
     # the binding roof: arithmetic intensity against the ridge point of the compute unit the path uses
     # (bf16 MFMA for bf16/INT4 experts, the fp32 vector ALUs for fp32 experts)
@@ -173,7 +180,7 @@ def main():
     roof.update(kernel=kernel_name, avg_launch_ms=round(gemm_ms, 4),
                 algorithmic_bytes=gemm_bytes, algorithmic_flops=gemm_flops)
 
-    step_bytes = (T * d * abytes + d * E * abytes + active * 2 * w_bytes + T * d * abytes + T * k * 8 + E * 4)
+    step_bytes = (T * d * abytes + d * E * abytes + active * (w1_bytes + w_bytes) + T * d * abytes + T * k * 8 + E * 4)
     out = {
         "metric": "MoE-layer tokens/s",
         "value": round(tokens_per_s, 1),
@@ -191,9 +198,9 @@ def main():
                    "router_bias": bool(cfg["bias"]), "tau": cfg["tau"], "gumbel": bool(cfg["gumbel"]),
                    "capacity_factor": args.capacity_factor,
                    "capacity_policy": args.capacity_policy if args.capacity_factor > 0 else None,
-                   "gate_norm": int(args.gate_norm), "noise_std": args.noise_std},
+                   "gate_norm": int(args.gate_norm), "noise_std": args.noise_std, "expert_act": args.expert_act},
         "layer_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "layer_mfma_frac": round(2 * gemm_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "layer_mfma_frac": round((gemm_flops + 2.0 * Tk * d * d_ff) / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "active_experts": active,
         "counts_var": float(np.var(counts)),
         "assignments_kept": kept,
@@ -262,7 +269,7 @@ def cpu_baseline(cfg, inp, layer, args):
     reps = 0
     while True:  # repeat the sample until ~10 s of oracle work has been timed
         orc.forward_tokens(xb, ref["ids"], ref["gate_p"], W1, W2, cfg["act"], cfg["w"], cfg["d_ff"], tokens,
-                           S1=S1, S2=S2)
+                           S1=S1, S2=S2, act=cfg.get("ffn", 0))
         reps += 1
         if time.perf_counter() - t0 >= 10.0:
             break

@@ -101,7 +101,17 @@ typedef struct moe_config {
     float noise_std;       /* sigma >= 0 (finite) of Gaussian router noise (P5 §3.3): z = (l + g + sigma n) / tau,
                               n standard normal by Box-Muller from words 2 and 3 of the (seed, token, expert)
                               Philox block; 0: none */
+    int32_t expert_act;    /* moe_expert_act */
 } moe_config;
+
+/* The experts' hidden activation (P3 §3.2 GELU; P1 §3.3 and §4.2 SiLU-gated units). */
+typedef enum moe_expert_act {
+    MOE_ACT_GELU = 0,   /* o = W2 GeLU(W1 x), GeLU(h) = h Phi(h); W1 has d_ff rows */
+    MOE_ACT_SILU = 1,   /* o = W2 SiLU(W1 x), SiLU(a) = a / (1 + e^-a); W1 has d_ff rows */
+    MOE_ACT_SWIGLU = 2  /* o = W2 (SiLU(G x) * U x): W1 has 2 d_ff rows interleaved in blocks of 16, rows
+                           32 b .. 32 b + 15 the gate rows of hidden units 16 b .. 16 b + 15 and the next 16 rows
+                           their up rows (INT4 scales follow the same rows) */
+} moe_expert_act;
 
 /* What happens to an assignment whose expert is full (P5 §3.2; P2 §3.2).  The
  * T k assignments queue in row-major (token, slot) order; each keeps its
@@ -128,7 +138,8 @@ moe_status moe_router_workspace_size(const moe_config *cfg, size_t *bytes);
  *   x            [T][d]   act_dtype                      (device, in)
  *   Wg           [d][E]   act_dtype                      (device, in)
  *   router_bias  [E]      float, or NULL for none        (device, in)
- *   W1, W2       expert 0's matrix; expert e starts e * W*_expert_stride bytes later
+ *   W1, W2       expert 0's matrix ([d_ff][d], or [2 d_ff][d] for SwiGLU; [d][d_ff]); expert e starts
+ *                e * W*_expert_stride bytes later
  *                (stride >= the matrix's bytes, multiple of 16)   (device, in)
  *   W1_scales, W2_scales  bf16 [E][N][K/128] for INT4 weights, NULL otherwise (device, in)
  *   y            [T][d]   act_dtype                      (device, out)
@@ -202,7 +213,8 @@ moe_status moe_permute(const moe_config *cfg, const int32_t *expert_ids, int32_t
  * One grouped expert GEMM over the dispatch order (P3 §3.2; P2 §2.3; P2 §3.3
  * fused activation).  For each expert e and each position s in
  * [offsets[e], offsets[e+1]):
- *   which == 1:  out[s][n] = GeLU( sum_c W1_e[n][c] * A[row(s)][c] ),  n < d_ff,
+ *   which == 1:  out[s][n] = act( sum_c W1_e[n][c] * A[row(s)][c] ),  n < d_ff, act per
+ *                expert_act (SwiGLU: SiLU of the unit's gate row times its up row, W1_e of 2 d_ff rows),
  *                row(s) = a_rows[s] (A = x, [T][d]); out = H, [T*k][d_ff],
  *                bf16 for BF16/INT4 weights, float for F32 weights.
  *   which == 2:  out[s][c] = sum_n W2_e[c][n] * A[s][n],  c < d;

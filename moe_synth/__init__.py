@@ -122,13 +122,16 @@ def generate(cfg, device="cpu", seed=0):
     """All inputs of a workload as torch tensors on `device`.
 
     Returns dict(x, Wg, bias (or None), W1, W2, S1, S2 (INT4 scales or None)).
-    W1 is [E, d_ff, d] (INT4: uint8 [E, d_ff, d/2]); W2 is [E, d, d_ff].
+    W1 is [E, d_ff, d] (INT4: uint8 [E, d_ff, d/2]); W2 is [E, d, d_ff].  With
+    cfg["ffn"] == 2 (SwiGLU experts) W1 has 2 d_ff rows, drawn like any other
+    (the gate/up interleave is a storage order, not a distribution).
     """
     T, d, d_ff, E = cfg["T"], cfg["d"], cfg["d_ff"], cfg["E"]
     wdt = cfg["w"]
     out = generate_router(cfg, device, seed)
     out.update(S1=None, S2=None)
-    for name, N, K in (("W1", d_ff, d), ("W2", d, d_ff)):
+    n1 = 2 * d_ff if cfg.get("ffn", 0) == 2 else d_ff
+    for name, N, K in (("W1", n1, d), ("W2", d, d_ff)):
         std = 1.0 / math.sqrt(K)
         if wdt == INT4_G128:
             codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=device)

@@ -15,6 +15,7 @@ MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMA
 F32, BF16, INT4_G128 = 0, 1, 2
 GEMM_AUTO, GEMM_STREAMING, GEMM_TILED = 0, 1, 2
 CAPACITY_DROP, CAPACITY_REROUTE = 0, 1
+ACT_GELU, ACT_SILU, ACT_SWIGLU = 0, 1, 2
 
 EXPORTS = ("moe_workspace_size", "moe_router_workspace_size", "moe_forward", "moe_router", "moe_permute",
            "moe_grouped_gemm", "moe_combine", "moe_router_stats_workspace_size", "moe_router_stats",
@@ -40,6 +41,7 @@ class MoeConfig(ctypes.Structure):
         ("capacity_policy", ctypes.c_int32),
         ("gate_norm", ctypes.c_int32),
         ("noise_std", ctypes.c_float),
+        ("expert_act", ctypes.c_int32),
     ]
 
 
@@ -89,9 +91,10 @@ def status_string(status):
 
 
 def config(T, d, d_ff, E, k, act_dtype, w_dtype, tau=1.0, use_gumbel=False, seed=0, token_offset=0,
-           gemm_path=GEMM_AUTO, capacity_factor=0.0, capacity_policy=CAPACITY_DROP, gate_norm=0, noise_std=0.0):
+           gemm_path=GEMM_AUTO, capacity_factor=0.0, capacity_policy=CAPACITY_DROP, gate_norm=0, noise_std=0.0,
+           expert_act=ACT_GELU):
     return MoeConfig(T, d, d_ff, E, k, act_dtype, w_dtype, tau, int(bool(use_gumbel)), seed, token_offset,
-                     gemm_path, 0, capacity_factor, capacity_policy, int(gate_norm), noise_std)
+                     gemm_path, 0, capacity_factor, capacity_policy, int(gate_norm), noise_std, expert_act)
 
 
 def _ptr(t):

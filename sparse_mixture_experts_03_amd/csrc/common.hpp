@@ -71,6 +71,25 @@ __device__ __forceinline__ float gelu_erf(float h) {
     return 0.5f * h * (1.0f + erff(h * 0.70710678118654752440f));
 }
 
+// SiLU (swish): a * sigmoid(a) = a / (1 + 2^(-a log2 e)), with the hardware
+// base-2 exponential and reciprocal (each about 1 ulp; the result is rounded
+// to bf16 or enters an fp32 product).  Few live temporaries: it sits in the
+// epilogue of kernels whose main loops use nearly every register.
+__device__ __forceinline__ float silu_f(float a) {
+    return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * -1.4426950408889634f));
+}
+
+// Expert activation codes (match moe_expert_act in include/moe.h).  SwiGLU's
+// first GEMM has 2 d_ff weight rows interleaved in blocks of 16: rows
+// [32 b, 32 b + 16) are the gate rows of hidden units [16 b, 16 b + 16) and
+// the next 16 rows their up rows, so a 32-row block of outputs yields 16 units.
+constexpr int kActGelu = 0;
+constexpr int kActSilu = 1;
+constexpr int kActSwiglu = 2;
+
+// The elementwise activation of GEMM1 (GeLU or SiLU).
+__device__ __forceinline__ float act_f(float v, int act) { return act == kActSilu ? silu_f(v) : gelu_erf(v); }
+
 // The m-tiles of a grouped GEMM whose experts hold offsets[e+1]-offsets[e]
 // rows, cut into tiles of BM rows and numbered expert-major.  Built by one
 // whole wavefront (every lane gets the same total); E <= 256, 4 experts per

@@ -18,7 +18,7 @@ template <int WHICH>
 __global__ void __launch_bounds__(256)
 gemm_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__ a_rows,
                 const int32_t* __restrict__ offsets, int E, const float* __restrict__ W, int64_t W_stride_elems,
-                float* __restrict__ out, int N, int K, int ntiles_n) {
+                float* __restrict__ out, int N, int K, int ntiles_n, int act) {
     __shared__ float As[kFK][kFB + 4];
     __shared__ float Bs[kFK][kFB + 4];
     const int tid = threadIdx.x;
@@ -70,16 +70,37 @@ gemm_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__ a_rows,
         }
         __syncthreads();
     }
+    if (WHICH == 1 && act == kActSwiglu) {
+        // weight rows 4 tx + j: tx % 8 < 4 holds gate rows of a 32-row block, tx + 4 the matching up rows
+        float up[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) up[i][j] = __shfl_xor(acc[i][j], 4, 64);
+        if ((tx & 4) == 0) {
+            const int Nh = N >> 1;
+            const int unit = (n0 >> 1) + 16 * (tx >> 3) + 4 * (tx & 3);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = ty * 4 + i;
+                if (m >= rows) continue;
+                const float4 v = make_float4(silu_f(acc[i][0]) * up[i][0], silu_f(acc[i][1]) * up[i][1],
+                                             silu_f(acc[i][2]) * up[i][2], silu_f(acc[i][3]) * up[i][3]);
+                *reinterpret_cast<float4*>(out + (int64_t)(p0 + m) * Nh + unit) = v;
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int m = ty * 4 + i;
         if (m >= rows) continue;
         float4 v = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
         if (WHICH == 1) {
-            v.x = gelu_erf(v.x);
-            v.y = gelu_erf(v.y);
-            v.z = gelu_erf(v.z);
-            v.w = gelu_erf(v.w);
+            v.x = act_f(v.x, act);
+            v.y = act_f(v.y, act);
+            v.z = act_f(v.z, act);
+            v.w = act_f(v.w, act);
         }
         *reinterpret_cast<float4*>(out + (int64_t)(p0 + m) * N + n0 + tx * 4) = v;
     }
@@ -100,10 +121,10 @@ hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t stream) {
     float* out = static_cast<float*>(a.out);
     if (a.which == 1)
         hipLaunchKernelGGL(gemm_f32_kernel<1>, grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
-                           a.W_stride / 4, out, (int)a.N, (int)a.K, ntiles_n);
+                           a.W_stride / 4, out, (int)a.N, (int)a.K, ntiles_n, a.act);
     else
         hipLaunchKernelGGL(gemm_f32_kernel<2>, grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
-                           a.W_stride / 4, out, (int)a.N, (int)a.K, ntiles_n);
+                           a.W_stride / 4, out, (int)a.N, (int)a.K, ntiles_n, 0);
     return hipGetLastError();
 }
 

@@ -84,19 +84,32 @@ __device__ __forceinline__ bf16x8 int4x8_to_bf16_offset136(uint32_t w) {
 }
 
 template <int WHICH>
-__device__ __forceinline__ void store_tile(void* out, int64_t N, int p0, int rows, int n0, f32x4 v, int lane) {
+__device__ __forceinline__ void store_tile(void* out, int64_t N, int p0, int rows, int n0, f32x4 v, int lane,
+                                           int act) {
     const int m = lane & 15;
     if (m >= rows) return;
     const int n = n0 + 4 * (lane >> 4);
     if constexpr (WHICH == 1) {
         uint2 packed;
-        packed.x = float_to_bf16_bits(gelu_erf(v[0])) | (float_to_bf16_bits(gelu_erf(v[1])) << 16);
-        packed.y = float_to_bf16_bits(gelu_erf(v[2])) | (float_to_bf16_bits(gelu_erf(v[3])) << 16);
+        packed.x = float_to_bf16_bits(act_f(v[0], act)) | (float_to_bf16_bits(act_f(v[1], act)) << 16);
+        packed.y = float_to_bf16_bits(act_f(v[2], act)) | (float_to_bf16_bits(act_f(v[3], act)) << 16);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (int64_t)(p0 + m) * N + n) = packed;
     } else {
         *reinterpret_cast<float4*>(static_cast<float*>(out) + (int64_t)(p0 + m) * N + n) =
             make_float4(v[0], v[1], v[2], v[3]);
     }
+}
+
+// SwiGLU: a gate block g and its up block u (16 weight rows each) give 16
+// hidden units starting at u0 of H (row stride Nh).
+__device__ __forceinline__ void store_swiglu(void* out, int64_t Nh, int p0, int rows, int u0, f32x4 g, f32x4 u,
+                                             int lane) {
+    const int m = lane & 15;
+    if (m >= rows) return;
+    uint2 packed;
+    packed.x = float_to_bf16_bits(silu_f(g[0]) * u[0]) | (float_to_bf16_bits(silu_f(g[1]) * u[1]) << 16);
+    packed.y = float_to_bf16_bits(silu_f(g[2]) * u[2]) | (float_to_bf16_bits(silu_f(g[3]) * u[3]) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (int64_t)(p0 + m) * Nh + u0 + 4 * (lane >> 4)) = packed;
 }
 
 // Only experts holding n rows with rows_lo < n <= rows_hi are multiplied here.
@@ -105,7 +118,7 @@ __global__ void __launch_bounds__(256)
 gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
                    const int32_t* __restrict__ offsets, int E, const uint8_t* __restrict__ W,
                    const uint16_t* __restrict__ Wsc, int64_t W_stride, void* __restrict__ out, int N, int K,
-                   int ntiles_n, int rows_lo, int rows_hi) {
+                   int ntiles_n, int rows_lo, int rows_hi, int act) {
     constexpr int ROWS = 16 * NB;              // weight rows per workgroup
     constexpr int SEGS = kStageBytes / 16;     // 16-byte segments per row per stage
     constexpr int LROW = kStageBytes + 16;     // padded LDS row (conflict-free 16-row column reads)
@@ -305,6 +318,23 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
     }
     __syncthreads();
     if (wave == 0) {
+        if constexpr (WHICH == 1 && NB % 2 == 0) {
+            if (act == kActSwiglu) {  // blocks 2 b' (gate) and 2 b' + 1 (up) of 32 aligned rows
+#pragma unroll
+                for (int b = 0; b < NB; b += 2)
+#pragma unroll
+                    for (int c = 0; c < MT; ++c) {
+                        f32x4 g = acc[b][c], u = acc[b + 1][c];
+#pragma unroll
+                        for (int w = 0; w < 3; ++w) {
+                            g += red[w][b * MT + c][lane];
+                            u += red[w][(b + 1) * MT + c][lane];
+                        }
+                        store_swiglu(out, N >> 1, p0 + 16 * c, rows - 16 * c, (n0 + 16 * b) >> 1, g, u, lane);
+                    }
+                return;
+            }
+        }
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -312,7 +342,7 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
                 f32x4 v = acc[b][c];
 #pragma unroll
                 for (int w = 0; w < 3; ++w) v += red[w][b * MT + c][lane];
-                store_tile<WHICH>(out, N, p0 + 16 * c, rows - 16 * c, n0 + 16 * b, v, lane);
+                store_tile<WHICH>(out, N, p0 + 16 * c, rows - 16 * c, n0 + 16 * b, v, lane, act);
             }
     }
 }
@@ -331,10 +361,10 @@ hipError_t launch_stream_nb(const GemmArgs& a, hipStream_t stream) {
     dim3 grid((unsigned)blocks), block(256);
     if (a.which == 1)
         hipLaunchKernelGGL((gemm_stream_kernel<WQ, 1, NB, MT, SB>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E,
-                           W, S, a.W_stride, a.out, (int)a.N, (int)a.K, ntiles_n, a.rows_lo, a.rows_hi);
+                           W, S, a.W_stride, a.out, (int)a.N, (int)a.K, ntiles_n, a.rows_lo, a.rows_hi, a.act);
     else
         hipLaunchKernelGGL((gemm_stream_kernel<WQ, 2, NB, MT, SB>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E,
-                           W, S, a.W_stride, a.out, (int)a.N, (int)a.K, ntiles_n, a.rows_lo, a.rows_hi);
+                           W, S, a.W_stride, a.out, (int)a.N, (int)a.K, ntiles_n, a.rows_lo, a.rows_hi, a.act);
     return hipGetLastError();
 }
 
@@ -343,6 +373,9 @@ hipError_t launch_stream_nb(const GemmArgs& a, hipStream_t stream) {
 // weights streamed from HBM; the wider tiles stage 128 bytes of each row (the
 // register double buffer stays at 8 loads per lane).  INT4: 64 weight rows.
 hipError_t launch_stream_bf16(const GemmArgs& a, hipStream_t stream) {
+    // SwiGLU pairs a gate and an up block of 16 rows inside one workgroup: NB even
+    if (a.stream_mt == 1 && a.which == 1 && a.act == kActSwiglu && MOE_STREAM_NB_BF16 % 2 != 0)
+        return launch_stream_nb<kBF16, 2, 1, 128>(a, stream);
     if (a.stream_mt == 1) return launch_stream_nb<kBF16, MOE_STREAM_NB_BF16, 1, MOE_STREAM_STAGE_BF16>(a, stream);
     if (a.stream_mt == 2) return launch_stream_nb<kBF16, 2, 2, 128>(a, stream);
     return launch_stream_nb<kBF16, 4, 4, 128>(a, stream);

@@ -131,9 +131,36 @@ __device__ __forceinline__ void dequant_word_to_lds(uint32_t word, uint32_t sbit
 
 // Epilogue: element v of acc[i][j] is D[n = wn + 32i + 8(v/4) + 4h + (v%4)][m = wm + 32j + r];
 // GEMM1 stores bf16 GeLU(D), GEMM2 stores fp32 D, for rows below `rows` and n below N.
-template <int WHICH, int TI, int TJ>
+template <int WHICH, int TI, int TJ, int ACT>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TI][TJ], void* __restrict__ out, int N, int n0, int p0,
                                            int rows, int wn, int wm, int r, int h) {
+    if constexpr (WHICH == 1 && ACT == kActSwiglu) {
+        // accumulators 0..7 of a 32-row block hold gate rows 8 q + 4 h + c (q < 2), 8..15 the up rows 16 below
+        const int Nh = N >> 1;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+            const int m = wm + 32 * j + r;
+            if (m >= rows) continue;
+            const int64_t orow = (int64_t)(p0 + m) * Nh;
+#pragma unroll
+            for (int i = 0; i < TI; ++i) {
+                const int nb = n0 + wn + 32 * i;
+                if (nb >= N) continue;
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    float hv[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) hv[c] = silu_f(acc[i][j][4 * q + c]) * acc[i][j][4 * q + 8 + c];
+                    uint2 packed;
+                    packed.x = float_to_bf16_bits(hv[0]) | (float_to_bf16_bits(hv[1]) << 16);
+                    packed.y = float_to_bf16_bits(hv[2]) | (float_to_bf16_bits(hv[3]) << 16);
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + orow + (nb >> 1) + 8 * q + 4 * h) =
+                        packed;
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
         const int m = wm + 32 * j + r;
@@ -149,8 +176,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TI][TJ], void* __
                 const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
                 if constexpr (WHICH == 1) {
                     uint2 packed;
-                    packed.x = float_to_bf16_bits(gelu_erf(v0)) | (float_to_bf16_bits(gelu_erf(v1)) << 16);
-                    packed.y = float_to_bf16_bits(gelu_erf(v2)) | (float_to_bf16_bits(gelu_erf(v3)) << 16);
+                    packed.x = float_to_bf16_bits(act_f(v0, ACT)) | (float_to_bf16_bits(act_f(v1, ACT)) << 16);
+                    packed.y = float_to_bf16_bits(act_f(v2, ACT)) | (float_to_bf16_bits(act_f(v3, ACT)) << 16);
                     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + orow + n) = packed;
                 } else {
                     *reinterpret_cast<float4*>(static_cast<float*>(out) + orow + n) = make_float4(v0, v1, v2, v3);
@@ -167,7 +194,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TI][TJ], void* __
 // so that a remainder of 40 rows costs a quarter tile, not a full one.
 // WQ = kBF16: Wexp is the expert's bf16 [N][K] matrix; WQ = kINT4: its packed
 // codes [N][K/2] with bf16 scales Wsc [N][K/128].
-template <int WQ, int WHICH, int TI, int TJ, int XROWS>
+template <int WQ, int WHICH, int TI, int TJ, int XROWS, int ACT>
 __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*Xt)[kTileBytes], uint8_t (*Ct)[4096],
                                           uint8_t (*St)[4096],
                                           const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
@@ -425,7 +452,7 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
         step(s0 + 3, 3, 0);
     }
 
-    store_tile<WHICH, TI, TJ>(acc, out, N, n0, p0, rows, wn, wm, r, h);
+    store_tile<WHICH, TI, TJ, ACT>(acc, out, N, n0, p0, rows, wn, wm, r, h);
 }
 
 // bf16 weights, K-stages of 64: each stage holds 128 bytes (one whole
@@ -437,7 +464,7 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
 // groups.  Stage k is multiplied in four k-substeps of 16.  Logical segment seg of tile row
 // `row` sits at byte row * 128 + 16 * (seg ^ ((row >> 1) & 7)) of a stage.
 
-template <int WHICH, int TI, int TJ, int XROWS>
+template <int WHICH, int TI, int TJ, int XROWS, int ACT>
 __device__ __forceinline__ void tile_gemm_bf16_bk64(uint8_t* Wl, uint8_t* Xl, const uint16_t* __restrict__ A,
                                                     const int32_t* __restrict__ a_rows, const void* Wexp,
                                                     void* __restrict__ out, int N, int K, int n0, int p0, int rows) {
@@ -557,13 +584,13 @@ __device__ __forceinline__ void tile_gemm_bf16_bk64(uint8_t* Wl, uint8_t* Xl, co
         compute_pair(wb, xb, 0);
         compute_pair(wb, xb, 1);
     }
-    store_tile<WHICH, TI, TJ>(acc, out, N, n0, p0, rows, wn, wm, r, h);
+    store_tile<WHICH, TI, TJ, ACT>(acc, out, N, n0, p0, rows, wn, wm, r, h);
 }
 
 // W: the experts' weights, W_stride bytes apart (bf16 [N][K] or INT4 codes
 // [N][K/2]); Wsc: INT4 scales bf16 [E][N][K/128] (unused for bf16).  Only
 // experts holding more than rows_lo rows are multiplied here.
-template <int WQ, int WHICH>
+template <int WQ, int WHICH, int ACT>
 __global__ void __launch_bounds__(256, 1)
 gemm_tiled_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
                   const int32_t* __restrict__ offsets, int E, const uint8_t* __restrict__ W, int64_t W_stride,
@@ -599,19 +626,19 @@ gemm_tiled_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_
     const void* Wsc_e = (WQ == kINT4) ? (const void*)(Wsc + (int64_t)e * N * (K / 128)) : nullptr;
     if constexpr (WQ == kBF16) {
         if (rows > 128)
-            tile_gemm_bf16_bk64<WHICH, 4, 4, 256>(smem, smem + 3 * 32768, A, a_rows, Wexp, out, N, K, n0, p0, rows);
+            tile_gemm_bf16_bk64<WHICH, 4, 4, 256, ACT>(smem, smem + 3 * 32768, A, a_rows, Wexp, out, N, K, n0, p0, rows);
         else if (rows > 64)
-            tile_gemm_bf16_bk64<WHICH, 2, 4, 128>(smem, smem + 3 * 32768, A, a_rows, Wexp, out, N, K, n0, p0, rows);
+            tile_gemm_bf16_bk64<WHICH, 2, 4, 128, ACT>(smem, smem + 3 * 32768, A, a_rows, Wexp, out, N, K, n0, p0, rows);
         else
-            tile_gemm_bf16_bk64<WHICH, 2, 2, 64>(smem, smem + 3 * 32768, A, a_rows, Wexp, out, N, K, n0, p0, rows);
+            tile_gemm_bf16_bk64<WHICH, 2, 2, 64, ACT>(smem, smem + 3 * 32768, A, a_rows, Wexp, out, N, K, n0, p0, rows);
         return;
     }
     if (rows > 128)
-        tile_gemm<WQ, WHICH, 4, 4, 256>(Wt, Xt, Ct, St, A, a_rows, Wexp, Wsc_e, out, N, K, n0, p0, rows);
+        tile_gemm<WQ, WHICH, 4, 4, 256, ACT>(Wt, Xt, Ct, St, A, a_rows, Wexp, Wsc_e, out, N, K, n0, p0, rows);
     else if (rows > 64)
-        tile_gemm<WQ, WHICH, 2, 4, 128>(Wt, Xt, Ct, St, A, a_rows, Wexp, Wsc_e, out, N, K, n0, p0, rows);
+        tile_gemm<WQ, WHICH, 2, 4, 128, ACT>(Wt, Xt, Ct, St, A, a_rows, Wexp, Wsc_e, out, N, K, n0, p0, rows);
     else
-        tile_gemm<WQ, WHICH, 2, 2, 64>(Wt, Xt, Ct, St, A, a_rows, Wexp, Wsc_e, out, N, K, n0, p0, rows);
+        tile_gemm<WQ, WHICH, 2, 2, 64, ACT>(Wt, Xt, Ct, St, A, a_rows, Wexp, Wsc_e, out, N, K, n0, p0, rows);
 }
 
 }  // namespace
@@ -628,21 +655,21 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
     const uint16_t* S = static_cast<const uint16_t*>(a.W_scales);
     dim3 grid((unsigned)blocks), block(256);
     const int N = (int)a.N, K = (int)a.K;
+#define MOE_TILED_LAUNCH(WQ_, WHICH_, ACT_)                                                                        \
+    hipLaunchKernelGGL((gemm_tiled_kernel<WQ_, WHICH_, ACT_>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W, \
+                       a.W_stride, S, a.out, N, K, ntiles_n, a.rows_lo)
     if (a.w_dtype == kINT4) {
-        if (a.which == 1)
-            hipLaunchKernelGGL((gemm_tiled_kernel<kINT4, 1>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
-                               a.W_stride, S, a.out, N, K, ntiles_n, a.rows_lo);
-        else
-            hipLaunchKernelGGL((gemm_tiled_kernel<kINT4, 2>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
-                               a.W_stride, S, a.out, N, K, ntiles_n, a.rows_lo);
+        if (a.which == 2) MOE_TILED_LAUNCH(kINT4, 2, kActGelu);
+        else if (a.act == kActSilu) MOE_TILED_LAUNCH(kINT4, 1, kActSilu);
+        else if (a.act == kActSwiglu) MOE_TILED_LAUNCH(kINT4, 1, kActSwiglu);
+        else MOE_TILED_LAUNCH(kINT4, 1, kActGelu);
     } else {
-        if (a.which == 1)
-            hipLaunchKernelGGL((gemm_tiled_kernel<kBF16, 1>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
-                               a.W_stride, S, a.out, N, K, ntiles_n, a.rows_lo);
-        else
-            hipLaunchKernelGGL((gemm_tiled_kernel<kBF16, 2>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E, W,
-                               a.W_stride, S, a.out, N, K, ntiles_n, a.rows_lo);
+        if (a.which == 2) MOE_TILED_LAUNCH(kBF16, 2, kActGelu);
+        else if (a.act == kActSilu) MOE_TILED_LAUNCH(kBF16, 1, kActSilu);
+        else if (a.act == kActSwiglu) MOE_TILED_LAUNCH(kBF16, 1, kActSwiglu);
+        else MOE_TILED_LAUNCH(kBF16, 1, kActGelu);
     }
+#undef MOE_TILED_LAUNCH
     return hipGetLastError();
 }
 

@@ -68,19 +68,20 @@ hipError_t launch_zero_counts(int32_t* counts, int E, int32_t* offsets, hipStrea
 
 // ---------------------------------------------------------- grouped GEMM
 struct GemmArgs {
-    int which;              // 1: out = GeLU(W1 . A[a_rows]) ; 2: out = W2 . A
+    int which;              // 1: out = act(W1 . A[a_rows]) ; 2: out = W2 . A
     const void* A;          // activations: x [T][K] (which 1) or H [T*k][K] (which 2)
     const int32_t* a_rows;  // which 1: dispatch position -> token row of A
     const int32_t* offsets; // [E+1]
     const void* W;          // expert 0's [N][K] matrix
     const void* W_scales;   // INT4: bf16 [E][N][K/128]
     int64_t W_stride;       // bytes between experts
-    void* out;              // [T*k][N]
+    void* out;              // [T*k][N] ([T*k][N/2] for SwiGLU)
     int64_t T, N, K;        // T: tokens (rows = T * k)
     int E, k, w_dtype, act_dtype;
     int path;               // 1 streaming, 2 tiled
     int rows_lo, rows_hi;   // only experts holding n rows, rows_lo < n <= rows_hi
     int stream_mt;          // streaming kernel: 16-row dispatch tiles per workgroup (1, 2 or 4)
+    int act = 0;            // which 1: kActGelu, kActSilu or kActSwiglu (N = 2 d_ff weight rows)
 };
 hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream);  // BF16 / INT4 weights
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);   // BF16 weights

@@ -39,6 +39,9 @@ int64_t elem_bits(int32_t dtype) { return dtype == MOE_DTYPE_F32 ? 32 : dtype ==
 // whole blocks of 8 scale groups.
 bool int4_tiled_ok(const moe_config& c) { return c.d % 1024 == 0 && c.d_ff % 1024 == 0; }
 
+// Rows of each expert's W1: d_ff, or 2 d_ff (gate and up) for SwiGLU.
+int64_t w1_rows(const moe_config& c) { return c.expert_act == MOE_ACT_SWIGLU ? 2 * c.d_ff : c.d_ff; }
+
 moe_status check_config(const moe_config* c) {
     if (!c) return MOE_ERR_INVALID_ARGUMENT;
     if (c->T < 0 || c->T > kMaxT) return MOE_ERR_INVALID_ARGUMENT;
@@ -58,6 +61,7 @@ moe_status check_config(const moe_config* c) {
     if (!(c->noise_std >= 0.0f) || !isfinite(c->noise_std)) return MOE_ERR_INVALID_ARGUMENT;
     // a rerouted or dropped slot has no renormalised gate defined
     if (c->gate_norm == 1 && c->capacity_factor > 0.0f) return MOE_ERR_UNSUPPORTED;
+    if (c->expert_act < MOE_ACT_GELU || c->expert_act > MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARGUMENT;
     if (c->act_dtype != MOE_DTYPE_F32 && c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARGUMENT;
     if (c->w_dtype < MOE_DTYPE_F32 || c->w_dtype > MOE_DTYPE_INT4_G128) return MOE_ERR_INVALID_ARGUMENT;
     if (c->w_dtype == MOE_DTYPE_INT4_G128 && (c->d % 128 != 0 || c->d_ff % 128 != 0))
@@ -71,7 +75,7 @@ moe_status check_config(const moe_config* c) {
     const int64_t ab = c->act_dtype == MOE_DTYPE_F32 ? 4 : 2;
     const int64_t Tk = c->T * c->k;
     if (c->T * c->d * ab >= kMaxArrayBytes || Tk * c->d_ff * 4 >= kMaxArrayBytes || Tk * c->d * 4 >= kMaxArrayBytes ||
-        c->d * c->d_ff * elem_bits(c->w_dtype) / 8 >= kMaxArrayBytes)
+        w1_rows(*c) * c->d * elem_bits(c->w_dtype) / 8 >= kMaxArrayBytes)
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
@@ -154,13 +158,14 @@ hipError_t run_gemm(const moe_config& c, int which, const void* A, const int32_t
     g.W_stride = stride;
     g.out = out;
     g.T = c.T;
-    g.N = which == 1 ? c.d_ff : c.d;
+    g.N = which == 1 ? w1_rows(c) : c.d;
     g.K = which == 1 ? c.d : c.d_ff;
     g.E = c.E;
     g.k = c.k;
     g.w_dtype = c.w_dtype;
     g.act_dtype = c.act_dtype;
     g.path = gemm_path_of(c);
+    g.act = which == 1 ? c.expert_act : 0;
     g.rows_lo = 0;
     g.rows_hi = 0x7fffffff;
     // a token adds at most one row to an expert, so no expert holds more than T rows
@@ -230,7 +235,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
     if (!expert_ids || !aligned(expert_ids, 4) || !gate_weights || !aligned(gate_weights, 4))
         return MOE_ERR_INVALID_ARGUMENT;
     if (router_bias && !aligned(router_bias, 4)) return MOE_ERR_INVALID_ARGUMENT;
-    if ((s = check_weights(c, W1, W1_scales, W1_expert_stride, c.d_ff, c.d)) != MOE_OK) return s;
+    if ((s = check_weights(c, W1, W1_scales, W1_expert_stride, w1_rows(c), c.d)) != MOE_OK) return s;
     if ((s = check_weights(c, W2, W2_scales, W2_expert_stride, c.d, c.d_ff)) != MOE_OK) return s;
     const Layout L = layout_of(c);
     if (!workspace || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
@@ -373,7 +378,7 @@ moe_status moe_grouped_gemm(const moe_config* cfg, int32_t which, const void* A,
     if (!A || !aligned(A, 16) || !offsets || !aligned(offsets, 4) || !out || !aligned(out, 16))
         return MOE_ERR_INVALID_ARGUMENT;
     if (which == 1 && (!a_rows || !aligned(a_rows, 4))) return MOE_ERR_INVALID_ARGUMENT;
-    const int64_t N = which == 1 ? c.d_ff : c.d;
+    const int64_t N = which == 1 ? w1_rows(c) : c.d;
     const int64_t K = which == 1 ? c.d : c.d_ff;
     if ((s = check_weights(c, W, W_scales, W_expert_stride, N, K)) != MOE_OK) return s;
     hipError_t e = run_gemm(c, which, A, a_rows, offsets, W, W_scales, W_expert_stride, out, stream);

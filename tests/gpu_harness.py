@@ -30,7 +30,8 @@ def tau32(tau):
 def abi_config(cfg, gemm_path=moe.GEMM_AUTO, seed=0, token_offset=0):
     return moe.config(cfg["T"], cfg["d"], cfg["d_ff"], cfg["E"], cfg["k"], cfg["act"], cfg["w"], tau=cfg["tau"],
                       use_gumbel=cfg["gumbel"], seed=seed, token_offset=token_offset, gemm_path=gemm_path,
-                      gate_norm=cfg.get("gate_norm", 0), noise_std=cfg.get("noise", 0.0))
+                      gate_norm=cfg.get("gate_norm", 0), noise_std=cfg.get("noise", 0.0),
+                      expert_act=cfg.get("ffn", 0))
 
 
 def run_forward(cfg, inp, gemm_path=moe.GEMM_AUTO, noise_seed=0, token_offset=0, device="cuda"):
@@ -129,7 +130,7 @@ def oracle_y(orc, cfg, inp, ref, tokens):
             S1[e] = moe_synth.to_bits(inp["S1"][e])
             S2[e] = moe_synth.to_bits(inp["S2"][e])
     return orc.forward_tokens(moe_synth.to_bits(inp["x"]), ref["ids"], ref["gate_p"], W1, W2, cfg["act"], cfg["w"],
-                              cfg["d_ff"], tokens, S1=S1, S2=S2)
+                              cfg["d_ff"], tokens, S1=S1, S2=S2, act=cfg.get("ffn", 0))
 
 
 def normwise_err(y_gpu_rows, y_ref):

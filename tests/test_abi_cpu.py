@@ -64,7 +64,7 @@ def _cfg(**kw):
     base.update(kw)
     c = moe.config(base["T"], base["d"], base["d_ff"], base["E"], base["k"], base["act_dtype"], base["w_dtype"])
     for key in ("tau", "use_gumbel", "gemm_path", "reserved", "capacity_factor", "capacity_policy", "gate_norm",
-                "noise_std"):
+                "noise_std", "expert_act"):
         if key in kw:
             setattr(c, key, kw[key])
     return c
@@ -79,7 +79,7 @@ BAD = [
     dict(capacity_factor=-0.0 - 1e-30), dict(capacity_policy=2), dict(capacity_policy=-1),
     dict(capacity_factor=1.25, capacity_policy=7),
     dict(gate_norm=2), dict(gate_norm=-1), dict(noise_std=-0.1), dict(noise_std=float("nan")),
-    dict(noise_std=float("inf")),
+    dict(noise_std=float("inf")), dict(expert_act=3), dict(expert_act=-1),
 ]
 
 
@@ -180,6 +180,14 @@ def test_forward_rejects_bad_pointers(lib, bad):
 
 def test_forward_rejects_small_workspace(lib):
     assert _forward(lib, _cfg(), wsb=1024) == binding.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_swiglu_w1_holds_gate_and_up_rows(lib):
+    """SwiGLU experts read 2 d_ff rows of W1: a stride of one d_ff x d matrix is too small."""
+    c = _cfg(expert_act=moe.ACT_SWIGLU)
+    one = 256 * 512 * 2
+    assert _forward(lib, c, s1=one) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert _forward(lib, c, s1=2 * one, ws=0x90000, wsb=1024) == binding.MOE_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_int4_needs_scales(lib):

@@ -14,9 +14,12 @@ pytestmark = pytest.mark.gpu
 F32, BF16, INT4 = moe.F32, moe.BF16, moe.INT4_G128
 
 
-def case(T, d, d_ff, E, k=2, act=BF16, w=BF16, bias=False, tau=1.0, gumbel=False, gate_norm=0, noise=0.0):
+def case(T, d, d_ff, E, k=2, act=BF16, w=BF16, bias=False, tau=1.0, gumbel=False, gate_norm=0, noise=0.0, ffn=0):
     return dict(T=T, d=d, d_ff=d_ff, E=E, k=k, act=act, w=w, bias=bias, tau=tau, gumbel=gumbel, gate_norm=gate_norm,
-                noise=noise, name="case")
+                noise=noise, ffn=ffn, name="case")
+
+
+SILU, SWIGLU = moe.ACT_SILU, moe.ACT_SWIGLU
 
 
 ROUTER_CASES = {
@@ -130,6 +133,22 @@ FORWARD_CASES = {
     "int4-T12-d512-dff1024-E8-renorm-gumbel": (case(12, 512, 1024, 8, w=INT4, tau=0.5, gumbel=True, gate_norm=1),
                                                [moe.GEMM_AUTO]),
     "f32-T64-d128-dff256-E6-k3-renorm": (case(64, 128, 256, 6, k=3, act=F32, w=F32, gate_norm=1), [moe.GEMM_AUTO]),
+    # expert activations: SiLU and SwiGLU on every kernel (streaming with 16-, 32- and 64-row tiles, tiled with
+    # its three tile heights, INT4 on both, fp32)
+    "bf16-T300-d512-dff1024-E8-skewed-silu": (case(300, 512, 1024, 8, bias=True, ffn=SILU),
+                                              [moe.GEMM_STREAMING, moe.GEMM_TILED]),
+    "bf16-T300-d512-dff1024-E8-skewed-swiglu": (case(300, 512, 1024, 8, bias=True, ffn=SWIGLU),
+                                                [moe.GEMM_STREAMING, moe.GEMM_TILED]),
+    "bf16-T12-d512-dff1024-E8-swiglu": (case(12, 512, 1024, 8, ffn=SWIGLU), [moe.GEMM_STREAMING]),
+    "bf16-T24-d512-dff1024-E4-swiglu": (case(24, 512, 1024, 4, ffn=SWIGLU), [moe.GEMM_STREAMING]),
+    "bf16-T150-d320-dff576-E6-ntail-swiglu": (case(150, 320, 576, 6, ffn=SWIGLU), [moe.GEMM_STREAMING, moe.GEMM_TILED]),
+    "int4-T200-d1024-dff1024-E8-skewed-swiglu": (case(200, 1024, 1024, 8, w=INT4, bias=True, ffn=SWIGLU),
+                                                 [moe.GEMM_STREAMING, moe.GEMM_TILED]),
+    "int4-T200-d1024-dff1024-E8-skewed-silu": (case(200, 1024, 1024, 8, w=INT4, bias=True, ffn=SILU),
+                                               [moe.GEMM_STREAMING, moe.GEMM_TILED]),
+    "int4-T12-d512-dff1024-E8-swiglu": (case(12, 512, 1024, 8, w=INT4, ffn=SWIGLU), [moe.GEMM_AUTO]),
+    "f32-T130-d192-dff320-E5-k3-swiglu": (case(130, 192, 320, 5, k=3, act=F32, w=F32, ffn=SWIGLU), [moe.GEMM_AUTO]),
+    "f32-T64-d128-dff256-E6-silu": (case(64, 128, 256, 6, act=F32, w=F32, ffn=SILU), [moe.GEMM_AUTO]),
 }
 FORWARD_PARAMS = [(n, p) for n, (_, paths) in FORWARD_CASES.items() for p in paths]
 
