@@ -71,6 +71,25 @@ __device__ __forceinline__ float gelu_erf(float h) {
     return 0.5f * h * (1.0f + erff(h * 0.70710678118654752440f));
 }
 
+// GeLU h * Phi(h) for results rounded to bf16: Phi from erf by Abramowitz &
+// Stegun's rational approximation 7.1.26, erf(x) = 1 - q(x) for x >= 0 with
+// q = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e^(-x^2), t = 1 / (1 + p x),
+// |error| <= 1.5e-7, evaluated with the hardware base-2 exponential and
+// reciprocal.  With x = |h| / sqrt 2: GeLU(h) = h - h q / 2 for h >= 0 and
+// h q / 2 for h < 0 (absolute error below 2e-7 |h|, far under the 2^-9
+// relative rounding of bf16).  One branch-free path: no lane divergence.
+__device__ __forceinline__ float gelu_bf16(float h) {
+    const float x = fabsf(h) * 0.70710678118654752440f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+    float poly = fmaf(t, 1.061405429f, -1.453152027f);
+    poly = fmaf(t, poly, 1.421413741f);
+    poly = fmaf(t, poly, -0.284496736f);
+    poly = fmaf(t, poly, 0.254829592f);
+    const float q = t * poly * __builtin_amdgcn_exp2f(-(x * x) * 1.4426950408889634f);
+    const float hq = 0.5f * h * q;
+    return h >= 0.0f ? h - hq : hq;
+}
+
 // SiLU (swish): a * sigmoid(a) = a / (1 + 2^(-a log2 e)), with the hardware
 // base-2 exponential and reciprocal (each about 1 ulp; the result is rounded
 // to bf16 or enters an fp32 product).  Few live temporaries: it sits in the
@@ -87,8 +106,8 @@ constexpr int kActGelu = 0;
 constexpr int kActSilu = 1;
 constexpr int kActSwiglu = 2;
 
-// The elementwise activation of GEMM1 (GeLU or SiLU).
-__device__ __forceinline__ float act_f(float v, int act) { return act == kActSilu ? silu_f(v) : gelu_erf(v); }
+// The elementwise activation of GEMM1 (GeLU or SiLU) for a bf16 H.
+__device__ __forceinline__ float act_f(float v, int act) { return act == kActSilu ? silu_f(v) : gelu_bf16(v); }
 
 // The m-tiles of a grouped GEMM whose experts hold offsets[e+1]-offsets[e]
 // rows, cut into tiles of BM rows and numbered expert-major.  Built by one

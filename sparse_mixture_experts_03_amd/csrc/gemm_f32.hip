@@ -97,10 +97,11 @@ gemm_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__ a_rows,
         if (m >= rows) continue;
         float4 v = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
         if (WHICH == 1) {
-            v.x = act_f(v.x, act);
-            v.y = act_f(v.y, act);
-            v.z = act_f(v.z, act);
-            v.w = act_f(v.w, act);
+            // fp32 H: the erff GeLU, not the bf16-grade one
+            v.x = act == kActSilu ? silu_f(v.x) : gelu_erf(v.x);
+            v.y = act == kActSilu ? silu_f(v.y) : gelu_erf(v.y);
+            v.z = act == kActSilu ? silu_f(v.z) : gelu_erf(v.z);
+            v.w = act == kActSilu ? silu_f(v.w) : gelu_erf(v.w);
         }
         *reinterpret_cast<float4*>(out + (int64_t)(p0 + m) * N + n0 + tx * 4) = v;
     }

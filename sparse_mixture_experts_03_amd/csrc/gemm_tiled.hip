@@ -131,7 +131,10 @@ __device__ __forceinline__ void dequant_word_to_lds(uint32_t word, uint32_t sbit
 
 // Epilogue: element v of acc[i][j] is D[n = wn + 32i + 8(v/4) + 4h + (v%4)][m = wm + 32j + r];
 // GEMM1 stores bf16 GeLU(D), GEMM2 stores fp32 D, for rows below `rows` and n below N.
-template <int WHICH, int TI, int TJ, int ACT>
+// GELU_ERF: GeLU through erff instead of the cheaper bf16-grade form.  The
+// INT4 kernel keeps it: its main loop holds nearly every register, and with
+// the other form the allocator spills inside the MFMA loop (measured 5x slower).
+template <int WHICH, int TI, int TJ, int ACT, bool GELU_ERF = false>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TI][TJ], void* __restrict__ out, int N, int n0, int p0,
                                            int rows, int wn, int wm, int r, int h) {
     if constexpr (WHICH == 1 && ACT == kActSwiglu) {
@@ -176,8 +179,20 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TI][TJ], void* __
                 const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
                 if constexpr (WHICH == 1) {
                     uint2 packed;
-                    packed.x = float_to_bf16_bits(act_f(v0, ACT)) | (float_to_bf16_bits(act_f(v1, ACT)) << 16);
-                    packed.y = float_to_bf16_bits(act_f(v2, ACT)) | (float_to_bf16_bits(act_f(v3, ACT)) << 16);
+                    float a0, a1, a2, a3;
+                    if constexpr (GELU_ERF && ACT == kActGelu) {
+                        a0 = gelu_erf(v0);
+                        a1 = gelu_erf(v1);
+                        a2 = gelu_erf(v2);
+                        a3 = gelu_erf(v3);
+                    } else {
+                        a0 = act_f(v0, ACT);
+                        a1 = act_f(v1, ACT);
+                        a2 = act_f(v2, ACT);
+                        a3 = act_f(v3, ACT);
+                    }
+                    packed.x = float_to_bf16_bits(a0) | (float_to_bf16_bits(a1) << 16);
+                    packed.y = float_to_bf16_bits(a2) | (float_to_bf16_bits(a3) << 16);
                     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + orow + n) = packed;
                 } else {
                     *reinterpret_cast<float4*>(static_cast<float*>(out) + orow + n) = make_float4(v0, v1, v2, v3);
@@ -452,7 +467,7 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
         step(s0 + 3, 3, 0);
     }
 
-    store_tile<WHICH, TI, TJ, ACT>(acc, out, N, n0, p0, rows, wn, wm, r, h);
+    store_tile<WHICH, TI, TJ, ACT, WQ == kINT4>(acc, out, N, n0, p0, rows, wn, wm, r, h);
 }
 
 // bf16 weights, K-stages of 64: each stage holds 128 bytes (one whole
