@@ -31,13 +31,16 @@
  *      Selecting on z equals selecting on softmax(z) (softmax is monotone). P1 §3.1 step 4; P2 §2.2 step 3
  *   5. p = softmax(z) over all E, max-subtracted; gate[j] = p[ids[j]] (not
  *      renormalised over the k chosen).                              P2 §2.2 step 4; P5 §3.1 worked example
- *   Variants (oracle_route_ex):
+ *   Variants (oracle_route_ex, oracle_router_encoder):
+ *   1'. two-layer router: a hidden layer h = GeLU(W_in x + b_in) of width
+ *      d_r (d/4 in the pages), stored in the activation dtype (rounded to
+ *      nearest even), then the linear router of step 1 on h.           P3 §3.1 (input encoder), §4.2
  *   2'. Gaussian noise sigma * n[e] added to the logits, n standard normal by
  *      Box-Muller from the same Philox block: z = (l + g + sigma n) / tau   P5 §3.3 (router noise injection)
  *   5'. renormalised gates: gate[j] = softmax over the k chosen z values
  *      (= p[ids[j]] / sum_j' p[ids[j']])                                   P4 §4.3 (softmax over the top-k)
  *   6. expert FFN  o = W2_e * GeLU(W1_e * x),  GeLU(h) = h * Phi(h)
- *                  = 0.5 h (1 + erf(h / sqrt 2)), no bias.           P3 §3.2 (d -> 4d -> d MLP, GELU)
+ *                  = 0.5 h erfc(-h / sqrt 2), no bias.           P3 §3.2 (d -> 4d -> d MLP, GELU)
  *      W1_e is d_ff x d, W2_e is d x d_ff (out x in, input dim contiguous).
  *      INT4 experts: w[n,c] = q[n,c] * s[n, c/128] exactly, q in [-8,7]
  *      (symmetric group-128 codes with bf16 scales).                 P1 §5.4; P2 §2.3 (dequantize step)
@@ -62,6 +65,28 @@
 #define ORACLE_INT4_G128 2
 
 /* ---------------------------------------------------------------- decoding */
+
+/* binary64 -> bf16 bits, rounded to nearest even in one step.  The value is
+ * first rounded to binary32 (nearest even); when that lands exactly on a bf16
+ * midpoint, the binary64 value decides the direction (above or below the
+ * midpoint in magnitude; an exact midpoint goes to the even neighbour). */
+static uint16_t double_to_bf16_bits(double v)
+{
+    float f = (float)v;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x40u); /* quiet NaN */
+    uint32_t hi = u >> 16, low = u & 0xffffu;
+    int up;
+    if (low != 0x8000u)
+        up = low > 0x8000u;
+    else if (fabs(v) != fabs((double)f))
+        up = fabs(v) > fabs((double)f);
+    else
+        up = (int)(hi & 1u);
+    return (uint16_t)(hi + (uint32_t)up);
+}
 
 static double bf16_to_double(uint16_t bits)
 {
@@ -161,10 +186,11 @@ double oracle_silu(double a)
     return a / (1.0 + exp(-a));
 }
 
-/* GeLU in its exact form h * Phi(h). */
+/* GeLU in its exact form h * Phi(h), with Phi(h) = erfc(-h / sqrt 2) / 2
+ * (no cancellation in the negative tail, where 1 + erf(h / sqrt 2) rounds to 0). */
 double oracle_gelu(double h)
 {
-    return 0.5 * h * (1.0 + erf(h / sqrt(2.0)));
+    return 0.5 * h * erfc(-h / sqrt(2.0));
 }
 
 /* ------------------------------------------------------------------ routing */
@@ -273,6 +299,34 @@ int oracle_route_ex(int64_t T, int64_t d, int32_t E, int32_t k, int32_t act_dtyp
             memcpy(p_out + t * E, p, sizeof(double) * (size_t)E);
     }
     free(l); free(z); free(p); free(taken);
+    return 0;
+}
+
+/*
+ * Hidden layer of the two-layer router (step 1'): for every token t and hidden
+ * unit j < d_r, r = sum_i x[t,i] W_in[j,i] (ascending i) + b_in[j], and
+ * h[t][j] = GeLU(r) stored in act_dtype (float, or bf16 bits rounded to
+ * nearest even from the binary64 value).  W_in is d_r x d (out x in), in
+ * act_dtype; b_in (float) may be NULL.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_router_encoder(int64_t T, int64_t d, int64_t d_r, int32_t act_dtype, const void *x,
+                          const void *W_in, const float *b_in, void *h_out)
+{
+    if (T < 0 || d < 1 || d_r < 1 || (act_dtype != ORACLE_F32 && act_dtype != ORACLE_BF16))
+        return -1;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t j = 0; j < d_r; ++j) {
+            double r = 0.0;
+            for (int64_t i = 0; i < d; ++i)
+                r += load_act(x, act_dtype, t * d + i) * load_act(W_in, act_dtype, j * d + i);
+            if (b_in)
+                r += (double)b_in[j];
+            double a = oracle_gelu(r);
+            if (act_dtype == ORACLE_F32)
+                ((float *)h_out)[t * d_r + j] = (float)a;
+            else
+                ((uint16_t *)h_out)[t * d_r + j] = double_to_bf16_bits(a);
+        }
     return 0;
 }
 

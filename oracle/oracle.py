@@ -58,6 +58,8 @@ class Oracle:
         lib.oracle_route.argtypes = [_I64, _I64, _I32, _I32, _I32, _P, _P, _P,
                                      ctypes.c_double, _I32, _U64, _U64, _P, _P, _P, _P, _P]
         lib.oracle_route.restype = ctypes.c_int
+        lib.oracle_router_encoder.argtypes = [_I64, _I64, _I64, _I32, _P, _P, _P, _P]
+        lib.oracle_router_encoder.restype = ctypes.c_int
         lib.oracle_route_ex.argtypes = [_I64, _I64, _I32, _I32, _I32, _P, _P, _P, ctypes.c_double, _I32,
                                         ctypes.c_double, _I32, _U64, _U64, _P, _P, _P, _P, _P]
         lib.oracle_route_ex.restype = ctypes.c_int
@@ -100,10 +102,32 @@ class Oracle:
         return self.lib.oracle_gelu(float(h))
 
     # -- routing ----------------------------------------------------------------
+    def router_encoder(self, x, W_in, b_in, act_dtype):
+        """Hidden layer of the two-layer router: GeLU(x W_in^T + b_in) in act_dtype
+        (float32, or bf16 bits as uint16), [T, d_r]."""
+        x = np.ascontiguousarray(x)
+        W_in = np.ascontiguousarray(W_in)
+        T, d = x.shape
+        d_r = W_in.shape[0]
+        assert W_in.shape[1] == d
+        b = None if b_in is None else np.ascontiguousarray(b_in, dtype=np.float32)
+        h = np.zeros((T, d_r), dtype=np.float32 if act_dtype == F32 else np.uint16)
+        rc = self.lib.oracle_router_encoder(T, d, d_r, act_dtype, x.ctypes.data, W_in.ctypes.data,
+                                            None if b is None else b.ctypes.data, h.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle_router_encoder rejected its arguments")
+        return h
+
     def route(self, x, Wg, k, act_dtype, bias=None, tau=1.0, use_gumbel=False, seed=0,
-              token_offset=0, want_zp=False, noise_std=0.0, gate_norm=0):
+              token_offset=0, want_zp=False, noise_std=0.0, gate_norm=0, encoder=None):
         """Returns dict(ids[T,k] int32, gates[T,k] float32, gate_p[T,k] float64 [, z, p]).
-        noise_std: sigma of the Gaussian logit noise; gate_norm=1: gates renormalised over the k chosen."""
+        noise_std: sigma of the Gaussian logit noise; gate_norm=1: gates renormalised over the k chosen.
+        encoder=(W_in, b_in): two-layer router; Wg is then the second layer [d_r, E] and the
+        result also holds the hidden layer "h"."""
+        hidden = None
+        if encoder is not None:
+            hidden = self.router_encoder(x, encoder[0], encoder[1], act_dtype)
+            x = hidden
         x = np.ascontiguousarray(x)
         Wg = np.ascontiguousarray(Wg)
         T, d = x.shape
@@ -126,6 +150,8 @@ class Oracle:
         out = dict(ids=ids, gates=gates, gate_p=gate_p)
         if want_zp:
             out.update(z=z, p=p)
+        if hidden is not None:
+            out["h"] = hidden
         return out
 
     def permute(self, ids, E):

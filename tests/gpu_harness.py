@@ -78,8 +78,24 @@ def check_routing(gpu_ids, gpu_gates, ref, k):
     return sorted(amb)
 
 
-def check_dispatch(orc, gpu_ids, E, counts, offsets=None, sorted_token=None, pos=None):
-    ref = orc.permute(gpu_ids, E)
+def check_forward_counts(orc, ref_ids, gpu_ids, amb, E, counts):
+    """The layer's per-expert counts.  Without ambiguous tokens the GPU ids equal
+    the oracle's, so the counts must equal the oracle's dispatch of its own
+    routing.  With some, either choice was allowed for those tokens: then the
+    counts must agree with the ids the GPU returned (numpy bincount), and the
+    oracle's counts may differ only by the ambiguous tokens' assignments."""
+    ref = orc.permute(ref_ids, E)
+    if not amb:
+        assert np.array_equal(counts, ref["counts"]), "counts differ"
+        return
+    assert np.array_equal(counts, np.bincount(gpu_ids.reshape(-1), minlength=E)), "counts disagree with ids"
+    k = gpu_ids.shape[1]
+    assert np.abs(counts.astype(np.int64) - ref["counts"]).sum() <= 2 * k * len(amb)
+
+
+def check_dispatch(orc, ids, E, counts, offsets=None, sorted_token=None, pos=None):
+    """Dispatch arrays of a given (oracle-side) routing against the oracle's permutation of it."""
+    ref = orc.permute(ids, E)
     assert np.array_equal(counts, ref["counts"]), "counts differ"
     if offsets is not None:
         assert np.array_equal(offsets, ref["offsets"]), "offsets differ"

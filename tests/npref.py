@@ -22,6 +22,23 @@ def f64_to_bf16_bits(a):
     return ((f + 0x7FFF + lsb) >> 16).astype(np.uint16)
 
 
+def f64_to_bf16_nearest(a):
+    """bf16 bits of the bf16 value nearest to each float64 (ties to the even code),
+    chosen by comparing the distances to the neighbouring bf16 values in float64."""
+    shape = np.shape(a)
+    a = np.asarray(a, dtype=np.float64).ravel()
+    guess = f64_to_bf16_bits(a).astype(np.int64)
+    out = np.empty(len(a), dtype=np.uint16)
+    for i, (v, g) in enumerate(zip(a, guess)):
+        cands = [c for c in (g - 1, g, g + 1) if 0 <= c <= 0xFFFF and ((c >> 15) == (g >> 15))]
+        vals = bf16_bits_to_f64(np.array(cands, dtype=np.uint16))
+        dist = np.abs(vals - v)
+        best = np.flatnonzero(dist == dist.min())
+        pick = [cands[j] for j in best]
+        out[i] = pick[0] if len(pick) == 1 else [c for c in pick if c % 2 == 0][0]
+    return out.reshape(shape)
+
+
 def unpack_int4(codes):
     """Signed INT4 codes [..., K] from packed bytes [..., K/2] (even index in the low nibble)."""
     codes = np.asarray(codes, dtype=np.uint8)

@@ -125,7 +125,9 @@ def pin_uniform_stream_layout(orc):
 
 def pin_gelu(orc):
     """GeLU(h) = h * Phi(h): table value Phi(1) = 0.8413447460685429, zero at
-    zero, odd-part identity GeLU(h) - GeLU(-h) = h, scipy's normal CDF."""
+    zero, odd-part identity GeLU(h) - GeLU(-h) = h, scipy's normal CDF, and
+    relative accuracy in the negative tail (Phi(-10) = 7.62e-24 from scipy's
+    log CDF), where 1 + erf cancels to zero."""
     assert orc.gelu(0.0) == 0.0
     assert abs(orc.gelu(1.0) - 0.8413447460685429) < 1e-15
     for h in np.linspace(-6, 6, 97):
@@ -134,6 +136,9 @@ def pin_gelu(orc):
         assert abs(orc.gelu(h) - orc.gelu(-h) - h) <= 1e-14 * max(1.0, abs(h)), h
     assert orc.gelu(40.0) == 40.0
     assert abs(orc.gelu(-40.0)) < 1e-300
+    for h in (-8.0, -10.0, -20.0, -30.0):
+        want = h * np.exp(stats.norm.logcdf(h))
+        assert abs(orc.gelu(h) - want) <= 1e-12 * abs(want), h  # erfc at x = |h|/sqrt 2: ~2 x^2 ulp
 
 
 # -------------------------------------------------------------------- routing
@@ -331,6 +336,44 @@ def pin_gaussian_noise(orc):
             assert abs((b["z"][t, e] - a["z"][t, e]) - dn) <= 1e-14 * (abs(a["z"][t, e]) + abs(dn) + 1)
     part = orc.route(x[3:], Wg, 2, F32, tau=0.5, seed=3, token_offset=43, noise_std=0.1, want_zp=True)
     assert np.array_equal(part["z"], b["z"][3:]) and np.array_equal(part["ids"], b["ids"][3:])
+
+
+def pin_router_encoder(orc):
+    """P3 §3.1/§4.2: a two-layer router, h = GeLU(W_in x + b_in) of width d/4,
+    then the linear router on h.  The hidden layer is stored in the
+    activation dtype.  Pins: (1) bf16 rounding of h in one step from binary64:
+    with one-hot W_in rows, r = 16 + c + 1/16 where c = +-2^-30 or 0 comes from
+    a second bf16 input, and GeLU(r) = r exactly at this size; 16 + 1/16 is
+    the midpoint between the bf16 neighbours 16 and 16.125, where the binary32
+    value sits for all three c: +2^-30 must round up, -2^-30 down, 0 to the
+    even neighbour 16.  (2) With small-integer inputs every sum is exact, and
+    h equals numpy's GeLU (scipy normal CDF) rounded to the nearest bf16 by
+    comparing neighbour distances.  (3) The routing on h equals the dense
+    numpy softmax/top-k of h @ W_out."""
+    W_in = np.zeros((3, 2), np.float64)
+    W_in[:, 0] = 1.0
+    W_in[:, 1] = 1.0
+    x = np.array([[16.0, 2.0 ** -30], [16.0, -(2.0 ** -30)], [16.0, 0.0]])
+    h = orc.router_encoder(_bf16(x), _bf16(W_in), np.full(3, 0.0625, np.float32), BF16)
+    assert h[:, 0].tolist() == [0x4181, 0x4180, 0x4180]   # 16.125, 16, 16
+
+    r = _rng(27)
+    T, d, d_r, E = 20, 32, 16, 6
+    xi = r.integers(-2, 3, (T, d)).astype(np.float64)
+    Wi = r.integers(-1, 2, (d_r, d)).astype(np.float64)
+    bi = (r.integers(-8, 9, d_r) / 8.0).astype(np.float32)
+    h = orc.router_encoder(_bf16(xi), _bf16(Wi), bi, BF16)
+    pre = xi @ Wi.T + bi.astype(np.float64)
+    assert np.array_equal(h, npref.f64_to_bf16_nearest(npref.gelu_cdf(pre)))
+    hf = orc.router_encoder(xi.astype(np.float32), Wi.astype(np.float32), bi, F32)
+    ulp = np.spacing(np.abs(npref.gelu_cdf(pre).astype(np.float32)))
+    assert np.all(np.abs(hf.astype(np.float64) - npref.gelu_cdf(pre)) <= ulp)
+    Wo = r.standard_normal((d_r, E)).astype(np.float32)
+    out = orc.route(_bf16(xi), npref.f64_to_bf16_bits(Wo), 2, BF16, encoder=(_bf16(Wi), bi), want_zp=True)
+    assert np.array_equal(out["h"], h)
+    z = npref.bf16_bits_to_f64(h) @ npref.bf16_bits_to_f64(npref.f64_to_bf16_bits(Wo))
+    assert np.max(np.abs(out["z"] - z)) <= 1e-13 * np.max(np.abs(z))
+    assert np.array_equal(out["ids"], npref.topk_lexsort(z, 2))
 
 
 def pin_gumbel_max_theorem(orc):

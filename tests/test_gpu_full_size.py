@@ -40,7 +40,7 @@ def test_full_size_parity(oracle, name):
     ids = out["ids"].cpu().numpy()
     amb = H.check_routing(ids, out["gates"].cpu().numpy(), ref, cfg["k"])
     counts = out["counts"].cpu().numpy()
-    H.check_dispatch(oracle, ids, cfg["E"], counts)
+    H.check_forward_counts(oracle, ref["ids"], ids, amb, cfg["E"], counts)
     assert int(counts.sum()) == cfg["T"] * cfg["k"]
     tokens = H.sample_tokens(ref["ids"], cfg["E"], SAMPLE[name], exclude=set(amb))
     y_ref = H.oracle_y(oracle, cfg, inp, ref, tokens)

@@ -161,7 +161,7 @@ def test_forward_parity(dev, oracle, name, path):
     ref = H.oracle_route(oracle, cfg, inp, noise_seed=5)
     ids = out["ids"].cpu().numpy()
     amb = H.check_routing(ids, out["gates"].cpu().numpy(), ref, cfg["k"])
-    H.check_dispatch(oracle, ids, cfg["E"], out["counts"].cpu().numpy())
+    H.check_forward_counts(oracle, ref["ids"], ids, amb, cfg["E"], out["counts"].cpu().numpy())
     assert int(out["counts"].sum()) == cfg["T"] * cfg["k"]
     tokens = np.array([t for t in range(cfg["T"]) if t not in amb], dtype=np.int64)
     y_ref = H.oracle_y(oracle, cfg, inp, ref, tokens)

@@ -24,12 +24,12 @@ MUTANTS = [
     ("softmax on logits", "p[e] = exp(z[e] - m);", "p[e] = exp(l[e] - m);"),
     ("gate from slot index", "gates[t * k + j] = (float)p[best];", "gates[t * k + j] = (float)p[j];"),
     ("gate_p from slot index", "gate_p[t * k + j] = p[best];", "gate_p[t * k + j] = p[j];"),
-    ("gelu tanh form", "return 0.5 * h * (1.0 + erf(h / sqrt(2.0)));",
+    ("gelu tanh form", "return 0.5 * h * erfc(-h / sqrt(2.0));",
      "return 0.5 * h * (1.0 + tanh(0.7978845608028654 * (h + 0.044715 * h * h * h)));"),
-    ("gelu half dropped", "return 0.5 * h * (1.0 + erf(h / sqrt(2.0)));",
-     "return h * (1.0 + erf(h / sqrt(2.0)));"),
-    ("gelu sqrt2 dropped", "return 0.5 * h * (1.0 + erf(h / sqrt(2.0)));",
-     "return 0.5 * h * (1.0 + erf(h));"),
+    ("gelu half dropped", "return 0.5 * h * erfc(-h / sqrt(2.0));", "return h * erfc(-h / sqrt(2.0));"),
+    ("gelu sqrt2 dropped", "return 0.5 * h * erfc(-h / sqrt(2.0));", "return 0.5 * h * erfc(-h);"),
+    ("gelu tail lost to cancellation", "return 0.5 * h * erfc(-h / sqrt(2.0));",
+     "return 0.5 * h * (1.0 + erf(h / sqrt(2.0)));"),
     ("W1 reads x reversed", "h += load_w(W1e, S1e, w_dtype, d, n, i) * xr[i];",
      "h += load_w(W1e, S1e, w_dtype, d, n, i) * xr[d - 1 - i];"),
     ("GeLU skipped", "a[n] = oracle_gelu(h);", "a[n] = h;"),
@@ -37,6 +37,12 @@ MUTANTS = [
     ("SwiGLU interleaved in blocks of 8", "int64_t rg = 32 * (n / 16) + n % 16, ru = rg + 16;",
      "int64_t rg = 16 * (n / 8) + n % 8, ru = rg + 8;"),
     ("SiLU sign", "return a / (1.0 + exp(-a));", "return a / (1.0 + exp(a));"),
+    ("router encoder skips GeLU", "double a = oracle_gelu(r);", "double a = r;"),
+    ("router encoder drops its bias", "r += (double)b_in[j];", "r += 0.0;"),
+    ("router encoder reads W_in transposed", "load_act(W_in, act_dtype, j * d + i)",
+     "load_act(W_in, act_dtype, i * d_r + j)"),
+    ("bf16 midpoint always rounds up", "up = (int)(hi & 1u);", "up = 1;"),
+    ("bf16 rounded twice", "else if (fabs(v) != fabs((double)f))", "else if (0)"),
     ("SiLU expert computes GeLU", "a[n] = oracle_silu(h);", "a[n] = oracle_gelu(h);"),
     ("W2 reads hidden reversed", "acc += load_w(W2e, S2e, w_dtype, d_ff, c, n) * a[n];",
      "acc += load_w(W2e, S2e, w_dtype, d_ff, c, n) * a[d_ff - 1 - n];"),
