@@ -102,6 +102,9 @@ typedef struct moe_config {
                               n standard normal by Box-Muller from words 2 and 3 of the (seed, token, expert)
                               Philox block; 0: none */
     int32_t expert_act;    /* moe_expert_act */
+    int32_t router_hidden; /* 0: single linear router (l = Wg^T x + b).  d_r > 0 (multiple of 64): two-layer
+                              router (P3 §3.1, §4.2; d/4 there): h = GeLU(W_in x + b_in), W_in [d_r][d] and h in
+                              act_dtype (h rounded to nearest even), then l = Wg^T h + b with Wg [d_r][E] */
 } moe_config;
 
 /* The experts' hidden activation (P3 §3.2 GELU; P1 §3.3 and §4.2 SiLU-gated units). */
@@ -136,8 +139,10 @@ moe_status moe_router_workspace_size(const moe_config *cfg, size_t *bytes);
 /*
  * The whole layer (P2 §2.2 steps 1-4; P1 §3.1; P3 §3.2).
  *   x            [T][d]   act_dtype                      (device, in)
- *   Wg           [d][E]   act_dtype                      (device, in)
+ *   Wg           [d][E]   act_dtype ([router_hidden][E] with a router encoder)    (device, in)
  *   router_bias  [E]      float, or NULL for none        (device, in)
+ *   router_W_in  [router_hidden][d] act_dtype, router_b_in [router_hidden] float or NULL: the encoder
+ *                layer when router_hidden > 0; both NULL otherwise            (device, in)
  *   W1, W2       expert 0's matrix ([d_ff][d], or [2 d_ff][d] for SwiGLU; [d][d_ff]); expert e starts
  *                e * W*_expert_stride bytes later
  *                (stride >= the matrix's bytes, multiple of 16)   (device, in)
@@ -154,7 +159,7 @@ moe_status moe_router_workspace_size(const moe_config *cfg, size_t *bytes);
  * T == 0 is a valid no-op that writes counts = 0.
  */
 moe_status moe_forward(const moe_config *cfg, const void *x, const void *Wg, const float *router_bias,
-                       const void *W1, const void *W1_scales, int64_t W1_expert_stride,
+                       const void *router_W_in, const float *router_b_in, const void *W1, const void *W1_scales, int64_t W1_expert_stride,
                        const void *W2, const void *W2_scales, int64_t W2_expert_stride,
                        void *y, int32_t *expert_ids, float *gate_weights, int32_t *counts,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
@@ -165,12 +170,29 @@ moe_status moe_forward(const moe_config *cfg, const void *x, const void *Wg, con
  * (Philox4x64-10, key (seed, 0), counter (token_offset + t, e, 0, 0),
  * u = (top 53 bits of word 0 + 1/2) * 2^-53), temperature, top-k by z
  * (ties to the lower expert index), softmax in binary64.
+ * With router_hidden > 0 the logits come from the encoder's hidden layer
+ * (moe_router_encoder) instead of x.
  *   expert_ids [T][k] int32, gate_weights [T][k] float   (device, out)
  *   workspace  >= moe_router_workspace_size() bytes        (device, scratch)
  */
 moe_status moe_router(const moe_config *cfg, const void *x, const void *Wg, const float *router_bias,
-                      int32_t *expert_ids, float *gate_weights,
+                      const void *router_W_in, const float *router_b_in, int32_t *expert_ids, float *gate_weights,
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Router encoder stage (P3 §3.1 input encoder, §4.2 GeLU between the router's
+ * two linear layers), for cfg->router_hidden = d_r > 0:
+ *   hidden[t][j] = GeLU( sum_i W_in[j][i] x[t][i] + b_in[j] ),  j < d_r,
+ * accumulated in fp32 (MFMA for bf16), GeLU h * erfc(-h / sqrt 2) / 2 in fp32,
+ * stored in act_dtype (bf16: round to nearest even).
+ *   x [T][d], router_W_in [d_r][d] act_dtype; router_b_in [d_r] float or NULL (device, in)
+ *   hidden [T][d_r] act_dtype, 16-byte aligned                                (device, out)
+ *   workspace >= moe_router_workspace_size() bytes, 256-byte aligned          (device, scratch)
+ * MOE_ERR_INVALID_ARGUMENT when router_hidden == 0.
+ */
+moe_status moe_router_encoder(const moe_config *cfg, const void *x, const void *router_W_in,
+                              const float *router_b_in, void *hidden, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
 
 /*
  * Router statistics (P1 §3.2 router entropy; P3 §4.2 expert_load, the mean
@@ -192,7 +214,7 @@ moe_status moe_router(const moe_config *cfg, const void *x, const void *Wg, cons
  */
 moe_status moe_router_stats_workspace_size(const moe_config *cfg, size_t *bytes);
 moe_status moe_router_stats(const moe_config *cfg, const void *x, const void *Wg, const float *router_bias,
-                            int32_t *expert_ids, float *gate_weights, double *expert_fraction, double *mean_prob,
+                            const void *router_W_in, const float *router_b_in, int32_t *expert_ids, float *gate_weights, double *expert_fraction, double *mean_prob,
                             double *scalars, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*

@@ -47,7 +47,7 @@ WORKLOADS = {
                                           w=INT4_G128, bias=False, tau=0.5, gumbel=True),
 }
 
-TAGS = {"x": 1, "Wg": 2, "W1": 3, "W2": 4}
+TAGS = {"x": 1, "Wg": 2, "W1": 3, "W2": 4, "W_in": 5, "b_in": 6}
 _MASK = (1 << 64) - 1
 
 
@@ -110,12 +110,21 @@ def quantize_int4_g128(w):
 
 def generate_router(cfg, device="cpu", seed=0):
     """The router's inputs alone (the same tensors `generate` returns):
-    dict(x [T, d], Wg [d, E], bias [E] or None)."""
+    dict(x [T, d], Wg [d, E], bias [E] or None, W_in, b_in).  With
+    cfg["router_hidden"] = d_r > 0 (two-layer router): W_in [d_r, d] ~ N(0, 1/d)
+    in the activation dtype, b_in [d_r] fp32 ~ N(0, 0.1^2), and Wg [d_r, E]
+    ~ N(0, 1/d_r); otherwise W_in and b_in are None."""
     T, d, E, act = cfg["T"], cfg["d"], cfg["E"], cfg["act"]
+    d_r = cfg.get("router_hidden", 0)
     x = _store(_normal((T, d), 1.0, device, stream_seed(seed, TAGS["x"])), act)
-    Wg = _store(_normal((d, E), 1.0 / math.sqrt(d), device, stream_seed(seed, TAGS["Wg"])), act)
+    d_g = d_r if d_r else d
+    Wg = _store(_normal((d_g, E), 1.0 / math.sqrt(d_g), device, stream_seed(seed, TAGS["Wg"])), act)
     bias = router_bias(E).to(device) if cfg.get("bias") else None
-    return dict(x=x, Wg=Wg, bias=bias)
+    W_in = b_in = None
+    if d_r:
+        W_in = _store(_normal((d_r, d), 1.0 / math.sqrt(d), device, stream_seed(seed, TAGS["W_in"])), act)
+        b_in = _normal((d_r,), 0.1, device, stream_seed(seed, TAGS["b_in"])).float()
+    return dict(x=x, Wg=Wg, bias=bias, W_in=W_in, b_in=b_in)
 
 
 def generate(cfg, device="cpu", seed=0):

@@ -19,7 +19,7 @@ ACT_GELU, ACT_SILU, ACT_SWIGLU = 0, 1, 2
 
 EXPORTS = ("moe_workspace_size", "moe_router_workspace_size", "moe_forward", "moe_router", "moe_permute",
            "moe_grouped_gemm", "moe_combine", "moe_router_stats_workspace_size", "moe_router_stats",
-           "moe_status_string", "moe_last_hip_error")
+           "moe_router_encoder", "moe_status_string", "moe_last_hip_error")
 
 
 class MoeConfig(ctypes.Structure):
@@ -42,6 +42,7 @@ class MoeConfig(ctypes.Structure):
         ("gate_norm", ctypes.c_int32),
         ("noise_std", ctypes.c_float),
         ("expert_act", ctypes.c_int32),
+        ("router_hidden", ctypes.c_int32),
     ]
 
 
@@ -68,15 +69,17 @@ def load(path=LIB_PATH):
     CFG = ctypes.POINTER(MoeConfig)
     lib.moe_workspace_size.argtypes = [CFG, ctypes.POINTER(SZ)]
     lib.moe_router_workspace_size.argtypes = [CFG, ctypes.POINTER(SZ)]
-    lib.moe_forward.argtypes = [CFG, P, P, P, P, P, I64, P, P, I64, P, P, P, P, P, SZ, P]
-    lib.moe_router.argtypes = [CFG, P, P, P, P, P, P, SZ, P]
+    lib.moe_forward.argtypes = [CFG, P, P, P, P, P, P, P, I64, P, P, I64, P, P, P, P, P, SZ, P]
+    lib.moe_router.argtypes = [CFG, P, P, P, P, P, P, P, P, SZ, P]
+    lib.moe_router_encoder.argtypes = [CFG, P, P, P, P, P, SZ, P]
     lib.moe_permute.argtypes = [CFG, P, P, P, P, P, P]
     lib.moe_grouped_gemm.argtypes = [CFG, I32, P, P, P, P, P, I64, P, P]
     lib.moe_combine.argtypes = [CFG, P, P, P, P, P]
     lib.moe_router_stats_workspace_size.argtypes = [CFG, ctypes.POINTER(SZ)]
-    lib.moe_router_stats.argtypes = [CFG, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.moe_router_stats.argtypes = [CFG, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     for name in ("moe_workspace_size", "moe_router_workspace_size", "moe_forward", "moe_router", "moe_permute",
-                 "moe_grouped_gemm", "moe_combine", "moe_router_stats_workspace_size", "moe_router_stats"):
+                 "moe_grouped_gemm", "moe_combine", "moe_router_stats_workspace_size", "moe_router_stats",
+                 "moe_router_encoder"):
         getattr(lib, name).restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -92,9 +95,10 @@ def status_string(status):
 
 def config(T, d, d_ff, E, k, act_dtype, w_dtype, tau=1.0, use_gumbel=False, seed=0, token_offset=0,
            gemm_path=GEMM_AUTO, capacity_factor=0.0, capacity_policy=CAPACITY_DROP, gate_norm=0, noise_std=0.0,
-           expert_act=ACT_GELU):
+           expert_act=ACT_GELU, router_hidden=0):
     return MoeConfig(T, d, d_ff, E, k, act_dtype, w_dtype, tau, int(bool(use_gumbel)), seed, token_offset,
-                     gemm_path, 0, capacity_factor, capacity_policy, int(gate_norm), noise_std, expert_act)
+                     gemm_path, 0, capacity_factor, capacity_policy, int(gate_norm), noise_std, expert_act,
+                     router_hidden)
 
 
 def _ptr(t):
@@ -132,9 +136,9 @@ def moe_router_workspace_size(cfg):
 
 
 def moe_forward(cfg, x, Wg, bias, W1, W1_scales, W2, W2_scales, y, expert_ids, gate_weights, counts, workspace,
-                stream=None, W1_stride=None, W2_stride=None):
+                stream=None, W1_stride=None, W2_stride=None, W_in=None, b_in=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load().moe_forward(ctypes.byref(cfg), _ptr(x), _ptr(Wg), _ptr(bias),
+    st = load().moe_forward(ctypes.byref(cfg), _ptr(x), _ptr(Wg), _ptr(bias), _ptr(W_in), _ptr(b_in),
                             _ptr(W1), _ptr(W1_scales), W1_stride if W1_stride is not None else _expert_stride(W1),
                             _ptr(W2), _ptr(W2_scales), W2_stride if W2_stride is not None else _expert_stride(W2),
                             _ptr(y), _ptr(expert_ids), _ptr(gate_weights), _ptr(counts), _ptr(workspace), ws_bytes,
@@ -142,11 +146,18 @@ def moe_forward(cfg, x, Wg, bias, W1, W1_scales, W2, W2_scales, y, expert_ids, g
     _check(st, "moe_forward")
 
 
-def moe_router(cfg, x, Wg, bias, expert_ids, gate_weights, workspace, stream=None):
+def moe_router(cfg, x, Wg, bias, expert_ids, gate_weights, workspace, stream=None, W_in=None, b_in=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load().moe_router(ctypes.byref(cfg), _ptr(x), _ptr(Wg), _ptr(bias), _ptr(expert_ids), _ptr(gate_weights),
-                           _ptr(workspace), ws_bytes, _stream(stream))
+    st = load().moe_router(ctypes.byref(cfg), _ptr(x), _ptr(Wg), _ptr(bias), _ptr(W_in), _ptr(b_in),
+                           _ptr(expert_ids), _ptr(gate_weights), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "moe_router")
+
+
+def moe_router_encoder(cfg, x, W_in, b_in, hidden, workspace, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().moe_router_encoder(ctypes.byref(cfg), _ptr(x), _ptr(W_in), _ptr(b_in), _ptr(hidden),
+                                   _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "moe_router_encoder")
 
 
 def moe_router_stats_workspace_size(cfg):
@@ -156,9 +167,10 @@ def moe_router_stats_workspace_size(cfg):
 
 
 def moe_router_stats(cfg, x, Wg, bias, expert_ids, gate_weights, expert_fraction, mean_prob, scalars, workspace,
-                     stream=None):
+                     stream=None, W_in=None, b_in=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load().moe_router_stats(ctypes.byref(cfg), _ptr(x), _ptr(Wg), _ptr(bias), _ptr(expert_ids),
+    st = load().moe_router_stats(ctypes.byref(cfg), _ptr(x), _ptr(Wg), _ptr(bias), _ptr(W_in), _ptr(b_in),
+                                 _ptr(expert_ids),
                                  _ptr(gate_weights), _ptr(expert_fraction), _ptr(mean_prob), _ptr(scalars),
                                  _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "moe_router_stats")

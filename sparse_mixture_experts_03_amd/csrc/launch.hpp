@@ -87,6 +87,13 @@ hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream);  // BF16 /
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);   // BF16 weights
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t stream);     // F32 weights
 
+// --------------------------------------------------------- router encoder
+// offsets = {0, T} (one expert holding every row), by a kernel
+hipError_t launch_encoder_offsets(int32_t* offsets, int64_t T, hipStream_t stream);
+// h[T][d_r] (act dtype) = GeLU(pre + b_in), pre fp32 [T][d_r]; b_in may be null; d_r % 64 == 0
+hipError_t launch_encoder_act(const float* pre, const float* b_in, void* h, int64_t T, int d_r, int act_dtype,
+                              hipStream_t stream);
+
 // --------------------------------------------------------------- combine
 hipError_t launch_combine(const float* Y, const int32_t* pos, const float* gates, void* y, int64_t T, int64_t d,
                           int k, int act_dtype, hipStream_t stream);

@@ -1,5 +1,6 @@
 // C ABI of the MoE-layer forward: argument checks, workspace carve-up and the
 // stream-ordered launch sequence
+//   [router encoder: GEMM (one expert) -> GeLU]
 //   router (partial logits, finalize) -> permute -> GEMM1 (+GeLU) -> GEMM2 -> combine,
 // with capacity-limited dispatch
 //   router (+ z and p rows) -> permute -> capacity -> permute -> GEMM1 -> GEMM2 -> combine.
@@ -62,6 +63,8 @@ moe_status check_config(const moe_config* c) {
     // a rerouted or dropped slot has no renormalised gate defined
     if (c->gate_norm == 1 && c->capacity_factor > 0.0f) return MOE_ERR_UNSUPPORTED;
     if (c->expert_act < MOE_ACT_GELU || c->expert_act > MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARGUMENT;
+    if (c->router_hidden < 0 || c->router_hidden > kMaxDim || c->router_hidden % 64 != 0)
+        return MOE_ERR_INVALID_ARGUMENT;
     if (c->act_dtype != MOE_DTYPE_F32 && c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARGUMENT;
     if (c->w_dtype < MOE_DTYPE_F32 || c->w_dtype > MOE_DTYPE_INT4_G128) return MOE_ERR_INVALID_ARGUMENT;
     if (c->w_dtype == MOE_DTYPE_INT4_G128 && (c->d % 128 != 0 || c->d_ff % 128 != 0))
@@ -75,6 +78,7 @@ moe_status check_config(const moe_config* c) {
     const int64_t ab = c->act_dtype == MOE_DTYPE_F32 ? 4 : 2;
     const int64_t Tk = c->T * c->k;
     if (c->T * c->d * ab >= kMaxArrayBytes || Tk * c->d_ff * 4 >= kMaxArrayBytes || Tk * c->d * 4 >= kMaxArrayBytes ||
+        (int64_t)c->router_hidden * c->d * ab >= kMaxArrayBytes || c->T * c->router_hidden * 4 >= kMaxArrayBytes ||
         w1_rows(*c) * c->d * elem_bits(c->w_dtype) / 8 >= kMaxArrayBytes)
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
@@ -92,6 +96,32 @@ int64_t capacity_of(const moe_config& c) {
 // Capacity can change the routing only when it is below T.
 bool capacity_active(const moe_config& c) { return capacity_of(c) > 0 && capacity_of(c) < c.T; }
 
+// Router workspace: the partial logits of the (last) router layer, and with a
+// router encoder its one-expert offsets, fp32 pre-activations and hidden layer.
+struct RouterLayout {
+    size_t partial, enc_offsets, enc_pre, enc_h, total;
+};
+
+RouterLayout router_layout_of(const moe_config& c) {
+    RouterLayout R;
+    const int64_t d_in = c.router_hidden > 0 ? c.router_hidden : c.d;
+    size_t off = 0;
+    R.partial = off;
+    off = round_up(off + moe::router_plan(c.T, d_in, c.E).partial_bytes, 256);
+    R.enc_offsets = R.enc_pre = R.enc_h = 0;
+    if (c.router_hidden > 0) {
+        const size_t ab = c.act_dtype == MOE_DTYPE_F32 ? 4 : 2;
+        R.enc_offsets = off;
+        off += 256;
+        R.enc_pre = off;
+        off = round_up(off + sizeof(float) * (size_t)c.T * (size_t)c.router_hidden, 256);
+        R.enc_h = off;
+        off = round_up(off + ab * (size_t)c.T * (size_t)c.router_hidden, 256);
+    }
+    R.total = c.T == 0 ? 0 : off;
+    return R;
+}
+
 struct Layout {
     size_t partial, offsets, sorted_token, pos, H, Y, z_rows, prob_rows, total;
 };
@@ -101,8 +131,8 @@ Layout layout_of(const moe_config& c) {
     const size_t Tk = (size_t)c.T * (size_t)c.k;
     const size_t hbytes = c.w_dtype == MOE_DTYPE_F32 ? 4 : 2;
     size_t off = 0;
-    L.partial = off;
-    off = round_up(off + moe::router_plan(c.T, c.d, c.E).partial_bytes, 256);
+    L.partial = off;  // the router workspace
+    off = round_up(off + router_layout_of(c).total, 256);
     L.offsets = off;
     off = round_up(off + sizeof(int32_t) * (size_t)(c.E + 1), 256);
     L.sorted_token = off;
@@ -175,14 +205,56 @@ hipError_t run_gemm(const moe_config& c, int which, const void* A, const int32_t
     return moe::launch_gemm_tiled(g, stream);
 }
 
+// The router encoder's product W_in x as a grouped GEMM with one expert of T
+// rows (which == 2: no gather, fp32 out, N = d_r, K = d).
+moe_config encoder_gemm_config(const moe_config& c) {
+    moe_config g;
+    memset(&g, 0, sizeof g);
+    g.T = c.T;
+    g.d = c.router_hidden;  // GEMM2's N
+    g.d_ff = c.d;           // GEMM2's K
+    g.E = 1;
+    g.k = 1;
+    g.act_dtype = c.act_dtype;
+    g.w_dtype = c.act_dtype;
+    g.tau = 1.0f;
+    g.gemm_path = MOE_GEMM_AUTO;
+    return g;
+}
+
+// Two-layer router, first layer: h = GeLU(W_in x + b_in) into h_out (by
+// default the router workspace's hidden layer).
+hipError_t run_router_encoder(const moe_config& c, const void* x, const void* W_in, const float* b_in, char* rws,
+                              hipStream_t stream, void* h_out = nullptr) {
+    const RouterLayout R = router_layout_of(c);
+    int32_t* offsets = reinterpret_cast<int32_t*>(rws + R.enc_offsets);
+    float* pre = reinterpret_cast<float*>(rws + R.enc_pre);
+    hipError_t e = moe::launch_encoder_offsets(offsets, c.T, stream);
+    if (e != hipSuccess) return e;
+    const moe_config g = encoder_gemm_config(c);
+    const int64_t stride = (int64_t)c.router_hidden * c.d * (c.act_dtype == MOE_DTYPE_F32 ? 4 : 2);
+    e = run_gemm(g, 2, x, nullptr, offsets, W_in, nullptr, stride, pre, stream);
+    if (e != hipSuccess) return e;
+    return moe::launch_encoder_act(pre, b_in, h_out ? h_out : rws + R.enc_h, c.T, c.router_hidden, c.act_dtype,
+                                   stream);
+}
+
+bool encoder_args_ok(const moe_config& c, const void* W_in, const float* b_in) {
+    if (c.router_hidden == 0) return W_in == nullptr && b_in == nullptr;
+    return W_in && aligned(W_in, 16) && (!b_in || aligned(b_in, 4));
+}
+
+// Router arguments on the workspace `rws` (router_layout_of): with an encoder
+// the router reads the hidden layer it wrote, with d = router_hidden.
 moe::RouterArgs router_args(const moe_config& c, const void* x, const void* Wg, const float* bias, int32_t* ids,
-                            float* gates, void* partial) {
+                            float* gates, void* rws) {
     moe::RouterArgs r;
-    r.x = x;
+    const RouterLayout R = router_layout_of(c);
+    r.x = c.router_hidden > 0 ? static_cast<const void*>(static_cast<char*>(rws) + R.enc_h) : x;
     r.Wg = Wg;
     r.bias = bias;
     r.T = c.T;
-    r.d = c.d;
+    r.d = c.router_hidden > 0 ? c.router_hidden : c.d;
     r.E = c.E;
     r.k = c.k;
     r.act_dtype = c.act_dtype;
@@ -192,10 +264,20 @@ moe::RouterArgs router_args(const moe_config& c, const void* x, const void* Wg, 
     r.gate_norm = c.gate_norm;
     r.seed = c.seed;
     r.token_offset = c.token_offset;
-    r.partial = static_cast<double*>(partial);
+    r.partial = reinterpret_cast<double*>(static_cast<char*>(rws) + R.partial);
     r.ids = ids;
     r.gates = gates;
     return r;
+}
+
+// The whole router: the encoder when configured, then partial logits and finalize.
+hipError_t run_router(const moe_config& c, const void* x, const void* W_in, const float* b_in,
+                      const moe::RouterArgs& r, char* rws, hipStream_t stream) {
+    if (c.router_hidden > 0) {
+        hipError_t e = run_router_encoder(c, x, W_in, b_in, rws, stream);
+        if (e != hipSuccess) return e;
+    }
+    return moe::launch_router(r, stream);
 }
 
 }  // namespace
@@ -214,12 +296,12 @@ moe_status moe_router_workspace_size(const moe_config* cfg, size_t* bytes) {
     moe_status s = check_config(cfg);
     if (s != MOE_OK) return s;
     if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
-    *bytes = cfg->T == 0 ? 0 : round_up(moe::router_plan(cfg->T, cfg->d, cfg->E).partial_bytes, 256);
+    *bytes = router_layout_of(*cfg).total;
     return MOE_OK;
 }
 
 moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, const float* router_bias,
-                       const void* W1, const void* W1_scales, int64_t W1_expert_stride, const void* W2,
+                       const void* router_W_in, const float* router_b_in, const void* W1, const void* W1_scales, int64_t W1_expert_stride, const void* W2,
                        const void* W2_scales, int64_t W2_expert_stride, void* y, int32_t* expert_ids,
                        float* gate_weights, int32_t* counts, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
@@ -235,6 +317,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
     if (!expert_ids || !aligned(expert_ids, 4) || !gate_weights || !aligned(gate_weights, 4))
         return MOE_ERR_INVALID_ARGUMENT;
     if (router_bias && !aligned(router_bias, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    if (!encoder_args_ok(c, router_W_in, router_b_in)) return MOE_ERR_INVALID_ARGUMENT;
     if ((s = check_weights(c, W1, W1_scales, W1_expert_stride, w1_rows(c), c.d)) != MOE_OK) return s;
     if ((s = check_weights(c, W2, W2_scales, W2_expert_stride, c.d, c.d_ff)) != MOE_OK) return s;
     const Layout L = layout_of(c);
@@ -254,7 +337,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
         r.z_rows = reinterpret_cast<double*>(ws + L.z_rows);
         r.prob_rows = reinterpret_cast<double*>(ws + L.prob_rows);
     }
-    hipError_t e = moe::launch_router(r, stream);
+    hipError_t e = run_router(c, x, router_W_in, router_b_in, r, ws + L.partial, stream);
     if (e != hipSuccess) return hip_fail(e);
     e = moe::launch_permute(expert_ids, c.T, c.E, c.k, counts, offsets, sorted_token, pos, stream);
     if (e != hipSuccess) return hip_fail(e);
@@ -276,8 +359,8 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
 }
 
 moe_status moe_router(const moe_config* cfg, const void* x, const void* Wg, const float* router_bias,
-                      int32_t* expert_ids, float* gate_weights, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream) {
+                      const void* router_W_in, const float* router_b_in, int32_t* expert_ids, float* gate_weights,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
     moe_status s = check_config(cfg);
     if (s != MOE_OK) return s;
     const moe_config& c = *cfg;
@@ -286,10 +369,30 @@ moe_status moe_router(const moe_config* cfg, const void* x, const void* Wg, cons
     if (!expert_ids || !aligned(expert_ids, 4) || !gate_weights || !aligned(gate_weights, 4))
         return MOE_ERR_INVALID_ARGUMENT;
     if (router_bias && !aligned(router_bias, 4)) return MOE_ERR_INVALID_ARGUMENT;
-    const size_t need = round_up(moe::router_plan(c.T, c.d, c.E).partial_bytes, 256);
+    if (!encoder_args_ok(c, router_W_in, router_b_in)) return MOE_ERR_INVALID_ARGUMENT;
     if (!workspace || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
-    if (workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
-    hipError_t e = moe::launch_router(router_args(c, x, Wg, router_bias, expert_ids, gate_weights, workspace), stream);
+    if (workspace_bytes < router_layout_of(c).total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    char* rws = static_cast<char*>(workspace);
+    hipError_t e = run_router(c, x, router_W_in, router_b_in,
+                              router_args(c, x, Wg, router_bias, expert_ids, gate_weights, rws), rws, stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+moe_status moe_router_encoder(const moe_config* cfg, const void* x, const void* router_W_in,
+                              const float* router_b_in, void* hidden, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    const moe_config& c = *cfg;
+    if (c.router_hidden == 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (c.T == 0) return MOE_OK;
+    if (!x || !aligned(x, 16) || !hidden || !aligned(hidden, 16)) return MOE_ERR_INVALID_ARGUMENT;
+    if (!encoder_args_ok(c, router_W_in, router_b_in)) return MOE_ERR_INVALID_ARGUMENT;
+    if (!workspace || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+    const RouterLayout R = router_layout_of(c);
+    if (workspace_bytes < R.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    char* rws = static_cast<char*>(workspace);
+    hipError_t e = run_router_encoder(c, x, router_W_in, router_b_in, rws, stream, hidden);
     return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
@@ -301,8 +404,8 @@ struct StatsLayout {
 StatsLayout stats_layout_of(const moe_config& c) {
     StatsLayout L;
     size_t off = 0;
-    L.partial = off;
-    off = round_up(off + moe::router_plan(c.T, c.d, c.E).partial_bytes, 256);
+    L.partial = off;  // the router workspace
+    off = round_up(off + router_layout_of(c).total, 256);
     L.prob_rows = off;
     off = round_up(off + sizeof(double) * (size_t)c.T * (size_t)c.E, 256);
     L.entropy_rows = off;
@@ -322,7 +425,7 @@ moe_status moe_router_stats_workspace_size(const moe_config* cfg, size_t* bytes)
 }
 
 moe_status moe_router_stats(const moe_config* cfg, const void* x, const void* Wg, const float* router_bias,
-                            int32_t* expert_ids, float* gate_weights, double* expert_fraction, double* mean_prob,
+                            const void* router_W_in, const float* router_b_in, int32_t* expert_ids, float* gate_weights, double* expert_fraction, double* mean_prob,
                             double* scalars, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     moe_status s = check_config(cfg);
     if (s != MOE_OK) return s;
@@ -338,6 +441,7 @@ moe_status moe_router_stats(const moe_config* cfg, const void* x, const void* Wg
     if (!expert_ids || !aligned(expert_ids, 4) || !gate_weights || !aligned(gate_weights, 4))
         return MOE_ERR_INVALID_ARGUMENT;
     if (router_bias && !aligned(router_bias, 4)) return MOE_ERR_INVALID_ARGUMENT;
+    if (!encoder_args_ok(c, router_W_in, router_b_in)) return MOE_ERR_INVALID_ARGUMENT;
     const StatsLayout L = stats_layout_of(c);
     if (!workspace || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
@@ -345,7 +449,7 @@ moe_status moe_router_stats(const moe_config* cfg, const void* x, const void* Wg
     moe::RouterArgs r = router_args(c, x, Wg, router_bias, expert_ids, gate_weights, ws + L.partial);
     r.prob_rows = reinterpret_cast<double*>(ws + L.prob_rows);
     r.entropy_rows = reinterpret_cast<double*>(ws + L.entropy_rows);
-    hipError_t e = moe::launch_router(r, stream);
+    hipError_t e = run_router(c, x, router_W_in, router_b_in, r, ws + L.partial, stream);
     if (e != hipSuccess) return hip_fail(e);
     e = moe::launch_router_stats(r.prob_rows, r.entropy_rows, expert_ids, c.T, c.E, c.k, ws + L.scratch,
                                  expert_fraction, mean_prob, scalars, stream);

@@ -31,20 +31,25 @@ def abi_config(cfg, gemm_path=moe.GEMM_AUTO, seed=0, token_offset=0):
     return moe.config(cfg["T"], cfg["d"], cfg["d_ff"], cfg["E"], cfg["k"], cfg["act"], cfg["w"], tau=cfg["tau"],
                       use_gumbel=cfg["gumbel"], seed=seed, token_offset=token_offset, gemm_path=gemm_path,
                       gate_norm=cfg.get("gate_norm", 0), noise_std=cfg.get("noise", 0.0),
-                      expert_act=cfg.get("ffn", 0))
+                      expert_act=cfg.get("ffn", 0), router_hidden=cfg.get("router_hidden", 0))
 
 
 def run_forward(cfg, inp, gemm_path=moe.GEMM_AUTO, noise_seed=0, token_offset=0, device="cuda"):
     c = abi_config(cfg, gemm_path, noise_seed, token_offset)
     layer = moe.MoELayerForward(c, device=device)
-    y, ids, gates, counts = layer(inp["x"], inp["Wg"], inp["bias"], inp["W1"], inp["W2"], inp["S1"], inp["S2"])
+    y, ids, gates, counts = layer(inp["x"], inp["Wg"], inp["bias"], inp["W1"], inp["W2"], inp["S1"], inp["S2"],
+                                  W_in=inp.get("W_in"), b_in=inp.get("b_in"))
     torch.cuda.synchronize()
     return dict(y=y, ids=ids, gates=gates, counts=counts, layer=layer)
 
 
 def oracle_route(orc, cfg, inp, noise_seed=0, token_offset=0):
     bias = None if inp["bias"] is None else inp["bias"].cpu().numpy()
+    enc = None
+    if inp.get("W_in") is not None:
+        enc = (moe_synth.to_bits(inp["W_in"]), None if inp["b_in"] is None else inp["b_in"].cpu().numpy())
     return orc.route(moe_synth.to_bits(inp["x"]), moe_synth.to_bits(inp["Wg"]), cfg["k"], cfg["act"], bias=bias,
+                     encoder=enc,
                      tau=tau32(cfg["tau"]), use_gumbel=cfg["gumbel"], seed=noise_seed, token_offset=token_offset,
                      want_zp=True, noise_std=tau32(cfg.get("noise", 0.0)), gate_norm=cfg.get("gate_norm", 0))
 

@@ -64,7 +64,7 @@ def _cfg(**kw):
     base.update(kw)
     c = moe.config(base["T"], base["d"], base["d_ff"], base["E"], base["k"], base["act_dtype"], base["w_dtype"])
     for key in ("tau", "use_gumbel", "gemm_path", "reserved", "capacity_factor", "capacity_policy", "gate_norm",
-                "noise_std", "expert_act"):
+                "noise_std", "expert_act", "router_hidden"):
         if key in kw:
             setattr(c, key, kw[key])
     return c
@@ -79,7 +79,8 @@ BAD = [
     dict(capacity_factor=-0.0 - 1e-30), dict(capacity_policy=2), dict(capacity_policy=-1),
     dict(capacity_factor=1.25, capacity_policy=7),
     dict(gate_norm=2), dict(gate_norm=-1), dict(noise_std=-0.1), dict(noise_std=float("nan")),
-    dict(noise_std=float("inf")), dict(expert_act=3), dict(expert_act=-1),
+    dict(noise_std=float("inf")), dict(expert_act=3), dict(expert_act=-1), dict(router_hidden=-64),
+    dict(router_hidden=100), dict(router_hidden=1 << 18),
 ]
 
 
@@ -162,10 +163,12 @@ def test_capacity_workspace(lib):
 
 def _forward(lib, c, **ptr):
     P = ctypes.c_void_p
-    a = dict(x=0x10000, Wg=0x20000, bias=None, W1=0x30000, S1=None, s1=c.d * c.d_ff * 2, W2=0x40000, S2=None,
-             s2=c.d * c.d_ff * 2, y=0x50000, ids=0x60000, gates=0x70000, counts=0x80000, ws=0x90000, wsb=1 << 40)
+    a = dict(x=0x10000, Wg=0x20000, bias=None, W_in=None, b_in=None, W1=0x30000, S1=None, s1=c.d * c.d_ff * 2,
+             W2=0x40000, S2=None, s2=c.d * c.d_ff * 2, y=0x50000, ids=0x60000, gates=0x70000, counts=0x80000,
+             ws=0x90000, wsb=1 << 40)
     a.update(ptr)
-    return lib.moe_forward(ctypes.byref(c), P(a["x"]), P(a["Wg"]), P(a["bias"]), P(a["W1"]), P(a["S1"]), a["s1"],
+    return lib.moe_forward(ctypes.byref(c), P(a["x"]), P(a["Wg"]), P(a["bias"]), P(a["W_in"]), P(a["b_in"]),
+                           P(a["W1"]), P(a["S1"]), a["s1"],
                            P(a["W2"]), P(a["S2"]), a["s2"], P(a["y"]), P(a["ids"]), P(a["gates"]), P(a["counts"]),
                            P(a["ws"]), a["wsb"], P(0))
 
@@ -190,6 +193,22 @@ def test_swiglu_w1_holds_gate_and_up_rows(lib):
     assert _forward(lib, c, s1=2 * one, ws=0x90000, wsb=1024) == binding.MOE_ERR_WORKSPACE_TOO_SMALL
 
 
+def test_router_encoder_workspace(lib):
+    """A router encoder of width d_r adds its fp32 pre-activations and act-dtype
+    hidden layer [T][d_r] to the router workspace (and so to the layer's)."""
+    n0, n1, r0, r1 = (ctypes.c_size_t() for _ in range(4))
+    T = 512
+    base, enc = _cfg(T=T, d=1024), _cfg(T=T, d=1024, router_hidden=256)
+    assert lib.moe_router_workspace_size(ctypes.byref(base), ctypes.byref(r0)) == 0
+    assert lib.moe_router_workspace_size(ctypes.byref(enc), ctypes.byref(r1)) == 0
+    assert r1.value >= T * 256 * (4 + 2)
+    assert lib.moe_workspace_size(ctypes.byref(base), ctypes.byref(n0)) == 0
+    assert lib.moe_workspace_size(ctypes.byref(enc), ctypes.byref(n1)) == 0
+    assert n1.value >= n0.value - r0.value + r1.value - 256
+    assert _forward(lib, enc) == binding.MOE_ERR_INVALID_ARGUMENT            # no W_in
+    assert _forward(lib, enc, W_in=0xA0000, wsb=1024) == binding.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_int4_needs_scales(lib):
     c = _cfg(w_dtype=moe.INT4_G128)
     assert _forward(lib, c, s1=256 * 512 // 2, s2=256 * 512 // 2) == binding.MOE_ERR_INVALID_ARGUMENT
@@ -198,10 +217,22 @@ def test_int4_needs_scales(lib):
 def test_stage_entry_points_check_arguments(lib):
     P = ctypes.c_void_p
     c = _cfg()
-    assert lib.moe_router(ctypes.byref(c), P(0), P(0x1000), None, P(0x2000), P(0x3000), P(0x4000), 1 << 30,
-                          P(0)) == binding.MOE_ERR_INVALID_ARGUMENT
-    assert lib.moe_router(ctypes.byref(c), P(0x1000), P(0x1000), None, P(0x2000), P(0x3000), P(0x4000), 16,
-                          P(0)) == binding.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert lib.moe_router(ctypes.byref(c), P(0), P(0x1000), None, None, None, P(0x2000), P(0x3000), P(0x4000),
+                          1 << 30, P(0)) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_router(ctypes.byref(c), P(0x1000), P(0x1000), None, None, None, P(0x2000), P(0x3000), P(0x4000),
+                          16, P(0)) == binding.MOE_ERR_WORKSPACE_TOO_SMALL
+    # encoder weights without an encoder, and an encoder without weights
+    assert lib.moe_router(ctypes.byref(c), P(0x1000), P(0x1000), None, P(0x5000), None, P(0x2000), P(0x3000),
+                          P(0x4000), 1 << 30, P(0)) == binding.MOE_ERR_INVALID_ARGUMENT
+    ce = _cfg(router_hidden=64)
+    assert lib.moe_router(ctypes.byref(ce), P(0x1000), P(0x1000), None, None, None, P(0x2000), P(0x3000),
+                          P(0x4000), 1 << 30, P(0)) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_router_encoder(ctypes.byref(c), P(0x1000), P(0x5000), None, P(0x6000), P(0x4000), 1 << 30,
+                                  P(0)) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_router_encoder(ctypes.byref(ce), P(0x1000), P(0x5000), P(0x7002), P(0x6000), P(0x4000), 1 << 30,
+                                  P(0)) == binding.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_router_encoder(ctypes.byref(ce), P(0x1000), P(0x5000), None, P(0x6000), P(0x4000), 64,
+                                  P(0)) == binding.MOE_ERR_WORKSPACE_TOO_SMALL
     assert lib.moe_permute(ctypes.byref(c), P(0x1000), None, P(0x2000), P(0x3000), P(0x4000),
                            P(0)) == binding.MOE_ERR_INVALID_ARGUMENT
     assert lib.moe_grouped_gemm(ctypes.byref(c), 3, P(0x1000), P(0x1000), P(0x1000), P(0x1000), None, 1 << 20,
@@ -222,7 +253,8 @@ def test_router_stats_checks_arguments(lib):
 
     def call(**kw):
         a = dict(good, **kw)
-        return lib.moe_router_stats(ctypes.byref(c), P(a["x"]), P(a["Wg"]), None, P(a["ids"]), P(a["gates"]),
+        return lib.moe_router_stats(ctypes.byref(c), P(a["x"]), P(a["Wg"]), None, None, None, P(a["ids"]),
+                                    P(a["gates"]),
                                     P(a["frac"]), P(a["mp"]), P(a["sc"]), P(a["ws"]), kw.get("wsb", 1 << 30), P(0))
     for bad in (dict(frac=None), dict(mp=0x6004), dict(sc=None), dict(x=None), dict(ids=0x3002), dict(ws=0x10008)):
         assert call(**bad) == binding.MOE_ERR_INVALID_ARGUMENT, bad
