@@ -2,7 +2,7 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                 [--capacity-factor CF --capacity-policy drop|reroute] [--gate-norm] [--noise-std SIGMA]
-                [--expert-act gelu|silu|swiglu]
+                [--expert-act gelu|silu|swiglu] [--router-hidden D_R]
 
 One step = the whole layer (router, dispatch, W1 GEMM + GeLU, W2 GEMM,
 combine) over one batch of seeded synthetic input already resident in HBM.
@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--noise-std", type=float, default=0.0, help="sigma of Gaussian router-logit noise")
     ap.add_argument("--expert-act", choices=["gelu", "silu", "swiglu"], default="gelu",
                     help="expert activation (swiglu: W1 holds 2 d_ff gate/up rows)")
+    ap.add_argument("--router-hidden", type=int, default=0,
+                    help="width of the two-layer router's hidden layer (0: linear router; the pages use d/4)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy first (reference kernel for HBM byte counters)")
     return ap.parse_args()
@@ -90,6 +92,7 @@ def main():
     cfg = moe_synth.workload(args.workload)
     act_code = {"gelu": moe.ACT_GELU, "silu": moe.ACT_SILU, "swiglu": moe.ACT_SWIGLU}[args.expert_act]
     cfg["ffn"] = act_code
+    cfg["router_hidden"] = args.router_hidden
     T, d, d_ff, E, k = cfg["T"], cfg["d"], cfg["d_ff"], cfg["E"], cfg["k"]
     n1 = 2 * d_ff if act_code == moe.ACT_SWIGLU else d_ff  # W1 rows
     print(f"[bench] generating {args.workload} on {dev}", file=sys.stderr, flush=True)
@@ -98,7 +101,7 @@ def main():
     policy = moe.CAPACITY_REROUTE if args.capacity_policy == "reroute" else moe.CAPACITY_DROP
     c = moe.config(T, d, d_ff, E, k, cfg["act"], cfg["w"], tau=cfg["tau"], use_gumbel=cfg["gumbel"], seed=0,
                    capacity_factor=args.capacity_factor, capacity_policy=policy, gate_norm=int(args.gate_norm),
-                   noise_std=args.noise_std, expert_act=act_code)
+                   noise_std=args.noise_std, expert_act=act_code, router_hidden=args.router_hidden)
     layer = moe.MoELayerForward(c, device=dev)
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -107,7 +110,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    run = lambda: layer(inp["x"], inp["Wg"], inp["bias"], inp["W1"], inp["W2"], inp["S1"], inp["S2"])
+    run = lambda: layer(inp["x"], inp["Wg"], inp["bias"], inp["W1"], inp["W2"], inp["S1"], inp["S2"],
+                        W_in=inp["W_in"], b_in=inp["b_in"])
 
     for _ in range(args.warmup):
         run()
@@ -152,9 +156,11 @@ def main():
     mprob = torch.empty(E, dtype=torch.float64, device=dev)
     scal = torch.empty(5, dtype=torch.float64, device=dev)
     router_ms = time_on_stream(torch, stream, lambda: moe.moe_router(c, inp["x"], inp["Wg"], inp["bias"], r_ids,
-                                                                     r_gates, r_ws), reps)
+                                                                     r_gates, r_ws, W_in=inp["W_in"],
+                                                                     b_in=inp["b_in"]), reps)
     stats_ms = time_on_stream(torch, stream, lambda: moe.moe_router_stats(c, inp["x"], inp["Wg"], inp["bias"], r_ids,
-                                                                          r_gates, frac, mprob, scal, s_ws), reps)
+                                                                          r_gates, frac, mprob, scal, s_ws,
+                                                                          W_in=inp["W_in"], b_in=inp["b_in"]), reps)
     if cfg["w"] == moe.F32:
         path = "f32"
     elif T <= 16 or (cfg["w"] == moe.INT4_G128 and (d % 1024 or d_ff % 1024)):
@@ -180,7 +186,9 @@ def main():
     roof.update(kernel=kernel_name, avg_launch_ms=round(gemm_ms, 4),
                 algorithmic_bytes=gemm_bytes, algorithmic_flops=gemm_flops)
 
-    step_bytes = (T * d * abytes + d * E * abytes + active * (w1_bytes + w_bytes) + T * d * abytes + T * k * 8 + E * 4)
+    d_r = args.router_hidden
+    router_w_bytes = (d_r * d * abytes + d_r * E * abytes) if d_r else d * E * abytes
+    step_bytes = (T * d * abytes + router_w_bytes + active * (w1_bytes + w_bytes) + T * d * abytes + T * k * 8 + E * 4)
     out = {
         "metric": "MoE-layer tokens/s",
         "value": round(tokens_per_s, 1),
@@ -198,7 +206,8 @@ def main():
                    "router_bias": bool(cfg["bias"]), "tau": cfg["tau"], "gumbel": bool(cfg["gumbel"]),
                    "capacity_factor": args.capacity_factor,
                    "capacity_policy": args.capacity_policy if args.capacity_factor > 0 else None,
-                   "gate_norm": int(args.gate_norm), "noise_std": args.noise_std, "expert_act": args.expert_act},
+                   "gate_norm": int(args.gate_norm), "noise_std": args.noise_std, "expert_act": args.expert_act,
+                   "router_hidden": args.router_hidden},
         "layer_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "layer_mfma_frac": round((gemm_flops + 2.0 * Tk * d * d_ff) / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "active_experts": active,
@@ -246,7 +255,10 @@ def cpu_baseline(cfg, inp, layer, args):
     tokens = np.unique(tokens)
     t0 = time.perf_counter()
     limited = args.capacity_factor > 0
-    ref = orc.route(xb, wgb, cfg["k"], cfg["act"], bias=bias, tau=float(np.float32(cfg["tau"])),
+    enc = None
+    if inp["W_in"] is not None:
+        enc = (moe_synth.to_bits(inp["W_in"]), inp["b_in"].cpu().numpy())
+    ref = orc.route(xb, wgb, cfg["k"], cfg["act"], bias=bias, tau=float(np.float32(cfg["tau"])), encoder=enc,
                     use_gumbel=cfg["gumbel"], seed=0, want_zp=limited, gate_norm=int(args.gate_norm),
                     noise_std=float(np.float32(args.noise_std)))
     if limited:
