@@ -52,10 +52,16 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash():
+KERNEL_SOURCES = {"f32": "gemm_f32.hip", "streaming": "gemm_stream.hip", "tiled": "gemm_tiled.hip"}
+
+
+def kernel_source_hash(kernel):
+    """Hash of the sources that define a W1 GEMM kernel: its own file, the
+    shared headers and the launch parameters chosen in moe_api.hip."""
     csrc = os.path.join(ROOT, "sparse_mixture_experts_03_amd", "csrc")
+    path = kernel.rsplit("_", 1)[-1]
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
+    for f in ("common.hpp", "launch.hpp", "moe_api.hip", KERNEL_SOURCES[path]):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -70,7 +76,7 @@ def load_traffic(workload, kernel):
     with open(path) as f:
         table = json.load(f)
     rec = table.get(f"{kernel}|{workload}")
-    if not rec or rec.get("source_hash") != kernel_source_hash():
+    if not rec or rec.get("source_hash") != kernel_source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 
