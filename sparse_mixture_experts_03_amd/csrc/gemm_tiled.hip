@@ -23,6 +23,8 @@
 // The m-tiles of all experts are numbered expert-major and located from the
 // offsets on the device, so skewed loads (0 .. thousands of rows per expert)
 // need no host round trip; tiles past the last real one exit at once.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -480,11 +482,14 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
 // `row` sits at byte row * 128 + 16 * (seg ^ ((row >> 1) & 7)) of a stage.
 
 template <int WHICH, int TI, int TJ, int XROWS, int ACT>
-__device__ __forceinline__ void tile_gemm_bf16_bk64(uint8_t* Wl, uint8_t* Xl, const uint16_t* __restrict__ A,
+__device__ __forceinline__ void tile_gemm_bf16_bk64(uint8_t* lds, const uint16_t* __restrict__ A,
                                                     const int32_t* __restrict__ a_rows, const void* Wexp,
                                                     void* __restrict__ out, int N, int K, int n0, int p0, int rows) {
     constexpr int WN_WAVES = 256 / (32 * TI);
     constexpr uint32_t kStage = 256 * 128;  // bytes per operand per stage
+    // LDS: two weight slots, then three dispatch-row slots (5 x 32 KB)
+    uint8_t* const Wr = lds;
+    uint8_t* const Xr = lds + 2 * kStage;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -508,17 +513,18 @@ __device__ __forceinline__ void tile_gemm_bf16_bk64(uint8_t* Wl, uint8_t* Xl, co
         const uint32_t arow = (WHICH == 1) ? (uint32_t)a_rows[p0 + drow] : (uint32_t)(p0 + drow);
         xoff[i] = arow * rowbytes + 16 * seg;
     }
-    auto issue_w = [&](int kt, int slot) {
+    auto issue_w = [&](int kt) {
         const uint32_t kb = (uint32_t)kt * 128;
+        uint8_t* slot = Wr + (kt & 1) * kStage;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) copy_rows_to_lds(wbase, woff[i] + kb, Wl + slot * kStage + (64 * wave + 8 * i) * 128);
+        for (int i = 0; i < 8; ++i) copy_rows_to_lds(wbase, woff[i] + kb, slot + (64 * wave + 8 * i) * 128);
     };
-    auto issue_x = [&](int kt, int slot) {
+    auto issue_x = [&](int kt) {
         const uint32_t kb = (uint32_t)kt * 128;
+        uint8_t* slot = Xr + (kt % 3) * kStage;
         if (xload) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                copy_rows_to_lds(xbase, xoff[i] + kb, Xl + slot * kStage + (64 * wave + 8 * i) * 128);
+            for (int i = 0; i < 8; ++i) copy_rows_to_lds(xbase, xoff[i] + kb, slot + (64 * wave + 8 * i) * 128);
         }
     };
 
@@ -540,65 +546,80 @@ __device__ __forceinline__ void tile_gemm_bf16_bk64(uint8_t* Wl, uint8_t* Xl, co
 #pragma unroll
     for (int j = 0; j < TJ; ++j) xrow_off[j] = (uint32_t)(wm + 32 * j + r) * 128;
     const uint32_t swz = (uint32_t)((r >> 1) & 7);
-    // two k-substeps: lane half h reads logical segments 2 ks + h, ks = 2 kp, 2 kp + 1
-    auto compute_pair = [&](uint32_t wb, uint32_t xb, int kp) {
-        const uint32_t sa = 16 * ((uint32_t)(4 * kp + h) ^ swz), sb = 16 * ((uint32_t)(4 * kp + 2 + h) ^ swz);
-        bf16x8 wf[2][TI], xf[2][TJ];
-#pragma unroll
-        for (int i = 0; i < TI; ++i) wf[0][i] = ds_read16(wb + wrow_off[i] + sa);
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) xf[0][j] = ds_read16(xb + xrow_off[j] + sa);
-#pragma unroll
-        for (int i = 0; i < TI; ++i) wf[1][i] = ds_read16(wb + wrow_off[i] + sb);
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) xf[1][j] = ds_read16(xb + xrow_off[j] + sb);
-        if constexpr (TI + TJ == 8) {
-            asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(wf[0][0]), "+v"(wf[0][1]), "+v"(wf[0][2]), "+v"(wf[0][3]),
-                         "+v"(xf[0][0]), "+v"(xf[0][1]), "+v"(xf[0][2]), "+v"(xf[0][3]));
-        } else if constexpr (TI + TJ == 6) {
-            asm volatile("s_waitcnt lgkmcnt(6)" : "+v"(wf[0][0]), "+v"(wf[0][1]), "+v"(xf[0][0]), "+v"(xf[0][1]),
-                         "+v"(xf[0][2]), "+v"(xf[0][3]));
-        } else {
-            asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(wf[0][0]), "+v"(wf[0][1]), "+v"(xf[0][0]), "+v"(xf[0][1]));
-        }
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-            for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32x32x16(wf[0][i], xf[0][j], acc[i][j]);
-        if constexpr (TI + TJ == 8) {
-            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(wf[1][0]), "+v"(wf[1][1]), "+v"(wf[1][2]), "+v"(wf[1][3]),
-                         "+v"(xf[1][0]), "+v"(xf[1][1]), "+v"(xf[1][2]), "+v"(xf[1][3]));
-        } else if constexpr (TI + TJ == 6) {
-            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(wf[1][0]), "+v"(wf[1][1]), "+v"(xf[1][0]), "+v"(xf[1][1]),
-                         "+v"(xf[1][2]), "+v"(xf[1][3]));
-        } else {
-            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(wf[1][0]), "+v"(wf[1][1]), "+v"(xf[1][0]), "+v"(xf[1][1]));
-        }
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-            for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32x32x16(wf[1][i], xf[1][j], acc[i][j]);
-    };
 
-    // Weight stages (three slots) are copied two stages ahead, dispatch-row
-    // stages (two slots; shared by the workgroups of one m-tile, mostly L2
-    // hits) one stage ahead, in the order W(0) X(0) W(1) | X(1) W(2) | X(2)
-    // W(3) | ...: at step k everything up to X(k) must have landed and only
-    // W(k+1) (8 loads) may still be in flight.  The barrier publishes stage k
-    // and frees the slots of stage k-1, which the step's copies then reuse.
+    // A stage is four k-substeps of 16; substep ks reads TI + TJ fragments,
+    // lane half h taking logical segment 2 ks + h of each row.
+    auto read_sub = [&](uint32_t wb, uint32_t xb, int ks, bf16x8 (&wf)[TI], bf16x8 (&xf)[TJ]) {
+        const uint32_t so = 16 * ((uint32_t)(2 * ks + h) ^ swz);
+#pragma unroll
+        for (int i = 0; i < TI; ++i) wf[i] = ds_read16(wb + wrow_off[i] + so);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) xf[j] = ds_read16(xb + xrow_off[j] + so);
+    };
+    auto mma_sub = [&](const bf16x8 (&wf)[TI], const bf16x8 (&xf)[TJ]) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32x32x16(wf[i], xf[j], acc[i][j]);
+    };
+    // wait until at most N fragment reads are outstanding; ties the fragments that must have landed
+    auto wait_frags = [&](auto nc, bf16x8 (&wf)[TI], bf16x8 (&xf)[TJ]) {
+        constexpr int N = decltype(nc)::value;
+        if constexpr (TI == 4 && TJ == 4)
+            asm volatile("s_waitcnt lgkmcnt(%8)" : "+v"(wf[0]), "+v"(wf[1]), "+v"(wf[2]), "+v"(wf[3]), "+v"(xf[0]),
+                         "+v"(xf[1]), "+v"(xf[2]), "+v"(xf[3]) : "n"(N));
+        else if constexpr (TI == 2 && TJ == 4)
+            asm volatile("s_waitcnt lgkmcnt(%6)" : "+v"(wf[0]), "+v"(wf[1]), "+v"(xf[0]), "+v"(xf[1]), "+v"(xf[2]),
+                         "+v"(xf[3]) : "n"(N));
+        else
+            asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(wf[0]), "+v"(wf[1]), "+v"(xf[0]), "+v"(xf[1]) : "n"(N));
+    };
+    using NF = std::integral_constant<int, TI + TJ>;
+    using N0 = std::integral_constant<int, 0>;
+
+    // Schedule (measured faster than copying right after the barrier):
+    // * weights (two slots) are copied one stage ahead, dispatch rows (three
+    //   slots, each stage's rows are new data for the XCD's L2) two ahead;
+    // * a step's copies are issued while its first fragment reads are in
+    //   flight (weights) or after its first half of MFMAs (dispatch rows), so
+    //   they do not delay the reads that start the step;
+    // * the last substep's MFMAs are held over the next barrier and issued
+    //   under the next stage's first reads, so the matrix pipe has queued
+    //   work across the stage boundary;
+    // * a scheduling fence after each first half stops the compiler from
+    //   hoisting the second fragment wait above those MFMAs.
+    // Issue order W(k+1) | X(k+2): at step k only X(k+1) (8 loads of the
+    // wavefronts that copy dispatch rows) may still be in flight.  The barrier
+    // publishes stage k and frees the slots of stage k-1 (W) and k-1 (X), which
+    // the step's copies reuse.
     const int nk = K / 64;
-    issue_w(0, 0);
-    issue_x(0, 0);
-    if (nk > 1) issue_w(1, 1);
+    issue_w(0);
+    issue_x(0);
+    if (nk > 1) issue_x(1);
+    bf16x8 dw[TI], dx[TJ];  // the held last substep of the previous stage
     for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) wait_vmcnt<8>(); else wait_vmcnt<0>();
+        if (kt + 1 < nk && xload) wait_vmcnt<8>(); else wait_vmcnt<0>();
         barrier();
-        if (kt + 1 < nk) issue_x(kt + 1, (kt + 1) & 1);
-        if (kt + 2 < nk) issue_w(kt + 2, (kt + 2) % 3);
-        const uint32_t wb = lds_addr(Wl + (kt % 3) * kStage), xb = lds_addr(Xl + (kt & 1) * kStage);
-        compute_pair(wb, xb, 0);
-        compute_pair(wb, xb, 1);
+        const uint32_t wb = lds_addr(Wr + (kt & 1) * kStage), xb = lds_addr(Xr + (kt % 3) * kStage);
+        bf16x8 w0[TI], x0[TJ], w1[TI], x1[TJ];
+        read_sub(wb, xb, 0, w0, x0);
+        read_sub(wb, xb, 1, w1, x1);
+        if (kt > 0) mma_sub(dw, dx);
+        if (kt + 1 < nk) issue_w(kt + 1);
+        wait_frags(NF{}, w0, x0);
+        mma_sub(w0, x0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_frags(N0{}, w1, x1);
+        mma_sub(w1, x1);
+        if (kt + 2 < nk) issue_x(kt + 2);
+        read_sub(wb, xb, 2, w0, x0);
+        read_sub(wb, xb, 3, dw, dx);
+        wait_frags(NF{}, w0, x0);
+        mma_sub(w0, x0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_frags(N0{}, dw, dx);
     }
+    mma_sub(dw, dx);
     store_tile<WHICH, TI, TJ, ACT>(acc, out, N, n0, p0, rows, wn, wm, r, h);
 }
 
@@ -610,7 +631,7 @@ __global__ void __launch_bounds__(256, 1)
 gemm_tiled_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
                   const int32_t* __restrict__ offsets, int E, const uint8_t* __restrict__ W, int64_t W_stride,
                   const uint16_t* __restrict__ Wsc, void* __restrict__ out, int N, int K, int ntiles_n, int rows_lo) {
-    // bf16: 3 weight + 2 dispatch-row stages of 32 KB (160 KB, all of a CU's LDS).
+    // bf16: 2 weight + 3 dispatch-row stages of 32 KB (160 KB, all of a CU's LDS).
     // INT4: 4 + 4 stages of 16 KB, the code ring (4 x 4 KB) and the scale ring (2 x 4 KB).
     constexpr int kLdsBytes = WQ == kBF16 ? 5 * 32768 : 2 * kStages * kTileBytes + kStages * 4096 + 2 * 4096;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
@@ -641,11 +662,11 @@ gemm_tiled_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_
     const void* Wsc_e = (WQ == kINT4) ? (const void*)(Wsc + (int64_t)e * N * (K / 128)) : nullptr;
     if constexpr (WQ == kBF16) {
         if (rows > 128)
-            tile_gemm_bf16_bk64<WHICH, 4, 4, 256, ACT>(smem, smem + 3 * 32768, A, a_rows, Wexp, out, N, K, n0, p0, rows);
+            tile_gemm_bf16_bk64<WHICH, 4, 4, 256, ACT>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows);
         else if (rows > 64)
-            tile_gemm_bf16_bk64<WHICH, 2, 4, 128, ACT>(smem, smem + 3 * 32768, A, a_rows, Wexp, out, N, K, n0, p0, rows);
+            tile_gemm_bf16_bk64<WHICH, 2, 4, 128, ACT>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows);
         else
-            tile_gemm_bf16_bk64<WHICH, 2, 2, 64, ACT>(smem, smem + 3 * 32768, A, a_rows, Wexp, out, N, K, n0, p0, rows);
+            tile_gemm_bf16_bk64<WHICH, 2, 2, 64, ACT>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows);
         return;
     }
     if (rows > 128)
