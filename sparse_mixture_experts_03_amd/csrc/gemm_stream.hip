@@ -143,7 +143,9 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
     const int g = lane >> 4;
     const int n0 = nt * ROWS;
     // dispatch row 16 c + r of the tile feeds MFMA column tile c; lanes past
-    // the tile's rows load nothing (at decode sizes most of them)
+    // the tile's rows load nothing (at decode sizes most of them); with INT4
+    // experts they read the tile's first row instead of branching around
+    // their loads (rows >= 1 in every tile; those output columns are never stored)
     bool mvalid[MT];
     const uint16_t* xrow[MT];
 #pragma unroll
@@ -152,8 +154,10 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
         mvalid[c] = m < rows;
         int64_t arow = 0;
         if (mvalid[c]) arow = (WHICH == 1) ? (int64_t)a_rows[p0 + m] : (int64_t)(p0 + m);
+        else if (WQ == kINT4) arow = (WHICH == 1) ? (int64_t)a_rows[p0] : (int64_t)p0;
         xrow[c] = A + arow * K;
     }
+    const bool xall = WQ == kINT4;
     const int64_t row_bytes = (WQ == kBF16) ? (int64_t)K * 2 : (int64_t)K / 2;
     const uint8_t* Wblk = W + (int64_t)e * W_stride + (int64_t)n0 * row_bytes;
     uint8_t* lds = stage_lds[wave];
@@ -167,6 +171,15 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
     auto gload = [&](int st, uint4 (&buf)[LOADS]) {
         const int64_t s0 = (int64_t)st * kStageBytes;
         const int64_t valid = min((int64_t)kStageBytes, row_bytes - s0);
+        if (WQ == kINT4 && valid == kStageBytes) {  // every stage but a K tail: no per-load guards
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int flat = 64 * i + lane;
+                const int row = flat / SEGS, seg = flat % SEGS;
+                buf[i] = ldw16(Wblk + (int64_t)row * row_bytes + s0 + seg * 16);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int flat = 64 * i + lane;
@@ -255,7 +268,8 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
 #pragma unroll
                 for (int c = 0; c < MT; ++c)
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) xv[c][s] = mvalid[c] ? ld16(xrow[c] + grp * 128 + 32 * g + 8 * s) : zero4;
+                    for (int s = 0; s < 4; ++s)
+                        xv[c][s] = (xall || mvalid[c]) ? ld16(xrow[c] + grp * 128 + 32 * g + 8 * s) : zero4;
                 f32x4 t[NB][MT], sx[MT];
                 uint4 q[NB];
 #pragma unroll
