@@ -34,8 +34,8 @@ combine_kernel(const float* __restrict__ Y, const int32_t* __restrict__ pos, con
         *reinterpret_cast<float4*>(static_cast<float*>(y) + t * d + c) = acc;
     } else {
         uint2 packed;
-        packed.x = float_to_bf16_bits(acc.x) | (float_to_bf16_bits(acc.y) << 16);
-        packed.y = float_to_bf16_bits(acc.z) | (float_to_bf16_bits(acc.w) << 16);
+        packed.x = pack_bf16x2(acc.x, acc.y);
+        packed.y = pack_bf16x2(acc.z, acc.w);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + t * d + c) = packed;
     }
 }

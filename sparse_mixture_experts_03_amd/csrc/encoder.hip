@@ -40,8 +40,8 @@ encoder_act_kernel(const float* __restrict__ pre, const float* __restrict__ b_in
         reinterpret_cast<float4*>(h)[i] = make_float4(r[0], r[1], r[2], r[3]);
     } else {
         uint2 packed;
-        packed.x = float_to_bf16_bits(r[0]) | (float_to_bf16_bits(r[1]) << 16);
-        packed.y = float_to_bf16_bits(r[2]) | (float_to_bf16_bits(r[3]) << 16);
+        packed.x = pack_bf16x2(r[0], r[1]);
+        packed.y = pack_bf16x2(r[2], r[3]);
         reinterpret_cast<uint2*>(h)[i] = packed;
     }
 }

@@ -91,8 +91,8 @@ __device__ __forceinline__ void store_tile(void* out, int64_t N, int p0, int row
     const int n = n0 + 4 * (lane >> 4);
     if constexpr (WHICH == 1) {
         uint2 packed;
-        packed.x = float_to_bf16_bits(act_f(v[0], act)) | (float_to_bf16_bits(act_f(v[1], act)) << 16);
-        packed.y = float_to_bf16_bits(act_f(v[2], act)) | (float_to_bf16_bits(act_f(v[3], act)) << 16);
+        packed.x = pack_bf16x2(act_f(v[0], act), act_f(v[1], act));
+        packed.y = pack_bf16x2(act_f(v[2], act), act_f(v[3], act));
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (int64_t)(p0 + m) * N + n) = packed;
     } else {
         *reinterpret_cast<float4*>(static_cast<float*>(out) + (int64_t)(p0 + m) * N + n) =
@@ -107,8 +107,8 @@ __device__ __forceinline__ void store_swiglu(void* out, int64_t Nh, int p0, int 
     const int m = lane & 15;
     if (m >= rows) return;
     uint2 packed;
-    packed.x = float_to_bf16_bits(silu_f(g[0]) * u[0]) | (float_to_bf16_bits(silu_f(g[1]) * u[1]) << 16);
-    packed.y = float_to_bf16_bits(silu_f(g[2]) * u[2]) | (float_to_bf16_bits(silu_f(g[3]) * u[3]) << 16);
+    packed.x = pack_bf16x2(silu_f(g[0]) * u[0], silu_f(g[1]) * u[1]);
+    packed.y = pack_bf16x2(silu_f(g[2]) * u[2], silu_f(g[3]) * u[3]);
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (int64_t)(p0 + m) * Nh + u0 + 4 * (lane >> 4)) = packed;
 }
 

@@ -136,6 +136,43 @@ __device__ __forceinline__ void dequant_word_to_lds(uint32_t word, uint32_t sbit
 // GELU_ERF: GeLU through erff instead of the cheaper bf16-grade form.  The
 // INT4 kernel keeps it: its main loop holds nearly every register, and with
 // the other form the allocator spills inside the MFMA loop (measured 5x slower).
+// GEMM1 epilogue of the bf16 kernel, staged through LDS (free once the K loop
+// is done): each wavefront writes its activated bf16 tile into a private
+// padded region laid out [dispatch row][weight row], then reads it back in
+// 16-byte chunks, so every store instruction writes whole 128-byte lines of H
+// instead of 16-byte pieces of 32 rows.  Not for SwiGLU (two rows per unit).
+template <int TI, int TJ, int ACT>
+__device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[TI][TJ], uint8_t* lds, void* __restrict__ out,
+                                               int N, int n0, int p0, int rows, int wn, int wm, int r, int h) {
+    constexpr int NW = 32 * TI, MW = 32 * TJ;  // this wavefront's weight rows x dispatch rows
+    constexpr int STRIDE = NW * 2 + 16;        // padded LDS row in bytes (16-byte aligned)
+    static_assert(4 * MW * STRIDE <= 5 * 32768, "epilogue staging exceeds the kernel's LDS");
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    uint8_t* wl = lds + wave * (MW * STRIDE);
+    barrier();  // every wavefront has finished reading the last stage
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint2 packed;
+                packed.x = pack_bf16x2(act_f(acc[i][j][4 * q], ACT), act_f(acc[i][j][4 * q + 1], ACT));
+                packed.y = pack_bf16x2(act_f(acc[i][j][4 * q + 2], ACT), act_f(acc[i][j][4 * q + 3], ACT));
+                *reinterpret_cast<uint2*>(wl + (32 * j + r) * STRIDE + (32 * i + 8 * q + 4 * h) * 2) = packed;
+            }
+    constexpr int CH = NW * 2 / 16, RPI = 64 / CH;  // chunks per row, rows per instruction
+    const int cr = lane / CH, cc = lane % CH;
+    const int n = n0 + wn + cc * 8;  // N is a multiple of 8
+#pragma unroll
+    for (int k = 0; k < MW / RPI; ++k) {
+        const int ml = k * RPI + cr;
+        const uint4 v = *reinterpret_cast<const uint4*>(wl + ml * STRIDE + cc * 16);
+        if (wm + ml < rows && n < N)
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + (int64_t)(p0 + wm + ml) * N + n) = v;
+    }
+}
+
 template <int WHICH, int TI, int TJ, int ACT, bool GELU_ERF = false>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TI][TJ], void* __restrict__ out, int N, int n0, int p0,
                                            int rows, int wn, int wm, int r, int h) {
@@ -157,8 +194,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TI][TJ], void* __
 #pragma unroll
                     for (int c = 0; c < 4; ++c) hv[c] = silu_f(acc[i][j][4 * q + c]) * acc[i][j][4 * q + 8 + c];
                     uint2 packed;
-                    packed.x = float_to_bf16_bits(hv[0]) | (float_to_bf16_bits(hv[1]) << 16);
-                    packed.y = float_to_bf16_bits(hv[2]) | (float_to_bf16_bits(hv[3]) << 16);
+                    packed.x = pack_bf16x2(hv[0], hv[1]);
+                    packed.y = pack_bf16x2(hv[2], hv[3]);
                     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + orow + (nb >> 1) + 8 * q + 4 * h) =
                         packed;
                 }
@@ -193,8 +230,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TI][TJ], void* __
                         a2 = act_f(v2, ACT);
                         a3 = act_f(v3, ACT);
                     }
-                    packed.x = float_to_bf16_bits(a0) | (float_to_bf16_bits(a1) << 16);
-                    packed.y = float_to_bf16_bits(a2) | (float_to_bf16_bits(a3) << 16);
+                    packed.x = pack_bf16x2(a0, a1);
+                    packed.y = pack_bf16x2(a2, a3);
                     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + orow + n) = packed;
                 } else {
                     *reinterpret_cast<float4*>(static_cast<float*>(out) + orow + n) = make_float4(v0, v1, v2, v3);
@@ -620,7 +657,10 @@ __device__ __forceinline__ void tile_gemm_bf16_bk64(uint8_t* lds, const uint16_t
         wait_frags(N0{}, dw, dx);
     }
     mma_sub(dw, dx);
-    store_tile<WHICH, TI, TJ, ACT>(acc, out, N, n0, p0, rows, wn, wm, r, h);
+    if constexpr (WHICH == 1 && ACT != kActSwiglu)
+        store_tile_lds<TI, TJ, ACT>(acc, lds, out, N, n0, p0, rows, wn, wm, r, h);
+    else
+        store_tile<WHICH, TI, TJ, ACT>(acc, out, N, n0, p0, rows, wn, wm, r, h);
 }
 
 // W: the experts' weights, W_stride bytes apart (bf16 [N][K] or INT4 codes
