@@ -141,15 +141,17 @@ __device__ __forceinline__ void dequant_word_to_lds(uint32_t word, uint32_t sbit
 // padded region laid out [dispatch row][weight row], then reads it back in
 // 16-byte chunks, so every store instruction writes whole 128-byte lines of H
 // instead of 16-byte pieces of 32 rows.  Not for SwiGLU (two rows per unit).
-template <int TI, int TJ, int ACT>
+template <int TI, int TJ, int ACT, int NWAVE>
 __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[TI][TJ], uint8_t* lds, void* __restrict__ out,
-                                               int N, int n0, int p0, int rows, int wn, int wm, int r, int h) {
+                                               int N, int n0, int p0, int rows, int wn, int wm, int r, int h,
+                                               bool math) {
     constexpr int NW = 32 * TI, MW = 32 * TJ;  // this wavefront's weight rows x dispatch rows
     constexpr int STRIDE = NW * 2 + 16;        // padded LDS row in bytes (16-byte aligned)
-    static_assert(4 * MW * STRIDE <= 5 * 32768, "epilogue staging exceeds the kernel's LDS");
+    static_assert(NWAVE * MW * STRIDE <= 5 * 32768, "epilogue staging exceeds the kernel's LDS");
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     uint8_t* wl = lds + wave * (MW * STRIDE);
     barrier();  // every wavefront has finished reading the last stage
+    if (!math) return;
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
@@ -517,33 +519,54 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
 // so 16 consecutive rows read at one logical segment hit 16 distinct bank
 // groups.  Stage k is multiplied in four k-substeps of 16.  Logical segment seg of tile row
 // `row` sits at byte row * 128 + 16 * (seg ^ ((row >> 1) & 7)) of a stage.
-
-template <int WHICH, int TI, int TJ, int XROWS, int ACT>
-__device__ __forceinline__ void tile_gemm_bf16_bk64(uint8_t* lds, const uint16_t* __restrict__ A,
-                                                    const int32_t* __restrict__ a_rows, const void* Wexp,
-                                                    void* __restrict__ out, int N, int K, int n0, int p0, int rows) {
+//
+// Eight wavefronts per workgroup, two per SIMD, so one wavefront's MFMAs run
+// while the other waits on fragment reads, copies or the barrier (measured
+// 7-15% faster per 256-row tile than four wavefronts of 128 x 128).  With 256
+// dispatch rows each of the 8 computes 128 weight rows x 64 dispatch rows
+// (128 accumulators, about 220 registers in all); with 128 rows 64 x 64; with
+// 64 rows (weight-streaming tiles) only wavefronts 0-3 compute 64 x 64, which
+// measured faster than spreading such a tile over all 8.  All 8 copy: wavefront
+// w moves tile rows [32 w, 32 w + 32) of each operand.
+//
+// Schedule (measured faster than copying right after the barrier):
+// * weights (two slots) are copied one stage ahead, dispatch rows (three
+//   slots, each stage's rows are new data for the XCD's L2) two ahead;
+// * a step's copies are issued while its first fragment reads are in
+//   flight (weights) or after its first half of MFMAs (dispatch rows), so
+//   they do not delay the reads that start the step;
+// * the last substep's MFMAs are held over the next barrier and issued
+//   under the next stage's first reads, so the matrix pipe has queued
+//   work across the stage boundary;
+// * a scheduling fence after each first half stops the compiler from
+//   hoisting the second fragment wait above those MFMAs.
+// Issue order W(k+1) | X(k+2): at step k only X(k+1) (4 loads of the
+// wavefronts that copy dispatch rows) may still be in flight.  The barrier
+// publishes stage k and frees the slots of stage k-1 (W) and k-1 (X), which
+// the step's copies reuse.
+template <int WHICH, int TI, int TJ, int XROWS, int ACT, int MWAVE = 8>
+__device__ __forceinline__ void tile_gemm_bf16(uint8_t* lds, const uint16_t* __restrict__ A,
+                                               const int32_t* __restrict__ a_rows, const void* Wexp,
+                                               void* __restrict__ out, int N, int K, int n0, int p0, int rows) {
+    constexpr int NWAVE = 8;
     constexpr int WN_WAVES = 256 / (32 * TI);
-    constexpr uint32_t kStage = 256 * 128;  // bytes per operand per stage
-    // LDS: two weight slots, then three dispatch-row slots (5 x 32 KB)
+    static_assert(WN_WAVES * (XROWS / (32 * TJ)) == MWAVE, "wave grid");
+    const bool math = (threadIdx.x >> 6) < MWAVE;
+    constexpr uint32_t kStage = 256 * 128;
     uint8_t* const Wr = lds;
     uint8_t* const Xr = lds + 2 * kStage;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-    // This wavefront copies tile rows [64 w, 64 w + 64) of the weight tile,
-    // and of the dispatch tile if they lie inside XROWS: 8 instructions of 8
-    // rows x 128 bytes per operand.  Lane L of instruction i takes physical
-    // slot L % 8 of row 64 w + 8 i + L / 8.  Rows past N or past the tile's
-    // dispatch rows are clamped to a valid row (their outputs are not stored).
-    const bool xload = 64 * wave < XROWS;
+    // wavefront w copies tile rows [32 w, 32 w + 32): 4 instructions of 8 rows x 128 bytes per operand
+    const bool xload = 32 * wave < XROWS;
     const char* wbase = reinterpret_cast<const char*>(Wexp);
     const char* xbase = reinterpret_cast<const char*>(A);
     const uint32_t rowbytes = (uint32_t)K * 2;
-    uint32_t woff[8], xoff[8];
+    uint32_t woff[4], xoff[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int trow = 64 * wave + 8 * i + (lane >> 3);
+    for (int i = 0; i < 4; ++i) {
+        const int trow = 32 * wave + 8 * i + (lane >> 3);
         const uint32_t seg = (uint32_t)((lane & 7) ^ ((trow >> 1) & 7));
         woff[i] = (uint32_t)min(n0 + trow, N - 1) * rowbytes + 16 * seg;
         const int drow = min(trow, rows - 1);
@@ -554,17 +577,16 @@ __device__ __forceinline__ void tile_gemm_bf16_bk64(uint8_t* lds, const uint16_t
         const uint32_t kb = (uint32_t)kt * 128;
         uint8_t* slot = Wr + (kt & 1) * kStage;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) copy_rows_to_lds(wbase, woff[i] + kb, slot + (64 * wave + 8 * i) * 128);
+        for (int i = 0; i < 4; ++i) copy_rows_to_lds(wbase, woff[i] + kb, slot + (32 * wave + 8 * i) * 128);
     };
     auto issue_x = [&](int kt) {
         const uint32_t kb = (uint32_t)kt * 128;
         uint8_t* slot = Xr + (kt % 3) * kStage;
         if (xload) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) copy_rows_to_lds(xbase, xoff[i] + kb, slot + (64 * wave + 8 * i) * 128);
+            for (int i = 0; i < 4; ++i) copy_rows_to_lds(xbase, xoff[i] + kb, slot + (32 * wave + 8 * i) * 128);
         }
     };
-
     const int wn = (wave % WN_WAVES) * (32 * TI);
     const int wm = (wave / WN_WAVES) * (32 * TJ);
     const int r = lane & 31;
@@ -576,17 +598,14 @@ __device__ __forceinline__ void tile_gemm_bf16_bk64(uint8_t* lds, const uint16_t
         for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-    // every fragment row of this lane is r modulo 16, so one slot permutation serves all
     uint32_t wrow_off[TI], xrow_off[TJ];
 #pragma unroll
     for (int i = 0; i < TI; ++i) wrow_off[i] = (uint32_t)(wn + 32 * i + r) * 128;
 #pragma unroll
     for (int j = 0; j < TJ; ++j) xrow_off[j] = (uint32_t)(wm + 32 * j + r) * 128;
     const uint32_t swz = (uint32_t)((r >> 1) & 7);
-
-    // A stage is four k-substeps of 16; substep ks reads TI + TJ fragments,
-    // lane half h taking logical segment 2 ks + h of each row.
     auto read_sub = [&](uint32_t wb, uint32_t xb, int ks, bf16x8 (&wf)[TI], bf16x8 (&xf)[TJ]) {
+        if (MWAVE < 8 && !math) return;
         const uint32_t so = 16 * ((uint32_t)(2 * ks + h) ^ swz);
 #pragma unroll
         for (int i = 0; i < TI; ++i) wf[i] = ds_read16(wb + wrow_off[i] + so);
@@ -594,48 +613,30 @@ __device__ __forceinline__ void tile_gemm_bf16_bk64(uint8_t* lds, const uint16_t
         for (int j = 0; j < TJ; ++j) xf[j] = ds_read16(xb + xrow_off[j] + so);
     };
     auto mma_sub = [&](const bf16x8 (&wf)[TI], const bf16x8 (&xf)[TJ]) {
+        if (MWAVE < 8 && !math) return;
 #pragma unroll
         for (int i = 0; i < TI; ++i)
 #pragma unroll
             for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32x32x16(wf[i], xf[j], acc[i][j]);
     };
-    // wait until at most N fragment reads are outstanding; ties the fragments that must have landed
+    // wait until at most N fragment reads are outstanding, then tie the fragments to the wait
     auto wait_frags = [&](auto nc, bf16x8 (&wf)[TI], bf16x8 (&xf)[TJ]) {
-        constexpr int N = decltype(nc)::value;
-        if constexpr (TI == 4 && TJ == 4)
-            asm volatile("s_waitcnt lgkmcnt(%8)" : "+v"(wf[0]), "+v"(wf[1]), "+v"(wf[2]), "+v"(wf[3]), "+v"(xf[0]),
-                         "+v"(xf[1]), "+v"(xf[2]), "+v"(xf[3]) : "n"(N));
-        else if constexpr (TI == 2 && TJ == 4)
-            asm volatile("s_waitcnt lgkmcnt(%6)" : "+v"(wf[0]), "+v"(wf[1]), "+v"(xf[0]), "+v"(xf[1]), "+v"(xf[2]),
-                         "+v"(xf[3]) : "n"(N));
-        else
-            asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(wf[0]), "+v"(wf[1]), "+v"(xf[0]), "+v"(xf[1]) : "n"(N));
+        constexpr int NN = decltype(nc)::value;
+        asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(NN) : "memory");
+#pragma unroll
+        for (int i = 0; i < TI; ++i) asm volatile("" : "+v"(wf[i]));
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) asm volatile("" : "+v"(xf[j]));
     };
     using NF = std::integral_constant<int, TI + TJ>;
     using N0 = std::integral_constant<int, 0>;
-
-    // Schedule (measured faster than copying right after the barrier):
-    // * weights (two slots) are copied one stage ahead, dispatch rows (three
-    //   slots, each stage's rows are new data for the XCD's L2) two ahead;
-    // * a step's copies are issued while its first fragment reads are in
-    //   flight (weights) or after its first half of MFMAs (dispatch rows), so
-    //   they do not delay the reads that start the step;
-    // * the last substep's MFMAs are held over the next barrier and issued
-    //   under the next stage's first reads, so the matrix pipe has queued
-    //   work across the stage boundary;
-    // * a scheduling fence after each first half stops the compiler from
-    //   hoisting the second fragment wait above those MFMAs.
-    // Issue order W(k+1) | X(k+2): at step k only X(k+1) (8 loads of the
-    // wavefronts that copy dispatch rows) may still be in flight.  The barrier
-    // publishes stage k and frees the slots of stage k-1 (W) and k-1 (X), which
-    // the step's copies reuse.
     const int nk = K / 64;
     issue_w(0);
     issue_x(0);
     if (nk > 1) issue_x(1);
-    bf16x8 dw[TI], dx[TJ];  // the held last substep of the previous stage
+    bf16x8 dw[TI], dx[TJ];
     for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk && xload) wait_vmcnt<8>(); else wait_vmcnt<0>();
+        if (kt + 1 < nk && xload) wait_vmcnt<4>(); else wait_vmcnt<0>();
         barrier();
         const uint32_t wb = lds_addr(Wr + (kt & 1) * kStage), xb = lds_addr(Xr + (kt % 3) * kStage);
         bf16x8 w0[TI], x0[TJ], w1[TI], x1[TJ];
@@ -657,11 +658,13 @@ __device__ __forceinline__ void tile_gemm_bf16_bk64(uint8_t* lds, const uint16_t
         wait_frags(N0{}, dw, dx);
     }
     mma_sub(dw, dx);
-    if constexpr (WHICH == 1 && ACT != kActSwiglu)
-        store_tile_lds<TI, TJ, ACT>(acc, lds, out, N, n0, p0, rows, wn, wm, r, h);
-    else
-        store_tile<WHICH, TI, TJ, ACT>(acc, out, N, n0, p0, rows, wn, wm, r, h);
+    if constexpr (WHICH == 1 && ACT != kActSwiglu) {
+        store_tile_lds<TI, TJ, ACT, NWAVE>(acc, lds, out, N, n0, p0, rows, wn, wm, r, h, math);
+    } else {
+        if (math) store_tile<WHICH, TI, TJ, ACT>(acc, out, N, n0, p0, rows, wn, wm, r, h);
+    }
 }
+
 
 // W: the experts' weights, W_stride bytes apart (bf16 [N][K] or INT4 codes
 // [N][K/2]); Wsc: INT4 scales bf16 [E][N][K/128] (unused for bf16).  Only
@@ -671,9 +674,9 @@ __global__ void __launch_bounds__(256, 1)
 gemm_tiled_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
                   const int32_t* __restrict__ offsets, int E, const uint8_t* __restrict__ W, int64_t W_stride,
                   const uint16_t* __restrict__ Wsc, void* __restrict__ out, int N, int K, int ntiles_n, int rows_lo) {
-    // bf16: 2 weight + 3 dispatch-row stages of 32 KB (160 KB, all of a CU's LDS).
-    // INT4: 4 + 4 stages of 16 KB, the code ring (4 x 4 KB) and the scale ring (2 x 4 KB).
-    constexpr int kLdsBytes = WQ == kBF16 ? 5 * 32768 : 2 * kStages * kTileBytes + kStages * 4096 + 2 * 4096;
+    // 4 + 4 stages of 16 KB, the code ring (4 x 4 KB) and the scale ring (2 x 4 KB).
+    static_assert(WQ == kINT4, "bf16 experts use gemm_tiled_bf16_kernel");
+    constexpr int kLdsBytes = 2 * kStages * kTileBytes + kStages * 4096 + 2 * 4096;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
     uint8_t (*Wt)[kTileBytes] = reinterpret_cast<uint8_t (*)[kTileBytes]>(smem);
     uint8_t (*Xt)[kTileBytes] = reinterpret_cast<uint8_t (*)[kTileBytes]>(smem + kStages * kTileBytes);
@@ -700,21 +703,40 @@ gemm_tiled_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_
     const int n0 = nt * kTBN;
     const void* Wexp = W + (int64_t)e * W_stride;
     const void* Wsc_e = (WQ == kINT4) ? (const void*)(Wsc + (int64_t)e * N * (K / 128)) : nullptr;
-    if constexpr (WQ == kBF16) {
-        if (rows > 128)
-            tile_gemm_bf16_bk64<WHICH, 4, 4, 256, ACT>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows);
-        else if (rows > 64)
-            tile_gemm_bf16_bk64<WHICH, 2, 4, 128, ACT>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows);
-        else
-            tile_gemm_bf16_bk64<WHICH, 2, 2, 64, ACT>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows);
-        return;
-    }
     if (rows > 128)
         tile_gemm<WQ, WHICH, 4, 4, 256, ACT>(Wt, Xt, Ct, St, A, a_rows, Wexp, Wsc_e, out, N, K, n0, p0, rows);
     else if (rows > 64)
         tile_gemm<WQ, WHICH, 2, 4, 128, ACT>(Wt, Xt, Ct, St, A, a_rows, Wexp, Wsc_e, out, N, K, n0, p0, rows);
     else
         tile_gemm<WQ, WHICH, 2, 2, 64, ACT>(Wt, Xt, Ct, St, A, a_rows, Wexp, Wsc_e, out, N, K, n0, p0, rows);
+}
+
+// bf16 experts: 2 weight + 3 dispatch-row stages of 32 KB (160 KB, all of a
+// CU's LDS), 8 wavefronts.
+template <int WHICH, int ACT>
+__global__ void __launch_bounds__(512, 1)
+gemm_tiled_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
+                       const int32_t* __restrict__ offsets, int E, const uint8_t* __restrict__ W, int64_t W_stride,
+                       void* __restrict__ out, int N, int K, int ntiles_n, int rows_lo) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[5 * 32768];
+    asm volatile("" ::: "a0");  // accumulators in AGPRs (see gemm_tiled_kernel)
+    const MtileScan scan = scan_mtiles(offsets, E, kTBM, rows_lo, 0x7fffffff);
+    const int mt = blockIdx.x / ntiles_n;
+    const int nt = blockIdx.x - mt * ntiles_n;
+    if (mt >= scan.total) return;
+    int e, p0, rows;
+    lookup_mtile(scan, offsets, kTBM, mt, &e, &p0, &rows);
+    e = __builtin_amdgcn_readfirstlane(e);
+    p0 = __builtin_amdgcn_readfirstlane(p0);
+    rows = __builtin_amdgcn_readfirstlane(rows);
+    const int n0 = nt * kTBN;
+    const void* Wexp = W + (int64_t)e * W_stride;
+    if (rows > 128)
+        tile_gemm_bf16<WHICH, 4, 2, 256, ACT>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows);
+    else if (rows > 64)
+        tile_gemm_bf16<WHICH, 2, 2, 128, ACT>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows);
+    else
+        tile_gemm_bf16<WHICH, 2, 2, 64, ACT, 4>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows);
 }
 
 }  // namespace
@@ -740,10 +762,14 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
         else if (a.act == kActSwiglu) MOE_TILED_LAUNCH(kINT4, 1, kActSwiglu);
         else MOE_TILED_LAUNCH(kINT4, 1, kActGelu);
     } else {
-        if (a.which == 2) MOE_TILED_LAUNCH(kBF16, 2, kActGelu);
-        else if (a.act == kActSilu) MOE_TILED_LAUNCH(kBF16, 1, kActSilu);
-        else if (a.act == kActSwiglu) MOE_TILED_LAUNCH(kBF16, 1, kActSwiglu);
-        else MOE_TILED_LAUNCH(kBF16, 1, kActGelu);
+#define MOE_TILED_BF16_LAUNCH(WHICH_, ACT_)                                                                      \
+    hipLaunchKernelGGL((gemm_tiled_bf16_kernel<WHICH_, ACT_>), grid, dim3(512), 0, stream, A, a.a_rows, a.offsets, \
+                       a.E, W, a.W_stride, a.out, N, K, ntiles_n, a.rows_lo)
+        if (a.which == 2) MOE_TILED_BF16_LAUNCH(2, kActGelu);
+        else if (a.act == kActSilu) MOE_TILED_BF16_LAUNCH(1, kActSilu);
+        else if (a.act == kActSwiglu) MOE_TILED_BF16_LAUNCH(1, kActSwiglu);
+        else MOE_TILED_BF16_LAUNCH(1, kActGelu);
+#undef MOE_TILED_BF16_LAUNCH
     }
 #undef MOE_TILED_LAUNCH
     return hipGetLastError();
