@@ -115,6 +115,8 @@ FORWARD_CASES = {
     "bf16-T16-d512-dff1024-E8": (case(16, 512, 1024, 8), [moe.GEMM_STREAMING, moe.GEMM_TILED]),
     "bf16-T300-d512-dff1024-E8-skewed": (case(300, 512, 1024, 8, bias=True), [moe.GEMM_STREAMING, moe.GEMM_TILED]),
     "bf16-T150-d320-dff576-E6-ntail": (case(150, 320, 576, 6), [moe.GEMM_STREAMING, moe.GEMM_TILED]),
+    # N tails (576 = 2 x 256 + 64 for W1, 320 for W2) on every tiled tile height: 256-, 128- and 64-row tiles
+    "bf16-T300-d320-dff576-E8-skewed-ntail": (case(300, 320, 576, 8, bias=True), [moe.GEMM_TILED]),
     "bf16-T40-d256-dff256-E256-k8": (case(40, 256, 256, 256, k=8), [moe.GEMM_STREAMING, moe.GEMM_TILED]),
     "bf16-T9-d256-dff512-E1-k1": (case(9, 256, 512, 1, k=1), [moe.GEMM_STREAMING, moe.GEMM_TILED]),
     # streaming with 32-row (T <= 32) and 64-row dispatch tiles
