@@ -14,7 +14,9 @@ struct RouterPlan {
     int expert_groups;     // power of two >= E / 8: 8-expert groups per Wg row
     int rows_per_split;    // input rows (of d) per split
     int splits;            // workgroups along the input dimension (<= 64)
-    size_t partial_bytes;  // binary64 partial logits [splits][T][E]
+    // bf16 activations with T >= 64: the fp64-MFMA partial kernel and its split
+    int mfma_rows_per_split, mfma_splits;
+    size_t partial_bytes;  // binary64 partial logits [splits][T][E], enough for either kernel
 };
 RouterPlan router_plan(int64_t T, int64_t d, int E);
 

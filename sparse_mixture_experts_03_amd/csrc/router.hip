@@ -12,6 +12,8 @@
 // Logits accumulate in binary64 from exact products (bf16*bf16 and
 // fp32*fp32 are exact in binary64), so expert choices agree with a binary64
 // reference except at ties closer than the binary64 rounding of the sums.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -139,6 +141,95 @@ router_partial_kernel(const void* __restrict__ x, const void* __restrict__ Wg, i
         const double v = ((red[0][g][t * 8 + j] + red[1][g][t * 8 + j]) + red[2][g][t * 8 + j]) + red[3][g][t * 8 + j];
         partial[((int64_t)blockIdx.y * T + t0 + t) * E + e] = v;
     }
+}
+
+// Partial logits by fp64 MFMA, for bf16 activations at prefill sizes.  Each
+// wavefront owns TT x ET tiles of 16 tokens x 16 experts over one slice of
+// the input dimension, accumulated by v_mfma_f64_16x16x4 (binary64 products of
+// the exact bf16 inputs, binary64 sums).  In each 16x16x4 step lane group g
+// (lanes 16 g .. 16 g + 15) supplies input row kb + 8 g + j to both operands
+// (A: the lane's token, B: the lane's expert); the sum over k is the same
+// whatever row each group takes, and this choice lets a lane fetch its x
+// values for 32 rows with one 16-byte load.  Its Wg values are eight 2-byte
+// loads of L2-resident rows.  Loads run one 32-row chunk ahead.  Workgroup:
+// 4 wavefronts along tokens (ET = 1, E <= 16) or 2 x 2 (ET = 2).
+typedef double f64x4 __attribute__((__vector_size__(4 * sizeof(double))));
+constexpr int kMfmaMinTokens = 64;
+constexpr int kMfmaChunk = 32;  // input rows per loop step
+
+template <int TT, int ET>
+__global__ void __launch_bounds__(256)
+router_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wg, int T, int d, int E,
+                   int rows_per_split, double* __restrict__ partial) {
+    constexpr int WT = (ET == 1) ? 4 : 2;  // wavefronts along tokens
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int wt = wave % WT, we = wave / WT;
+    const int t0 = (blockIdx.x * WT + wt) * (16 * TT);
+    const int e0 = (blockIdx.y * (4 / WT) + we) * (16 * ET);
+    const int k_begin = blockIdx.z * rows_per_split;
+    const int k_end = min(d, k_begin + rows_per_split);
+    // rows past T or columns past E read a valid row / column; their outputs are not stored
+    const uint16_t* xr[TT];
+#pragma unroll
+    for (int ti = 0; ti < TT; ++ti) xr[ti] = x + (int64_t)min(t0 + 16 * ti + r, T - 1) * d + 8 * g;
+    const uint16_t* wc[ET];
+#pragma unroll
+    for (int ei = 0; ei < ET; ++ei) wc[ei] = Wg + (int64_t)(8 * g) * E + min(e0 + 16 * ei + r, E - 1);
+    f64x4 acc[TT][ET];
+#pragma unroll
+    for (int ti = 0; ti < TT; ++ti)
+#pragma unroll
+        for (int ei = 0; ei < ET; ++ei) acc[ti][ei] = (f64x4){0.0, 0.0, 0.0, 0.0};
+    uint4 xv[TT], xn[TT];
+    uint16_t wv[ET][8], wn[ET][8];
+    auto load = [&](int kb, uint4 (&xs)[TT], uint16_t (&ws)[ET][8]) {
+#pragma unroll
+        for (int ti = 0; ti < TT; ++ti) xs[ti] = *reinterpret_cast<const uint4*>(xr[ti] + kb);
+#pragma unroll
+        for (int ei = 0; ei < ET; ++ei)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ws[ei][j] = wc[ei][(int64_t)(kb + j) * E];
+    };
+    if (k_begin < k_end) load(k_begin, xv, wv);
+    for (int kb = k_begin; kb < k_end; kb += kMfmaChunk) {
+        if (kb + kMfmaChunk < k_end) load(kb + kMfmaChunk, xn, wn);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            double a[TT], b[ET];
+#pragma unroll
+            for (int ti = 0; ti < TT; ++ti) {
+                const uint32_t word = (j >> 1) == 0 ? xv[ti].x : (j >> 1) == 1 ? xv[ti].y : (j >> 1) == 2 ? xv[ti].z : xv[ti].w;
+                a[ti] = (double)__uint_as_float((j & 1) ? (word & 0xffff0000u) : (word << 16));
+            }
+#pragma unroll
+            for (int ei = 0; ei < ET; ++ei) b[ei] = (double)bf16_bits_to_float(wv[ei][j]);
+#pragma unroll
+            for (int ti = 0; ti < TT; ++ti)
+#pragma unroll
+                for (int ei = 0; ei < ET; ++ei)
+                    acc[ti][ei] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[ti], b[ei], acc[ti][ei], 0, 0, 0);
+        }
+#pragma unroll
+        for (int ti = 0; ti < TT; ++ti) xv[ti] = xn[ti];
+#pragma unroll
+        for (int ei = 0; ei < ET; ++ei)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) wv[ei][j] = wn[ei][j];
+    }
+    // result i of lane (r, g) is row g + 4 i, column r of its 16 x 16 tile (the f64
+    // layout interleaves rows, unlike the f32 16x16 shapes: measured)
+#pragma unroll
+    for (int ti = 0; ti < TT; ++ti)
+#pragma unroll
+        for (int ei = 0; ei < ET; ++ei) {
+            const int e = e0 + 16 * ei + r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = t0 + 16 * ti + g + 4 * i;
+                if (t < T && e < E) partial[((int64_t)blockIdx.z * T + t) * E + e] = acc[ti][ei][i];
+            }
+        }
 }
 
 // Philox4x64-10 (Salmon et al., SC'11): two 64x64->128 products per round,
@@ -322,24 +413,48 @@ RouterPlan router_plan(int64_t T, int64_t d, int E) {
     const int chunks_per_split = (nchunks + want - 1) / want;
     p.rows_per_split = chunks_per_split * kRowChunk;
     p.splits = (nchunks + chunks_per_split - 1) / chunks_per_split;
-    p.partial_bytes = (size_t)p.splits * (size_t)T * (size_t)E * sizeof(double);
+    // fp64-MFMA kernel: about 512 workgroups, at least 128 input rows per split
+    const int64_t tok_wg = E <= 16 ? 256 : 64, exp_wg = E <= 16 ? 16 : 64;
+    const int64_t wgs = ((T + tok_wg - 1) / tok_wg) * ((E + exp_wg - 1) / exp_wg);
+    int64_t ms = wgs > 0 ? (512 + wgs - 1) / wgs : 1;
+    ms = std::min<int64_t>(ms, std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, d / 128)));
+    const int64_t chunks = (d + kMfmaChunk - 1) / kMfmaChunk;
+    const int64_t cps = (chunks + ms - 1) / ms;
+    p.mfma_rows_per_split = (int)(cps * kMfmaChunk);
+    p.mfma_splits = (int)((chunks + cps - 1) / cps);
+    p.partial_bytes = (size_t)std::max(p.splits, p.mfma_splits) * (size_t)T * (size_t)E * sizeof(double);
     return p;
 }
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t stream) {
     if (a.T == 0) return hipSuccess;
     const RouterPlan p = router_plan(a.T, a.d, a.E);
-    dim3 grid1(p.tiles, p.splits);
-    if (a.act_dtype == kF32) {
+    int nsplit = p.splits;
+    if (a.act_dtype == kBF16 && a.T >= kMfmaMinTokens) {
+        nsplit = p.mfma_splits;
+        const uint16_t* xb = static_cast<const uint16_t*>(a.x);
+        const uint16_t* wb = static_cast<const uint16_t*>(a.Wg);
+        if (a.E <= 16) {
+            dim3 grid((unsigned)((a.T + 255) / 256), 1, (unsigned)p.mfma_splits);
+            hipLaunchKernelGGL((router_mfma_kernel<4, 1>), grid, dim3(256), 0, stream, xb, wb, (int)a.T, (int)a.d, a.E,
+                               p.mfma_rows_per_split, a.partial);
+        } else {
+            dim3 grid((unsigned)((a.T + 63) / 64), (unsigned)((a.E + 63) / 64), (unsigned)p.mfma_splits);
+            hipLaunchKernelGGL((router_mfma_kernel<2, 2>), grid, dim3(256), 0, stream, xb, wb, (int)a.T, (int)a.d, a.E,
+                               p.mfma_rows_per_split, a.partial);
+        }
+    } else if (a.act_dtype == kF32) {
+        dim3 grid1(p.tiles, p.splits);
         hipLaunchKernelGGL(router_partial_kernel<kF32>, grid1, dim3(kRouterThreads), 0, stream, a.x, a.Wg, (int)a.T,
                            (int)a.d, a.E, p.expert_groups, p.rows_per_split, a.partial);
     } else {
+        dim3 grid1(p.tiles, p.splits);
         hipLaunchKernelGGL(router_partial_kernel<kBF16>, grid1, dim3(kRouterThreads), 0, stream, a.x, a.Wg,
                            (int)a.T, (int)a.d, a.E, p.expert_groups, p.rows_per_split, a.partial);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(router_finalize_kernel, dim3((unsigned)a.T), dim3(256), 0, stream, a.partial, p.splits,
+    hipLaunchKernelGGL(router_finalize_kernel, dim3((unsigned)a.T), dim3(256), 0, stream, a.partial, nsplit,
                        (int)a.T, a.E, a.k, a.bias, (double)a.tau, a.use_gumbel, (double)a.noise_std, a.gate_norm,
                        a.seed, a.token_offset, a.ids,
                        a.gates, a.prob_rows, a.entropy_rows, a.z_rows);
