@@ -31,6 +31,9 @@ ROUTER_CASES = {
     "bf16-T31-d192-E5-k3": case(31, 192, 64, 5, k=3),
     "f32-T40-d64-E1-k1": case(40, 64, 64, 1, k=1, act=F32, w=F32),
     "bf16-T1-d8192-E128": case(1, 8192, 64, 128),
+    # fp64-MFMA router (bf16, T >= 64): partial 32-expert blocks, E just past the 16-expert layout, d split unevenly
+    "bf16-T130-d640-E40-k3": case(130, 640, 64, 40, k=3),
+    "bf16-T70-d448-E17-bias": case(70, 448, 64, 17, bias=True),
     # variants: Gaussian logit noise, renormalised gates, both with Gumbel noise and a temperature
     "bf16-T200-d512-E64-gaussian0.1": case(200, 512, 64, 64, noise=0.1),
     "bf16-T77-d768-E16-gumbel-gaussian0.3-tau0.5-renorm": case(77, 768, 128, 16, tau=0.5, gumbel=True, noise=0.3,
