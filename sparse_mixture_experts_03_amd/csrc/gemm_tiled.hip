@@ -175,6 +175,43 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[TI][TJ], uint
     }
 }
 
+// GEMM2 epilogue of the bf16 kernel (fp32 Y), staged through LDS like GEMM1's
+// in passes of 32 dispatch rows (a wavefront's whole fp32 tile would not fit):
+// every store instruction writes whole rows of Y.  Each wavefront reuses only
+// its own region and its LDS operations execute in order, so one barrier (the
+// last stage is no longer read) is enough.
+template <int TI, int TJ, int NWAVE>
+__device__ __forceinline__ void store_tile_lds_f32(const f32x16 (&acc)[TI][TJ], uint8_t* lds, float* __restrict__ out,
+                                                   int N, int n0, int p0, int rows, int wn, int wm, int r, int h,
+                                                   bool math) {
+    constexpr int NW = 32 * TI;         // this wavefront's weight rows (columns of Y)
+    constexpr int STRIDE = NW * 4 + 16;  // padded LDS row in bytes
+    static_assert(NWAVE * 32 * STRIDE <= 5 * 32768, "epilogue staging exceeds the kernel's LDS");
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    uint8_t* wl = lds + wave * (32 * STRIDE);
+    constexpr int CH = NW * 4 / 16, RPI = 64 / CH;  // 16-byte chunks per row, rows per instruction
+    const int cr = lane / CH, cc = lane % CH;
+    const int n = n0 + wn + cc * 4;  // N is a multiple of 4
+    barrier();
+    if (!math) return;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<float4*>(wl + r * STRIDE + (32 * i + 8 * q + 4 * h) * 4) =
+                    make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+#pragma unroll
+        for (int k = 0; k < 32 / RPI; ++k) {
+            const int ml = k * RPI + cr;
+            const float4 v = *reinterpret_cast<const float4*>(wl + ml * STRIDE + cc * 16);
+            const int m = wm + 32 * j + ml;
+            if (m < rows && n < N) *reinterpret_cast<float4*>(out + (int64_t)(p0 + m) * N + n) = v;
+        }
+    }
+}
+
 template <int WHICH, int TI, int TJ, int ACT, bool GELU_ERF = false>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TI][TJ], void* __restrict__ out, int N, int n0, int p0,
                                            int rows, int wn, int wm, int r, int h) {
@@ -660,6 +697,8 @@ __device__ __forceinline__ void tile_gemm_bf16(uint8_t* lds, const uint16_t* __r
     mma_sub(dw, dx);
     if constexpr (WHICH == 1 && ACT != kActSwiglu) {
         store_tile_lds<TI, TJ, ACT, NWAVE>(acc, lds, out, N, n0, p0, rows, wn, wm, r, h, math);
+    } else if constexpr (WHICH == 2) {
+        store_tile_lds_f32<TI, TJ, NWAVE>(acc, lds, static_cast<float*>(out), N, n0, p0, rows, wn, wm, r, h, math);
     } else {
         if (math) store_tile<WHICH, TI, TJ, ACT>(acc, out, N, n0, p0, rows, wn, wm, r, h);
     }
