@@ -42,6 +42,15 @@
 #ifndef MOE_STREAM_NT
 #define MOE_STREAM_NT 1        // 1: non-temporal hint on weight loads
 #endif
+#ifndef MOE_STREAM_NB_INT4_16
+#define MOE_STREAM_NB_INT4_16 4  // the same for 16-row dispatch tiles
+#endif
+#ifndef MOE_STREAM_STAGE_INT4_16
+#define MOE_STREAM_STAGE_INT4_16 128  // the same for 16-row dispatch tiles
+#endif
+#ifndef MOE_STREAM_XPRE
+#define MOE_STREAM_XPRE 1      // 1: INT4, 16-row dispatch tiles: a stage's activations loaded before the next weights
+#endif
 
 namespace moe {
 
@@ -113,7 +122,7 @@ __device__ __forceinline__ void store_swiglu(void* out, int64_t Nh, int p0, int 
 }
 
 // Only experts holding n rows with rows_lo < n <= rows_hi are multiplied here.
-template <int WQ, int WHICH, int NB, int MT, int kStageBytes>
+template <int WQ, int WHICH, int NB, int MT, int kStageBytes, bool SCV = false>
 __global__ void __launch_bounds__(256)
 gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
                    const int32_t* __restrict__ offsets, int E, const uint8_t* __restrict__ W,
@@ -171,12 +180,14 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
     auto gload = [&](int st, uint4 (&buf)[LOADS]) {
         const int64_t s0 = (int64_t)st * kStageBytes;
         const int64_t valid = min((int64_t)kStageBytes, row_bytes - s0);
-        if (WQ == kINT4 && valid == kStageBytes) {  // every stage but a K tail: no per-load guards
+        if constexpr (WQ == kINT4) {
+            // no guards: segments past a K tail re-read the row's last 16 bytes
+            // (never used), so every stage issues the same loads unconditionally
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
                 const int flat = 64 * i + lane;
                 const int row = flat / SEGS, seg = flat % SEGS;
-                buf[i] = ldw16(Wblk + (int64_t)row * row_bytes + s0 + seg * 16);
+                buf[i] = ldw16(Wblk + (int64_t)row * row_bytes + min(s0 + seg * 16, row_bytes - 16));
             }
             return;
         }
@@ -208,22 +219,41 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
     const int groups = K / 128;
     const int srow = lane % ROWS;
     const uint16_t* sc_row = (WQ == kINT4) ? Wsc + (int64_t)e * N * groups + (int64_t)(n0 + srow) * groups : nullptr;
-    const bool sc_vec = (WQ == kINT4) && groups % GPS == 0 && ((uintptr_t)Wsc % 16) == 0;
     uint16_t* sc_lds = reinterpret_cast<uint16_t*>(lds + ROWS * LROW);  // [ROWS][GPS]
     typedef uint16_t scales_t __attribute__((ext_vector_type(GPS)));
     auto sload = [&](int st, scales_t& v) {
         const int gb = st * GPS;
-        if (sc_vec) {
+        if constexpr (SCV) {
             v = *reinterpret_cast<const scales_t*>(sc_row + gb);
         } else {
 #pragma unroll
-            for (int j = 0; j < GPS; ++j) v[j] = gb + j < groups ? sc_row[gb + j] : (uint16_t)0;
+            for (int j = 0; j < GPS; ++j) {  // unconditional loads (clamped), then zero past the last group
+                const uint16_t t = sc_row[min(gb + j, groups - 1)];
+                v[j] = gb + j < groups ? t : (uint16_t)0;
+            }
         }
     };
     const uint4 ones = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
 
     // Two register buffers: stage st + 1 is in flight while stage st is parked
     // in LDS and multiplied.
+    constexpr bool XP = WQ == kINT4 && MOE_STREAM_XPRE && MT == 1;
+    constexpr int XG = XP ? GPS : 1;
+    uint4 xs[XG][MT][4];
+    auto xload = [&](int st) {
+        if constexpr (XP) {
+            // groups past a K tail are never used: their loads repeat the last group
+            const int gbase = st * GPS;
+#pragma unroll
+            for (int cc = 0; cc < GPS; ++cc) {
+                const int grp = min(gbase + cc, groups - 1);
+#pragma unroll
+                for (int c = 0; c < MT; ++c)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) xs[cc][c][s] = ld16(xrow[c] + grp * 128 + 32 * g + 8 * s);
+            }
+        }
+    };
     auto process = [&](int st, const uint4 (&buf)[LOADS], const scales_t& sbuf) {
         lstore(buf);
         if constexpr (WQ == kINT4) {
@@ -259,7 +289,7 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
             for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sv[b][i] = *reinterpret_cast<const scales_t*>(sc_lds + (16 * b + 4 * g + i) * GPS);
-            const int nch = valid / 64;
+            const int nch = SCV ? GPS : valid / 64;  // SCV: K is a multiple of the stage
 #pragma unroll
             for (int cc = 0; cc < GPS; ++cc) {
                 if (cc >= nch) break;
@@ -269,7 +299,8 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
                 for (int c = 0; c < MT; ++c)
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
-                        xv[c][s] = (xall || mvalid[c]) ? ld16(xrow[c] + grp * 128 + 32 * g + 8 * s) : zero4;
+                        xv[c][s] = XP ? xs[XP ? cc : 0][c][s]
+                                 : (xall || mvalid[c]) ? ld16(xrow[c] + grp * 128 + 32 * g + 8 * s) : zero4;
                 f32x4 t[NB][MT], sx[MT];
                 uint4 q[NB];
 #pragma unroll
@@ -314,12 +345,32 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
     if (st0 < st1) fetch(st0, bufa, sa);
     // (using the two buffers in turn instead of copying needs two copies of the
     // stage code and more registers; measured slower at decode sizes)
-    for (int st = st0; st < st1; ++st) {
-        if (st + 1 < st1) fetch(st + 1, bufb, sb);
-        process(st, bufa, sa);
+    if constexpr (WQ == kINT4) {
+        // the last stage is peeled so that the loop's loads are unconditional
+        int st = st0;
+        for (; st + 1 < st1; ++st) {
+            if constexpr (XP) {
+                xload(st);  // issued before the next stage's weights, so its waits never include them
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            fetch(st + 1, bufb, sb);
+            process(st, bufa, sa);
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) bufa[i] = bufb[i];
-        sa = sb;
+            for (int i = 0; i < LOADS; ++i) bufa[i] = bufb[i];
+            sa = sb;
+        }
+        if (st < st1) {
+            if constexpr (XP) xload(st);
+            process(st, bufa, sa);
+        }
+    } else {
+        for (int st = st0; st < st1; ++st) {
+            if (st + 1 < st1) fetch(st + 1, bufb, sb);
+            process(st, bufa, sa);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) bufa[i] = bufb[i];
+            sa = sb;
+        }
     }
 
     // fixed-order reduction of the four K-slices (in the stage buffers, once every wavefront is done with them)
@@ -373,12 +424,23 @@ hipError_t launch_stream_nb(const GemmArgs& a, hipStream_t stream) {
     const uint8_t* W = static_cast<const uint8_t*>(a.W);
     const uint16_t* S = static_cast<const uint16_t*>(a.W_scales);
     dim3 grid((unsigned)blocks), block(256);
-    if (a.which == 1)
-        hipLaunchKernelGGL((gemm_stream_kernel<WQ, 1, NB, MT, SB>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E,
-                           W, S, a.W_stride, a.out, (int)a.N, (int)a.K, ntiles_n, a.rows_lo, a.rows_hi, a.act);
-    else
-        hipLaunchKernelGGL((gemm_stream_kernel<WQ, 2, NB, MT, SB>), grid, block, 0, stream, A, a.a_rows, a.offsets, a.E,
-                           W, S, a.W_stride, a.out, (int)a.N, (int)a.K, ntiles_n, a.rows_lo, a.rows_hi, a.act);
+    // INT4: each stage's group scales are one vector load when every row's
+    // scales start on a stage boundary of an aligned array
+    const bool scv = WQ == kINT4 && (a.K / 128) % (SB / 64) == 0 && ((uintptr_t)S % 16) == 0;
+#define MOE_STREAM_LAUNCH(WHICH_, SCV_)                                                                            \
+    hipLaunchKernelGGL((gemm_stream_kernel<WQ, WHICH_, NB, MT, SB, SCV_>), grid, block, 0, stream, A, a.a_rows,     \
+                       a.offsets, a.E, W, S, a.W_stride, a.out, (int)a.N, (int)a.K, ntiles_n, a.rows_lo, a.rows_hi, \
+                       a.act)
+    if constexpr (WQ == kINT4) {
+        if (a.which == 1) {
+            if (scv) MOE_STREAM_LAUNCH(1, true); else MOE_STREAM_LAUNCH(1, false);
+        } else {
+            if (scv) MOE_STREAM_LAUNCH(2, true); else MOE_STREAM_LAUNCH(2, false);
+        }
+    } else {
+        if (a.which == 1) MOE_STREAM_LAUNCH(1, false); else MOE_STREAM_LAUNCH(2, false);
+    }
+#undef MOE_STREAM_LAUNCH
     return hipGetLastError();
 }
 
@@ -395,7 +457,7 @@ hipError_t launch_stream_bf16(const GemmArgs& a, hipStream_t stream) {
     return launch_stream_nb<kBF16, 4, 4, 128>(a, stream);
 }
 hipError_t launch_stream_int4(const GemmArgs& a, hipStream_t stream) {
-    if (a.stream_mt == 1) return launch_stream_nb<kINT4, MOE_STREAM_NB_INT4, 1, MOE_STREAM_STAGE_INT4>(a, stream);
+    if (a.stream_mt == 1) return launch_stream_nb<kINT4, MOE_STREAM_NB_INT4_16, 1, MOE_STREAM_STAGE_INT4_16>(a, stream);
     if (a.stream_mt == 2) return launch_stream_nb<kINT4, MOE_STREAM_NB_INT4, 2, MOE_STREAM_STAGE_INT4>(a, stream);
     return launch_stream_nb<kINT4, MOE_STREAM_NB_INT4, 4, MOE_STREAM_STAGE_INT4>(a, stream);
 }
