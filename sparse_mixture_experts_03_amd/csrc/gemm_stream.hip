@@ -92,6 +92,36 @@ __device__ __forceinline__ bf16x8 int4x8_to_bf16_offset136(uint32_t w) {
     return as_bf16x8(r);
 }
 
+#ifndef MOE_STREAM_INT4_KPERM
+#define MOE_STREAM_INT4_KPERM 1
+#endif
+// The same eight codes in a permuted K order that needs no byte permute:
+// output dword j holds codes j (bits 4j..4j+3 of w, low half) and j + 4 (bits
+// 16+4j.., high half), i.e. K slots (0,4,1,5,2,6,3,7); the activation operand
+// is permuted to match (kperm_x).  One shift and one three-input bit operation
+// ((w >> 4j) & 0x000f000f) ^ 0x43084308 per dword: the xor flips bit 3 of each
+// code and sets the 0x43 exponent bytes.
+__device__ __forceinline__ bf16x8 int4x8_to_bf16_offset136_kperm(uint32_t w) {
+    constexpr uint32_t kNib = 0x000f000fu, kMagic = 0x43084308u;
+    constexpr uint32_t kAndXor = (0xf0 & 0xcc) ^ 0xaa;  // truth table of (src0 & src1) ^ src2
+    uint4 r;
+    r.x = __builtin_amdgcn_bitop3_b32(w, kNib, kMagic, kAndXor);
+    r.y = __builtin_amdgcn_bitop3_b32(w >> 4, kNib, kMagic, kAndXor);
+    r.z = __builtin_amdgcn_bitop3_b32(w >> 8, kNib, kMagic, kAndXor);
+    r.w = __builtin_amdgcn_bitop3_b32(w >> 12, kNib, kMagic, kAndXor);
+    return as_bf16x8(r);
+}
+// Eight bf16 activations (x0..x7) reordered to the K slots above: (x0,x4),
+// (x1,x5), (x2,x6), (x3,x7).
+__device__ __forceinline__ uint4 kperm_x(uint4 v) {
+    uint4 r;
+    r.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+    r.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
+    r.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+    r.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+    return r;
+}
+
 template <int WHICH>
 __device__ __forceinline__ void store_tile(void* out, int64_t N, int p0, int rows, int n0, f32x4 v, int lane,
                                            int act) {
@@ -313,15 +343,19 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
                 }
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
+                    uint4 xo[MT];
+#pragma unroll
+                    for (int c = 0; c < MT; ++c) xo[c] = MOE_STREAM_INT4_KPERM ? kperm_x(xv[c][s]) : xv[c][s];
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
                         const uint32_t word = s == 0 ? q[b].x : s == 1 ? q[b].y : s == 2 ? q[b].z : q[b].w;
-                        const bf16x8 wq = int4x8_to_bf16_offset136(word);
+                        const bf16x8 wq = MOE_STREAM_INT4_KPERM ? int4x8_to_bf16_offset136_kperm(word)
+                                                                : int4x8_to_bf16_offset136(word);
 #pragma unroll
-                        for (int c = 0; c < MT; ++c) t[b][c] = mfma16x16x32(wq, as_bf16x8(xv[c][s]), t[b][c]);
+                        for (int c = 0; c < MT; ++c) t[b][c] = mfma16x16x32(wq, as_bf16x8(xo[c]), t[b][c]);
                     }
 #pragma unroll
-                    for (int c = 0; c < MT; ++c) sx[c] = mfma16x16x32(as_bf16x8(ones), as_bf16x8(xv[c][s]), sx[c]);
+                    for (int c = 0; c < MT; ++c) sx[c] = mfma16x16x32(as_bf16x8(ones), as_bf16x8(xo[c]), sx[c]);
                 }
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
