@@ -314,6 +314,9 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
         } else {
             // one 128-column scale group per 64 bytes of each row; lane group g takes columns [32g, 32g+32)
             const int gbase = (int)(s0 / 64);
+            // the permuted-K dequantisation where registers allow it (16-row dispatch
+            // tiles; with 32 or 64 rows its activation copies would spill)
+            constexpr bool KPERM = MOE_STREAM_INT4_KPERM && MT == 1;
             scales_t sv[NB][4];  // this lane's output rows 16 b + 4 g + i
 #pragma unroll
             for (int b = 0; b < NB; ++b)
@@ -345,12 +348,11 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
                 for (int s = 0; s < 4; ++s) {
                     uint4 xo[MT];
 #pragma unroll
-                    for (int c = 0; c < MT; ++c) xo[c] = MOE_STREAM_INT4_KPERM ? kperm_x(xv[c][s]) : xv[c][s];
+                    for (int c = 0; c < MT; ++c) xo[c] = KPERM ? kperm_x(xv[c][s]) : xv[c][s];
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
                         const uint32_t word = s == 0 ? q[b].x : s == 1 ? q[b].y : s == 2 ? q[b].z : q[b].w;
-                        const bf16x8 wq = MOE_STREAM_INT4_KPERM ? int4x8_to_bf16_offset136_kperm(word)
-                                                                : int4x8_to_bf16_offset136(word);
+                        const bf16x8 wq = KPERM ? int4x8_to_bf16_offset136_kperm(word) : int4x8_to_bf16_offset136(word);
 #pragma unroll
                         for (int c = 0; c < MT; ++c) t[b][c] = mfma16x16x32(wq, as_bf16x8(xo[c]), t[b][c]);
                     }
