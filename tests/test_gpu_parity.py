@@ -128,6 +128,10 @@ FORWARD_CASES = {
     "int4-T12-d512-dff1024-E8-gumbel": (case(12, 512, 1024, 8, w=INT4, tau=0.5, gumbel=True), [moe.GEMM_AUTO]),
     # K tails in the streaming INT4 kernel: 5 and 9 scale groups, so the last 256-byte stage is partial
     "int4-T30-d640-dff1152-E8": (case(30, 640, 1152, 8, w=INT4), [moe.GEMM_STREAMING]),
+    # the same K tails with 16-row dispatch tiles (T <= 16): activations loaded ahead, permuted-K dequantisation,
+    # an odd number of scale groups per row (scales read one by one)
+    "int4-T12-d640-dff1152-E8": (case(12, 640, 1152, 8, w=INT4), [moe.GEMM_STREAMING]),
+    "int4-T5-d1152-dff640-E4-k1": (case(5, 1152, 640, 4, k=1, w=INT4), [moe.GEMM_STREAMING]),
     "int4-T200-d384-dff768-E8-gumbel": (case(200, 384, 768, 8, w=INT4, tau=0.5, gumbel=True), [moe.GEMM_AUTO]),
     # K = 1024 and 3072: one and three 32-stage scale blocks; skewed rows exercise all three tile heights
     "int4-T200-d1024-dff3072-E8-skewed": (case(200, 1024, 3072, 8, w=INT4, bias=True),
