@@ -12,10 +12,10 @@ namespace {
 
 constexpr int kCombineCols = 1024;  // columns per workgroup (256 threads x 4)
 
-template <int ACT>
+template <int ACT, bool SPLIT>
 __global__ void __launch_bounds__(256)
-combine_kernel(const float* __restrict__ Y, const int32_t* __restrict__ pos, const float* __restrict__ gates,
-               void* __restrict__ y, int64_t d, int k, int chunks) {
+combine_kernel(const float* __restrict__ Y, const float* __restrict__ Y2, const int32_t* __restrict__ pos,
+               const float* __restrict__ gates, void* __restrict__ y, int64_t d, int k, int chunks) {
     const int64_t t = blockIdx.x / chunks;
     const int64_t c = (int64_t)(blockIdx.x % chunks) * kCombineCols + threadIdx.x * 4;
     if (c >= d) return;
@@ -24,7 +24,14 @@ combine_kernel(const float* __restrict__ Y, const int32_t* __restrict__ pos, con
         const int p = pos[t * k + j];
         if (p < 0) continue;  // an assignment the dispatch rejected (expert id out of range)
         const float g = gates[t * k + j];
-        const float4 v = *reinterpret_cast<const float4*>(Y + (int64_t)p * d + c);
+        float4 v = *reinterpret_cast<const float4*>(Y + (int64_t)p * d + c);
+        if (SPLIT) {  // the two K halves of the expert output, added in a fixed order
+            const float4 v2 = *reinterpret_cast<const float4*>(Y2 + (int64_t)p * d + c);
+            v.x += v2.x;
+            v.y += v2.y;
+            v.z += v2.z;
+            v.w += v2.w;
+        }
         acc.x = fmaf(g, v.x, acc.x);
         acc.y = fmaf(g, v.y, acc.y);
         acc.z = fmaf(g, v.z, acc.z);
@@ -43,17 +50,20 @@ combine_kernel(const float* __restrict__ Y, const int32_t* __restrict__ pos, con
 }  // namespace
 
 hipError_t launch_combine(const float* Y, const int32_t* pos, const float* gates, void* y, int64_t T, int64_t d,
-                          int k, int act_dtype, hipStream_t stream) {
+                          int k, int act_dtype, hipStream_t stream, const float* Y2) {
     if (T == 0) return hipSuccess;
     const int chunks = (int)((d + kCombineCols - 1) / kCombineCols);
     const int64_t blocks = T * chunks;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    if (act_dtype == kF32)
-        hipLaunchKernelGGL(combine_kernel<kF32>, dim3((unsigned)blocks), dim3(256), 0, stream, Y, pos, gates, y, d,
-                           k, chunks);
-    else
-        hipLaunchKernelGGL(combine_kernel<kBF16>, dim3((unsigned)blocks), dim3(256), 0, stream, Y, pos, gates, y,
-                           d, k, chunks);
+#define MOE_COMBINE_LAUNCH(ACT_, SPLIT_)                                                                     \
+    hipLaunchKernelGGL((combine_kernel<ACT_, SPLIT_>), dim3((unsigned)blocks), dim3(256), 0, stream, Y, Y2, pos, \
+                       gates, y, d, k, chunks)
+    if (act_dtype == kF32) {
+        if (Y2) MOE_COMBINE_LAUNCH(kF32, true); else MOE_COMBINE_LAUNCH(kF32, false);
+    } else {
+        if (Y2) MOE_COMBINE_LAUNCH(kBF16, true); else MOE_COMBINE_LAUNCH(kBF16, false);
+    }
+#undef MOE_COMBINE_LAUNCH
     return hipGetLastError();
 }
 

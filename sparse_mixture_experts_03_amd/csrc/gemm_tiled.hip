@@ -584,7 +584,8 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
 template <int WHICH, int TI, int TJ, int XROWS, int ACT, int MWAVE = 8>
 __device__ __forceinline__ void tile_gemm_bf16(uint8_t* lds, const uint16_t* __restrict__ A,
                                                const int32_t* __restrict__ a_rows, const void* Wexp,
-                                               void* __restrict__ out, int N, int K, int n0, int p0, int rows) {
+                                               void* __restrict__ out, int N, int K, int n0, int p0, int rows,
+                                               int kt0, int nk) {
     constexpr int NWAVE = 8;
     constexpr int WN_WAVES = 256 / (32 * TI);
     static_assert(WN_WAVES * (XROWS / (32 * TJ)) == MWAVE, "wave grid");
@@ -610,14 +611,15 @@ __device__ __forceinline__ void tile_gemm_bf16(uint8_t* lds, const uint16_t* __r
         const uint32_t arow = (WHICH == 1) ? (uint32_t)a_rows[p0 + drow] : (uint32_t)(p0 + drow);
         xoff[i] = arow * rowbytes + 16 * seg;
     }
+    // stages kt0 .. kt0 + nk - 1 of the K dimension (kt counts from 0 within them)
     auto issue_w = [&](int kt) {
-        const uint32_t kb = (uint32_t)kt * 128;
+        const uint32_t kb = (uint32_t)(kt0 + kt) * 128;
         uint8_t* slot = Wr + (kt & 1) * kStage;
 #pragma unroll
         for (int i = 0; i < 4; ++i) copy_rows_to_lds(wbase, woff[i] + kb, slot + (32 * wave + 8 * i) * 128);
     };
     auto issue_x = [&](int kt) {
-        const uint32_t kb = (uint32_t)kt * 128;
+        const uint32_t kb = (uint32_t)(kt0 + kt) * 128;
         uint8_t* slot = Xr + (kt % 3) * kStage;
         if (xload) {
 #pragma unroll
@@ -667,7 +669,6 @@ __device__ __forceinline__ void tile_gemm_bf16(uint8_t* lds, const uint16_t* __r
     };
     using NF = std::integral_constant<int, TI + TJ>;
     using N0 = std::integral_constant<int, 0>;
-    const int nk = K / 64;
     issue_w(0);
     issue_x(0);
     if (nk > 1) issue_x(1);
@@ -756,12 +757,19 @@ template <int WHICH, int ACT>
 __global__ void __launch_bounds__(512, 1)
 gemm_tiled_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
                        const int32_t* __restrict__ offsets, int E, const uint8_t* __restrict__ W, int64_t W_stride,
-                       void* __restrict__ out, int N, int K, int ntiles_n, int rows_lo) {
+                       void* __restrict__ out, int N, int K, int ntiles_n, int rows_lo, int ksplit,
+                       int64_t split_stride) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[5 * 32768];
     asm volatile("" ::: "a0");  // accumulators in AGPRs (see gemm_tiled_kernel)
     const MtileScan scan = scan_mtiles(offsets, E, kTBM, rows_lo, 0x7fffffff);
-    const int mt = blockIdx.x / ntiles_n;
-    const int nt = blockIdx.x - mt * ntiles_n;
+    // ksplit = 2 (GEMM2 only): workgroups 2 b and 2 b + 1 take the two K halves
+    // of tile b and write them to out and out + split_stride (fp32 partials)
+    const int ks = blockIdx.x % ksplit;
+    const int b = blockIdx.x / ksplit;
+    const int mt = b / ntiles_n;
+    const int nt = b - mt * ntiles_n;
+    const int nk = K / 64 / ksplit, kt0 = ks * nk;
+    if (WHICH == 2) out = static_cast<float*>(out) + ks * split_stride;
     if (mt >= scan.total) return;
     int e, p0, rows;
     lookup_mtile(scan, offsets, kTBM, mt, &e, &p0, &rows);
@@ -771,11 +779,11 @@ gemm_tiled_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict
     const int n0 = nt * kTBN;
     const void* Wexp = W + (int64_t)e * W_stride;
     if (rows > 128)
-        tile_gemm_bf16<WHICH, 4, 2, 256, ACT>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows);
+        tile_gemm_bf16<WHICH, 4, 2, 256, ACT>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows, kt0, nk);
     else if (rows > 64)
-        tile_gemm_bf16<WHICH, 2, 2, 128, ACT>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows);
+        tile_gemm_bf16<WHICH, 2, 2, 128, ACT>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows, kt0, nk);
     else
-        tile_gemm_bf16<WHICH, 2, 2, 64, ACT, 4>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows);
+        tile_gemm_bf16<WHICH, 2, 2, 64, ACT, 4>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows, kt0, nk);
 }
 
 }  // namespace
@@ -801,9 +809,13 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
         else if (a.act == kActSwiglu) MOE_TILED_LAUNCH(kINT4, 1, kActSwiglu);
         else MOE_TILED_LAUNCH(kINT4, 1, kActGelu);
     } else {
-#define MOE_TILED_BF16_LAUNCH(WHICH_, ACT_)                                                                      \
-    hipLaunchKernelGGL((gemm_tiled_bf16_kernel<WHICH_, ACT_>), grid, dim3(512), 0, stream, A, a.a_rows, a.offsets, \
-                       a.E, W, a.W_stride, a.out, N, K, ntiles_n, a.rows_lo)
+        const int ksplit = (a.which == 2 && a.ksplit == 2 && K % 128 == 0) ? 2 : 1;
+        if ((int64_t)blocks * ksplit > 0x7fffffff) return hipErrorInvalidValue;
+        const dim3 grid_k((unsigned)(blocks * ksplit));
+        const int64_t split_stride = a.T * a.k * a.N;
+#define MOE_TILED_BF16_LAUNCH(WHICH_, ACT_)                                                                        \
+    hipLaunchKernelGGL((gemm_tiled_bf16_kernel<WHICH_, ACT_>), grid_k, dim3(512), 0, stream, A, a.a_rows,            \
+                       a.offsets, a.E, W, a.W_stride, a.out, N, K, ntiles_n, a.rows_lo, ksplit, split_stride)
         if (a.which == 2) MOE_TILED_BF16_LAUNCH(2, kActGelu);
         else if (a.act == kActSilu) MOE_TILED_BF16_LAUNCH(1, kActSilu);
         else if (a.act == kActSwiglu) MOE_TILED_BF16_LAUNCH(1, kActSwiglu);

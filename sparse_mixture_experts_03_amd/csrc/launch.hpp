@@ -84,6 +84,7 @@ struct GemmArgs {
     int rows_lo, rows_hi;   // only experts holding n rows, rows_lo < n <= rows_hi
     int stream_mt;          // streaming kernel: 16-row dispatch tiles per workgroup (1, 2 or 4)
     int act = 0;            // which 1: kActGelu, kActSilu or kActSwiglu (N = 2 d_ff weight rows)
+    int ksplit = 1;         // tiled bf16, which 2: K halves written to out and out + T*k*N (fp32 partials)
 };
 hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream);  // BF16 / INT4 weights
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);   // BF16 weights
@@ -97,7 +98,8 @@ hipError_t launch_encoder_act(const float* pre, const float* b_in, void* h, int6
                               hipStream_t stream);
 
 // --------------------------------------------------------------- combine
+// Y2: null, or the second K half of Y (added to Y before the gate weighting)
 hipError_t launch_combine(const float* Y, const int32_t* pos, const float* gates, void* y, int64_t T, int64_t d,
-                          int k, int act_dtype, hipStream_t stream);
+                          int k, int act_dtype, hipStream_t stream, const float* Y2 = nullptr);
 
 }  // namespace moe

@@ -7,6 +7,7 @@
 // No host synchronisation and no host<->device copy happens inside a call;
 // counts and the dispatch order stay on the device and every kernel finds its
 // work from them.
+#include <algorithm>
 #include <math.h>
 #include <string.h>
 
@@ -126,6 +127,20 @@ struct Layout {
     size_t partial, offsets, sorted_token, pos, H, Y, z_rows, prob_rows, total;
 };
 
+int gemm_path_of(const moe_config& c);
+
+// K halves of the layer's GEMM2 (bf16 tiled kernel): 2 when the grid holds
+// fewer than four rounds of 256-row tiles for 256 CUs, so that its last,
+// partly filled round of long tiles (K = d_ff) is split in two; the combine
+// adds the two fp32 partials.  1 otherwise.
+int w2_ksplit_of(const moe_config& c) {
+    if (c.w_dtype != MOE_DTYPE_BF16 || gemm_path_of(c) != MOE_GEMM_TILED || c.d_ff % 128 != 0) return 1;
+    const int64_t Tk = c.T * (int64_t)c.k;
+    const int64_t mtiles = Tk / 256 + std::min<int64_t>(Tk, c.E);
+    const int64_t ntiles = (c.d + 255) / 256;
+    return mtiles * ntiles < 4 * 256 ? 2 : 1;
+}
+
 Layout layout_of(const moe_config& c) {
     Layout L;
     const size_t Tk = (size_t)c.T * (size_t)c.k;
@@ -142,7 +157,7 @@ Layout layout_of(const moe_config& c) {
     L.H = off;
     off = round_up(off + hbytes * Tk * (size_t)c.d_ff, 256);
     L.Y = off;
-    off = round_up(off + sizeof(float) * Tk * (size_t)c.d, 256);
+    off = round_up(off + sizeof(float) * Tk * (size_t)c.d * (size_t)w2_ksplit_of(c), 256);
     L.z_rows = L.prob_rows = 0;
     if (capacity_active(c)) {
         L.z_rows = off;
@@ -177,7 +192,7 @@ moe_status check_weights(const moe_config& c, const void* W, const void* S, int6
 }
 
 hipError_t run_gemm(const moe_config& c, int which, const void* A, const int32_t* a_rows, const int32_t* offsets,
-                    const void* W, const void* S, int64_t stride, void* out, hipStream_t stream) {
+                    const void* W, const void* S, int64_t stride, void* out, hipStream_t stream, int ksplit = 1) {
     moe::GemmArgs g;
     g.which = which;
     g.A = A;
@@ -200,6 +215,7 @@ hipError_t run_gemm(const moe_config& c, int which, const void* A, const int32_t
     g.rows_hi = 0x7fffffff;
     // a token adds at most one row to an expert, so no expert holds more than T rows
     g.stream_mt = c.T <= 16 ? 1 : c.T <= 32 ? 2 : 4;
+    g.ksplit = ksplit;
     if (c.w_dtype == MOE_DTYPE_F32) return moe::launch_gemm_f32(g, stream);
     if (g.path == MOE_GEMM_STREAMING) return moe::launch_gemm_stream(g, stream);
     return moe::launch_gemm_tiled(g, stream);
@@ -351,9 +367,11 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
     }
     e = run_gemm(c, 1, x, sorted_token, offsets, W1, W1_scales, W1_expert_stride, H, stream);
     if (e != hipSuccess) return hip_fail(e);
-    e = run_gemm(c, 2, H, nullptr, offsets, W2, W2_scales, W2_expert_stride, Y, stream);
+    const int ksplit = w2_ksplit_of(c);
+    e = run_gemm(c, 2, H, nullptr, offsets, W2, W2_scales, W2_expert_stride, Y, stream, ksplit);
     if (e != hipSuccess) return hip_fail(e);
-    e = moe::launch_combine(Y, pos, gate_weights, y, c.T, c.d, c.k, c.act_dtype, stream);
+    const float* Y2 = ksplit == 2 ? Y + (int64_t)c.T * c.k * c.d : nullptr;
+    e = moe::launch_combine(Y, pos, gate_weights, y, c.T, c.d, c.k, c.act_dtype, stream, Y2);
     if (e != hipSuccess) return hip_fail(e);
     return MOE_OK;
 }
