@@ -130,7 +130,8 @@ typedef enum moe_capacity_policy {
 } moe_capacity_policy;
 
 /* Bytes of device workspace moe_forward needs for `cfg` (0 when T == 0); capacity-limited
- * dispatch adds the [T][E] logit and probability rows. */
+ * dispatch adds the [T][E] logit and probability rows, and a bf16 tiled GEMM2 run in two
+ * K halves (small tile grids) a second [T*k][d] float intermediate. */
 moe_status moe_workspace_size(const moe_config *cfg, size_t *bytes);
 
 /* Bytes of device workspace moe_router needs for `cfg`. */
