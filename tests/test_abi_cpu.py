@@ -268,3 +268,28 @@ def test_workloads_are_valid_configs(lib):
         c = moe.config(w["T"], w["d"], w["d_ff"], w["E"], w["k"], w["act"], w["w"], tau=w["tau"],
                        use_gumbel=w["gumbel"])
         assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == 0, name
+
+
+def _ws(lib, c):
+    n = ctypes.c_size_t()
+    assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == 0
+    return n.value
+
+
+def test_workspace_holds_two_gemm2_halves_for_small_tiled_grids(lib):
+    # bf16 tiled GEMM2 over a grid short of four rounds of 256-row tiles runs in two K halves, each writing its
+    # own fp32 [T*k][d] partial; the streaming path and large grids keep one
+    T, d, d_ff, E = 300, 512, 1024, 8
+    y_bytes = T * 2 * d * 4
+    tiled = _ws(lib, _cfg(T=T, d=d, d_ff=d_ff, E=E, gemm_path=moe.GEMM_TILED))
+    streaming = _ws(lib, _cfg(T=T, d=d, d_ff=d_ff, E=E, gemm_path=moe.GEMM_STREAMING))
+    assert tiled - streaming == y_bytes + (-y_bytes % 256)
+    # d_ff not a multiple of 128: one K range
+    assert _ws(lib, _cfg(T=T, d=d, d_ff=576, E=E, gemm_path=moe.GEMM_TILED)) == \
+        _ws(lib, _cfg(T=T, d=d, d_ff=576, E=E, gemm_path=moe.GEMM_STREAMING))
+    # 128 experts at T=2048: (2048*2/256 + 128) m-tiles x 32 n-tiles >= 1024 workgroups, one K range
+    big = dict(T=2048, d=8192, d_ff=8192, E=128)
+    assert _ws(lib, _cfg(gemm_path=moe.GEMM_TILED, **big)) == _ws(lib, _cfg(gemm_path=moe.GEMM_STREAMING, **big))
+    # fp32 and INT4 experts never split
+    assert _ws(lib, _cfg(T=T, d=d, d_ff=d_ff, E=E, act_dtype=moe.F32, w_dtype=moe.F32)) == \
+        _ws(lib, _cfg(T=T, d=d, d_ff=d_ff, E=E, act_dtype=moe.F32, w_dtype=moe.F32, gemm_path=moe.GEMM_STREAMING))
