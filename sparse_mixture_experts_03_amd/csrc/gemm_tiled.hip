@@ -28,6 +28,13 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#ifndef MOE_TILED_INT4_MIX
+#define MOE_TILED_INT4_MIX 1  // INT4: expand the next stage's codes between this stage's MFMAs
+#endif
+#ifndef MOE_TILED_INT4_MIX_VALU
+#define MOE_TILED_INT4_MIX_VALU 6  // VALU operations placed after each MFMA
+#endif
+
 namespace moe {
 
 namespace {
@@ -114,6 +121,22 @@ __device__ __forceinline__ void ds_write16(uint32_t addr, uint32_t a, uint32_t b
 // tile segment of 8 bf16 values bf16(q * s), written to LDS at `addr`.
 // q * s is formed exactly as fma(q + 8, s, -8 s) ((q + 8) * s has at most 12
 // significant bits) and rounded once, to nearest even.
+__device__ __forceinline__ uint4 dequant_word(uint32_t word, uint32_t sbits) {
+    const float s = bf16_bits_to_float(sbits);
+    const float m8s = -8.0f * s;
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const uint32_t lo = (word & 0x0f0f0f0fu) ^ 0x08080808u;
+    const uint32_t hi = ((word >> 4) & 0x0f0f0f0fu) ^ 0x08080808u;
+    uint32_t packed[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float a = __builtin_fmaf((float)((lo >> (8 * j)) & 0xffu), s, m8s);
+        const float b = __builtin_fmaf((float)((hi >> (8 * j)) & 0xffu), s, m8s);
+        const bf16x2_t v = {(__bf16)a, (__bf16)b};
+        packed[j] = __builtin_bit_cast(uint32_t, v);
+    }
+    return make_uint4(packed[0], packed[1], packed[2], packed[3]);
+}
 __device__ __forceinline__ void dequant_word_to_lds(uint32_t word, uint32_t sbits, uint32_t addr) {
     const float s = bf16_bits_to_float(sbits);
     const float m8s = -8.0f * s;
@@ -321,7 +344,7 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
     for (int i = 0; i < TI; ++i) wrow_off[i] = frag_offset(wn + 32 * i + r, 0);  // XOR 16*seg selects segment seg
 #pragma unroll
     for (int j = 0; j < TJ; ++j) xrow_off[j] = frag_offset(wm + 32 * j + r, 0);
-    auto compute = [&](int buf) {
+    auto compute = [&](int buf, auto mid) {
         const uint32_t wb = lds_addr(Wt[buf]), xb = lds_addr(Xt[buf]);
         bf16x8 wf[2][TI], xf[2][TJ];
 #pragma unroll
@@ -360,8 +383,10 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
             for (int i = 0; i < TI; ++i)
 #pragma unroll
                 for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32x32x16(wf[ks][i], xf[ks][j], acc[i][j]);
+            if (ks == 0) mid();
         }
     };
+    auto no_mid = [] {};
 
     const int nk = K / kTBK;
     if constexpr (WQ == kBF16) {
@@ -412,12 +437,12 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
             wait_stages(2);
             barrier();
             issue(kt + kStages - 1, (kt + kStages - 1) % kStages);
-            compute(kt % kStages);
+            compute(kt % kStages, no_mid);
         }
         for (; kt < nk; ++kt) {  // drain: every remaining stage is already issued
             wait_stages(nk - kt - 1);
             barrier();
-            compute(kt % kStages);
+            compute(kt % kStages, no_mid);
         }
     } else {
         // INT4: the 16 code bytes per weight-tile row for stage j, C(j), are
@@ -437,9 +462,13 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
         // Step s:
         //   wait for X(s) and for this thread's LDS stores (W(s), written at
         //   step s-1); barrier (publishes stage s, frees the slot of s-1);
-        //   issue X(s+3) into that slot and C(s+4); wait for C(s+1) and
-        //   dequantise it into LDS slot (s+1) % 4 (last read at step s-3,
-        //   before the barrier of step s-2); multiply stage s.
+        //   issue X(s+3) into that slot and C(s+4); wait for C(s+1) and read
+        //   its codes; multiply stage s, expanding those codes to bf16 in
+        //   registers between the MFMAs of its first substep (one wavefront
+        //   per SIMD: VALU work placed between MFMAs runs while they execute,
+        //   6 operations after each MFMA measured best); then store them to
+        //   LDS slot (s+1) % 4 (last read at step s-3, before the barrier of
+        //   step s-2).
         // K is a multiple of 1024: the stages come in whole blocks of 32.
         constexpr int XL = XROWS / 64;  // dispatch-row loads per wavefront per stage
         const char* cbase = reinterpret_cast<const char*>(Wexp);
@@ -524,12 +553,39 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
             barrier();
             if (rem >= 3) issue_xe(s + 3, (J + 3) % kStages);
             if (rem >= 4) issue_c(s + 4);
+            if (MOE_TILED_INT4_MIX && rem >= 1) {
+                // stage s + 1's codes are expanded between the MFMAs of stage s's
+                // first substep and written to their (free) slot after stage s
+                wait_c(rem);
+                if (J == 3) read_scales((s + 1) >> 2);
+                uint32_t w0, w1, w2, w3;
+                ds_read_codes(cread + (uint32_t)((s + 1) % kStages) * 4096, w0, w1, w2, w3);
+                uint4 d0, d1, d2, d3;
+                compute(J, [&] {
+                    d0 = dequant_word(w0, sc0);
+                    d1 = dequant_word(w1, sc1);
+                    d2 = dequant_word(w2, sc2);
+                    d3 = dequant_word(w3, sc3);
+                    // one MFMA, then a share of the expansion's VALU operations, in turn
+#pragma unroll
+                    for (int m = 0; m < TI * TJ; ++m) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, MOE_TILED_INT4_MIX_VALU, 0);
+                    }
+                });
+                const uint32_t wb = lds_addr(Wt[(s + 1) % kStages]) + wdst;
+                ds_write16(wb, d0.x, d0.y, d0.z, d0.w);
+                ds_write16(wb + 4096, d1.x, d1.y, d1.z, d1.w);
+                ds_write16(wb + 8192, d2.x, d2.y, d2.z, d2.w);
+                ds_write16(wb + 12288, d3.x, d3.y, d3.z, d3.w);
+                return;
+            }
             if (rem >= 1) {
                 wait_c(rem);
                 if (J == 3) read_scales((s + 1) >> 2);  // stage s + 1 opens a new group
                 dequant(s + 1);
             }
-            compute(J);
+            compute(J, no_mid);
         };
         int s0 = 0;
         for (; s0 + 8 <= nk; s0 += 4) {  // steady state: every step has 4 or more stages after it
