@@ -156,11 +156,8 @@ __device__ __forceinline__ void dequant_word_to_lds(uint32_t word, uint32_t sbit
 
 // Epilogue: element v of acc[i][j] is D[n = wn + 32i + 8(v/4) + 4h + (v%4)][m = wm + 32j + r];
 // GEMM1 stores bf16 GeLU(D), GEMM2 stores fp32 D, for rows below `rows` and n below N.
-// GELU_ERF: GeLU through erff instead of the cheaper bf16-grade form.  The
-// INT4 kernel keeps it: its main loop holds nearly every register, and with
-// the other form the allocator spills inside the MFMA loop (measured 5x slower).
-// GEMM1 epilogue of the bf16 kernel, staged through LDS (free once the K loop
-// is done): each wavefront writes its activated bf16 tile into a private
+// GEMM1 epilogue of both tiled kernels, staged through LDS (free once the K
+// loop is done): each wavefront writes its activated bf16 tile into a private
 // padded region laid out [dispatch row][weight row], then reads it back in
 // 16-byte chunks, so every store instruction writes whole 128-byte lines of H
 // instead of 16-byte pieces of 32 rows.  Not for SwiGLU (two rows per unit).
@@ -198,7 +195,7 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[TI][TJ], uint
     }
 }
 
-// GEMM2 epilogue of the bf16 kernel (fp32 Y), staged through LDS like GEMM1's
+// GEMM2 epilogue of both tiled kernels (fp32 Y), staged through LDS like GEMM1's
 // in passes of 32 dispatch rows (a wavefront's whole fp32 tile would not fit):
 // every store instruction writes whole rows of Y.  Each wavefront reuses only
 // its own region and its LDS operations execute in order, so one barrier (the
@@ -235,7 +232,7 @@ __device__ __forceinline__ void store_tile_lds_f32(const f32x16 (&acc)[TI][TJ], 
     }
 }
 
-template <int WHICH, int TI, int TJ, int ACT, bool GELU_ERF = false>
+template <int WHICH, int TI, int TJ, int ACT>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TI][TJ], void* __restrict__ out, int N, int n0, int p0,
                                            int rows, int wn, int wm, int r, int h) {
     if constexpr (WHICH == 1 && ACT == kActSwiglu) {
@@ -280,20 +277,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TI][TJ], void* __
                 const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
                 if constexpr (WHICH == 1) {
                     uint2 packed;
-                    float a0, a1, a2, a3;
-                    if constexpr (GELU_ERF && ACT == kActGelu) {
-                        a0 = gelu_erf(v0);
-                        a1 = gelu_erf(v1);
-                        a2 = gelu_erf(v2);
-                        a3 = gelu_erf(v3);
-                    } else {
-                        a0 = act_f(v0, ACT);
-                        a1 = act_f(v1, ACT);
-                        a2 = act_f(v2, ACT);
-                        a3 = act_f(v3, ACT);
-                    }
-                    packed.x = pack_bf16x2(a0, a1);
-                    packed.y = pack_bf16x2(a2, a3);
+                    packed.x = pack_bf16x2(act_f(v0, ACT), act_f(v1, ACT));
+                    packed.y = pack_bf16x2(act_f(v2, ACT), act_f(v3, ACT));
                     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + orow + n) = packed;
                 } else {
                     *reinterpret_cast<float4*>(static_cast<float*>(out) + orow + n) = make_float4(v0, v1, v2, v3);
@@ -601,7 +586,14 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
         step(s0 + 3, 3, 0);
     }
 
-    store_tile<WHICH, TI, TJ, ACT, WQ == kINT4>(acc, out, N, n0, p0, rows, wn, wm, r, h);
+    // the last stage waited for every load (vmcnt 0), so nothing lands in the staging area
+    if constexpr (WHICH == 1 && ACT != kActSwiglu) {
+        store_tile_lds<TI, TJ, ACT, 4>(acc, &Wt[0][0], out, N, n0, p0, rows, wn, wm, r, h, true);
+    } else if constexpr (WHICH == 2) {
+        store_tile_lds_f32<TI, TJ, 4>(acc, &Wt[0][0], static_cast<float*>(out), N, n0, p0, rows, wn, wm, r, h, true);
+    } else {
+        store_tile<WHICH, TI, TJ, ACT>(acc, out, N, n0, p0, rows, wn, wm, r, h);
+    }
 }
 
 // bf16 weights, K-stages of 64: each stage holds 128 bytes (one whole
