@@ -587,6 +587,27 @@ int oracle_expert_ffn(int64_t d, int64_t d_ff, int32_t w_dtype, int32_t act,
 }
 
 /*
+ * One expert linear map, out[n] = sum_i W_e[n][i] * xr[i] for n < N (ascending
+ * i), with W_e an N x K matrix in w_dtype (INT4: q * s exactly, from the bf16
+ * group scales S_e [N][K/128]).  This is each of the two products of step 6
+ * taken alone (P3 §3.2; P1 §5.4 and P2 §2.3 for the INT4 weights).  Returns 0,
+ * or -1 on a bad argument.
+ */
+int oracle_expert_linear(int64_t N, int64_t K, int32_t w_dtype, const double *xr, const void *We,
+                         const void *Se, double *out)
+{
+    if (N < 1 || K < 1 || (w_dtype == ORACLE_INT4_G128 && (K % 128 != 0 || !Se)))
+        return -1;
+    for (int64_t n = 0; n < N; ++n) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < K; ++i)
+            acc += load_w(We, Se, w_dtype, K, n, i) * xr[i];
+        out[n] = acc;
+    }
+    return 0;
+}
+
+/*
  * Layer output for the listed tokens: y[r][c] = sum_j gate_p[t][j] * o_j[c],
  * t = tokens[r], o_j the FFN of expert ids[t][j].  W1/S1/W2/S2 are arrays of E
  * per-expert pointers (an expert no listed token routes to may be NULL).

@@ -73,6 +73,8 @@ class Oracle:
         lib.oracle_capacity_dispatch.restype = ctypes.c_int
         lib.oracle_expert_ffn.argtypes = [_I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P]
         lib.oracle_expert_ffn.restype = ctypes.c_int
+        lib.oracle_expert_linear.argtypes = [_I64, _I64, _I32, _P, _P, _P, _P]
+        lib.oracle_expert_linear.restype = ctypes.c_int
         lib.oracle_forward_tokens.argtypes = [_I64, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _P,
                                               _P, _P, _P, _P, _P, _P, _I64, _P, _P]
         lib.oracle_forward_tokens.restype = ctypes.c_int
@@ -225,6 +227,21 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_expert_ffn rejected its arguments")
         return o
+
+    def expert_linear(self, xr, We, w_dtype, Se=None):
+        """out = We . xr in binary64 for one float64 row xr of length K; We is
+        [N, K] (float32, bf16 bits, or INT4 codes [N, K/2] with bf16 scales Se [N, K/128])."""
+        xr = np.ascontiguousarray(xr, dtype=np.float64)
+        K = xr.shape[0]
+        We = np.ascontiguousarray(We)
+        Se = None if Se is None else np.ascontiguousarray(Se)
+        N = We.shape[0]
+        out = np.zeros(N, dtype=np.float64)
+        rc = self.lib.oracle_expert_linear(N, K, w_dtype, xr.ctypes.data, We.ctypes.data,
+                                           None if Se is None else Se.ctypes.data, out.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle_expert_linear rejected its arguments")
+        return out
 
     def forward_tokens(self, x, ids, gate_p, W1, W2, act_dtype, w_dtype, d_ff, tokens,
                        S1=None, S2=None, act=0):

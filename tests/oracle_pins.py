@@ -121,6 +121,40 @@ def pin_uniform_stream_layout(orc):
         assert orc.gumbel(seed, t, e) == -math.log(-math.log(((r0 >> 11) + 0.5) / 2.0**53))
 
 
+def _philox_block_numpy(seed, t, e):
+    """The four words of the Philox4x64-10 block with key (seed, 0) and counter
+    (t, e, 0, 0), from numpy's Philox bit generator (which pre-increments its
+    counter, so it is started at counter - 1)."""
+    c = [t, e, 0, 0]
+    i = 0
+    while i < 4 and c[i] == 0:
+        c[i] = (1 << 64) - 1
+        i += 1
+    if i < 4:
+        c[i] -= 1
+    bg = np.random.Philox(counter=np.array(c, dtype=np.uint64), key=np.array([seed, 0], dtype=np.uint64))
+    return [int(w) for w in bg.random_raw(4)]
+
+
+def pin_normal_stream_layout(orc):
+    """The Gaussian noise draw for (seed, t, e), exactly: the Box-Muller
+    transform (Box & Muller 1958), sqrt(-2 ln u1) cos(2 pi u2), of u1 and u2
+    built like the Gumbel uniform from words 2 and 3 of the Philox4x64-10
+    block with key (seed, 0) and counter (t, e, 0, 0), the words read here from
+    numpy's Philox bit generator and the transform evaluated with Python's math
+    module (the same C library functions, so the result is bit-identical).  A
+    sine for the cosine, words 2 and 3 swapped, or the Gumbel's word 0 reused
+    all change the value."""
+    keys = [(0, 0, 0), (7, 3, 1), (17, 1999, 9), (2**40 + 1, 12345, 127), (5, 2**33, 255), (2**64 - 1, 1, 2)]
+    for seed, t, e in keys:
+        r = _philox_block_numpy(seed, t, e)
+        u1 = ((r[2] >> 11) + 0.5) / 2.0**53
+        u2 = ((r[3] >> 11) + 0.5) / 2.0**53
+        want = math.sqrt(-2.0 * math.log(u1)) * math.cos(2.0 * math.pi * u2)
+        got = orc.normal(seed, t, e)
+        assert got == want, (seed, t, e, got, want)
+
+
 # ----------------------------------------------------------------------- GeLU
 
 def pin_gelu(orc):
@@ -514,6 +548,41 @@ def pin_silu_and_swiglu_experts(orc):
     g, u = G @ x, U @ x
     want = npref.dequant_int4(c2, s2) @ (g * special.expit(g) * u)
     assert np.max(np.abs(o - want)) <= 1e-13 * np.max(np.abs(want))
+
+
+def pin_expert_linear(orc):
+    """One expert linear map alone (each of the FFN's two products): with unit
+    scales and integer inputs an INT4 map is an exact integer matrix product
+    (numpy int64 matmul); with random codes and scales it equals numpy's
+    float64 matmul on the dequantised weights q * s, and with bf16 and fp32
+    weights numpy's matmul on the widened values; one-hot inputs pick one
+    column exactly (every group's own scale)."""
+    r = _rng(41)
+    N, K = 96, 384
+    q = r.integers(-8, 8, size=(N, K))
+    codes = npref.pack_int4(q)
+    ones = _bf16(np.ones((N, K // 128)))
+    xi = r.integers(-5, 6, size=K)
+    got = orc.expert_linear(xi.astype(np.float64), codes, INT4_G128, Se=ones)
+    assert np.array_equal(got, (q @ xi).astype(np.float64))
+    sc = _bf16(r.uniform(0.001, 0.05, size=(N, K // 128)))
+    Wf = npref.dequant_int4(codes, sc)
+    x = r.standard_normal(K)
+    got = orc.expert_linear(x, codes, INT4_G128, Se=sc)
+    want = Wf @ x
+    assert np.max(np.abs(got - want)) <= 1e-14 * np.max(np.abs(want))
+    for c in (0, 127, 128, 200, 383):
+        e = np.zeros(K)
+        e[c] = 1.0
+        assert np.array_equal(orc.expert_linear(e, codes, INT4_G128, Se=sc), Wf[:, c])
+    wb = _bf16(r.standard_normal((N, K)) / math.sqrt(K))
+    got = orc.expert_linear(x, wb, BF16)
+    want = npref.bf16_bits_to_f64(wb) @ x
+    assert np.max(np.abs(got - want)) <= 1e-14 * np.max(np.abs(want))
+    wf = (r.standard_normal((N, K)) / math.sqrt(K)).astype(np.float32)
+    got = orc.expert_linear(x, wf, F32)
+    want = wf.astype(np.float64) @ x
+    assert np.max(np.abs(got - want)) <= 1e-14 * np.max(np.abs(want))
 
 
 def pin_int4_decode(orc):

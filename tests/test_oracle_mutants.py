@@ -77,6 +77,13 @@ MUTANTS = [
      "return sqrt(-log(u1)) * cos(two_pi * u2);"),
     ("gaussian reuses the gumbel word", "double u1 = ((double)(r[2] >> 11) + 0.5)",
      "double u1 = ((double)(r[0] >> 11) + 0.5)"),
+    ("box-muller sine for cosine", "return sqrt(-2.0 * log(u1)) * cos(two_pi * u2);",
+     "return sqrt(-2.0 * log(u1)) * sin(two_pi * u2);"),
+    ("gaussian words 2 and 3 swapped",
+     "(r[2] >> 11) + 0.5) * (1.0 / 9007199254740992.0);\n    double u2 = ((double)(r[3] >> 11)",
+     "(r[3] >> 11) + 0.5) * (1.0 / 9007199254740992.0);\n    double u2 = ((double)(r[2] >> 11)"),
+    ("expert linear map skips its last input", "for (int64_t i = 0; i < K; ++i)\n            acc += load_w(We",
+     "for (int64_t i = 0; i + 1 < K; ++i)\n            acc += load_w(We"),
     ("product term pairs fraction with itself", "fp += fraction[e] * mean_prob[e];",
      "fp += fraction[e] * fraction[e];"),
     ("mean prob not averaged", "mean_prob[e] /= (double)T;", "mean_prob[e] /= (double)E;"),
