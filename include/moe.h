@@ -18,7 +18,9 @@
  *  - Pointers named as device pointers must be device memory of the current
  *    HIP device, owned by the caller, 16-byte aligned, and must not alias an
  *    output.  The library allocates nothing and keeps no state besides a
- *    thread-local copy of the last HIP error code.
+ *    thread-local copy of the last HIP error code, and, for
+ *    moe_forward_no_alloc only, one static device scratch array per GPU and
+ *    its address per device.
  *  - Work is enqueued on `stream` (NULL = the null stream) and the call returns
  *    without waiting; outputs are valid once the stream has been synchronised.
  *    Nothing is copied between host and device inside a call.
@@ -164,6 +166,28 @@ moe_status moe_forward(const moe_config *cfg, const void *x, const void *Wg, con
                        const void *W2, const void *W2_scales, int64_t W2_expert_stride,
                        void *y, int32_t *expert_ids, float *gate_weights, int32_t *counts,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same layer, arguments and outputs, but no workspace argument.  The workspace
+ * is the library's own static device array of MOE_STATIC_SCRATCH_BYTES, one
+ * per GPU, held from the library's load on that GPU until the process ends;
+ * its address is looked up once per device on the first call there (with that
+ * device current).  Nothing is allocated or freed.  Every call on one GPU
+ * shares that GPU's array and leaves its contents behind (no kernel relies on
+ * them being zero): calls that overlap on one GPU (different streams, or
+ * different host threads without ordering) race on it and must be serialised
+ * by the caller.  A configuration whose moe_workspace_size() exceeds
+ * MOE_STATIC_SCRATCH_BYTES returns MOE_ERR_WORKSPACE_TOO_SMALL with nothing
+ * enqueued; other errors as moe_forward.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (64u * 1024u * 1024u)
+moe_status moe_forward_no_alloc(const moe_config *cfg, const void *x, const void *Wg, const float *router_bias,
+                                const void *router_W_in, const float *router_b_in, const void *W1,
+                                const void *W1_scales, int64_t W1_expert_stride, const void *W2,
+                                const void *W2_scales, int64_t W2_expert_stride, void *y, int32_t *expert_ids,
+                                float *gate_weights, int32_t *counts, hipStream_t stream);
 
 /*
  * Router stage (P2 §2.2 steps 1-3; P1 §3.1; P5 §3.2): logits accumulated in

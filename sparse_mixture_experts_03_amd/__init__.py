@@ -7,13 +7,13 @@ allocates outputs and workspace with torch and calls `moe_forward`.
 from . import binding
 from .binding import (ACT_GELU, ACT_SILU, ACT_SWIGLU, BF16, CAPACITY_DROP, CAPACITY_REROUTE, F32, GEMM_AUTO, GEMM_STREAMING, GEMM_TILED, INT4_G128,
                       MoeConfig, MoeError, config,
-                      moe_combine, moe_forward, moe_grouped_gemm, moe_permute, moe_router, moe_router_encoder,
+                      moe_combine, moe_forward, moe_forward_no_alloc, moe_grouped_gemm, moe_permute, moe_router, moe_router_encoder,
                       moe_router_stats,
                       moe_router_stats_workspace_size, moe_router_workspace_size, moe_workspace_size)
 
 __all__ = ["binding", "BF16", "F32", "INT4_G128", "GEMM_AUTO", "GEMM_STREAMING", "GEMM_TILED", "CAPACITY_DROP",
            "CAPACITY_REROUTE", "ACT_GELU", "ACT_SILU", "ACT_SWIGLU", "MoeConfig",
-           "MoeError", "config", "moe_forward", "moe_router", "moe_permute", "moe_grouped_gemm", "moe_combine",
+           "MoeError", "config", "moe_forward", "moe_forward_no_alloc", "moe_router", "moe_permute", "moe_grouped_gemm", "moe_combine",
            "moe_workspace_size", "moe_router_workspace_size", "moe_router_stats", "moe_router_stats_workspace_size",
            "moe_router_encoder",
            "MoELayerForward"]

@@ -19,7 +19,7 @@ ACT_GELU, ACT_SILU, ACT_SWIGLU = 0, 1, 2
 
 EXPORTS = ("moe_workspace_size", "moe_router_workspace_size", "moe_forward", "moe_router", "moe_permute",
            "moe_grouped_gemm", "moe_combine", "moe_router_stats_workspace_size", "moe_router_stats",
-           "moe_router_encoder", "moe_status_string", "moe_last_hip_error")
+           "moe_router_encoder", "moe_forward_no_alloc", "moe_status_string", "moe_last_hip_error")
 
 
 class MoeConfig(ctypes.Structure):
@@ -70,6 +70,7 @@ def load(path=LIB_PATH):
     lib.moe_workspace_size.argtypes = [CFG, ctypes.POINTER(SZ)]
     lib.moe_router_workspace_size.argtypes = [CFG, ctypes.POINTER(SZ)]
     lib.moe_forward.argtypes = [CFG, P, P, P, P, P, P, P, I64, P, P, I64, P, P, P, P, P, SZ, P]
+    lib.moe_forward_no_alloc.argtypes = [CFG, P, P, P, P, P, P, P, I64, P, P, I64, P, P, P, P, P]
     lib.moe_router.argtypes = [CFG, P, P, P, P, P, P, P, P, SZ, P]
     lib.moe_router_encoder.argtypes = [CFG, P, P, P, P, P, SZ, P]
     lib.moe_permute.argtypes = [CFG, P, P, P, P, P, P]
@@ -79,7 +80,7 @@ def load(path=LIB_PATH):
     lib.moe_router_stats.argtypes = [CFG, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     for name in ("moe_workspace_size", "moe_router_workspace_size", "moe_forward", "moe_router", "moe_permute",
                  "moe_grouped_gemm", "moe_combine", "moe_router_stats_workspace_size", "moe_router_stats",
-                 "moe_router_encoder"):
+                 "moe_router_encoder", "moe_forward_no_alloc"):
         getattr(lib, name).restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -144,6 +145,17 @@ def moe_forward(cfg, x, Wg, bias, W1, W1_scales, W2, W2_scales, y, expert_ids, g
                             _ptr(y), _ptr(expert_ids), _ptr(gate_weights), _ptr(counts), _ptr(workspace), ws_bytes,
                             _stream(stream))
     _check(st, "moe_forward")
+
+
+def moe_forward_no_alloc(cfg, x, Wg, bias, W1, W1_scales, W2, W2_scales, y, expert_ids, gate_weights, counts,
+                         stream=None, W1_stride=None, W2_stride=None, W_in=None, b_in=None):
+    st = load().moe_forward_no_alloc(ctypes.byref(cfg), _ptr(x), _ptr(Wg), _ptr(bias), _ptr(W_in), _ptr(b_in),
+                                     _ptr(W1), _ptr(W1_scales),
+                                     W1_stride if W1_stride is not None else _expert_stride(W1),
+                                     _ptr(W2), _ptr(W2_scales),
+                                     W2_stride if W2_stride is not None else _expert_stride(W2),
+                                     _ptr(y), _ptr(expert_ids), _ptr(gate_weights), _ptr(counts), _stream(stream))
+    _check(st, "moe_forward_no_alloc")
 
 
 def moe_router(cfg, x, Wg, bias, expert_ids, gate_weights, workspace, stream=None, W_in=None, b_in=None):

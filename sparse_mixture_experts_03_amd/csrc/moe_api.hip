@@ -9,11 +9,18 @@
 // work from them.
 #include <algorithm>
 #include <math.h>
+#include <mutex>
 #include <string.h>
 
 #include "../../include/moe.h"
 #include "common.hpp"
 #include "launch.hpp"
+
+// Device scratch of moe_forward_no_alloc: one copy per GPU, held from the
+// library's load on that GPU until the process ends.  Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in for the
+// symbol); it uses the per-device address from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -296,6 +303,29 @@ hipError_t run_router(const moe_config& c, const void* x, const void* W_in, cons
     return moe::launch_router(r, stream);
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of `scratch`, looked up once per device with that
+// device current (the first no-alloc call on it).
+hipError_t static_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -374,6 +404,22 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
     e = moe::launch_combine(Y, pos, gate_weights, y, c.T, c.d, c.k, c.act_dtype, stream, Y2);
     if (e != hipSuccess) return hip_fail(e);
     return MOE_OK;
+}
+
+moe_status moe_forward_no_alloc(const moe_config* cfg, const void* x, const void* Wg, const float* router_bias,
+                                const void* router_W_in, const float* router_b_in, const void* W1,
+                                const void* W1_scales, int64_t W1_expert_stride, const void* W2,
+                                const void* W2_scales, int64_t W2_expert_stride, void* y, int32_t* expert_ids,
+                                float* gate_weights, int32_t* counts, hipStream_t stream) {
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    if (layout_of(*cfg).total > (size_t)MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    hipError_t e = static_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e);
+    return moe_forward(cfg, x, Wg, router_bias, router_W_in, router_b_in, W1, W1_scales, W1_expert_stride, W2,
+                       W2_scales, W2_expert_stride, y, expert_ids, gate_weights, counts, ws,
+                       (size_t)MOE_STATIC_SCRATCH_BYTES, stream);
 }
 
 moe_status moe_router(const moe_config* cfg, const void* x, const void* Wg, const float* router_bias,
