@@ -3,6 +3,12 @@
 Every .hip file under csrc/ is compiled to an object in _build/ and the objects
 are linked into one shared library next to this file.  Packed fp32 VALU
 instructions are disabled (-packed-fp32-ops) for all device code.
+
+The tiled GEMM kernels read LDS through inline asm whose results the compiler
+sees as written at issue; their schedules were validated on the GPU with the
+compiler named in VALIDATED_COMPILER.  Another hipcc still builds, with a
+warning, and the parity tests must then be run again before its binaries are
+trusted.
 """
 import concurrent.futures
 import os
@@ -17,6 +23,7 @@ LIB = os.path.join(HERE, "libmoe_mi355x.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+VALIDATED_COMPILER = "AMD clang version 22.0.0git (https://github.com/RadeonOpenCompute/llvm-project roc-7.2.0 26014"
 FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
@@ -44,9 +51,17 @@ def _compile(src):
     return obj, msgs
 
 
+def compiler_version():
+    r = subprocess.run([HIPCC, "--version"], capture_output=True, text=True)
+    return r.stdout
+
+
 def build(verbose=True, jobs=None):
     """Compile all sources and link the library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
+    if VALIDATED_COMPILER not in compiler_version():
+        print(f"warning: {HIPCC} is not the compiler the kernels were validated with "
+              f"({VALIDATED_COMPILER}); run the GPU parity tests before using this build", file=sys.stderr)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:

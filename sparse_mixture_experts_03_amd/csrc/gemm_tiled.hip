@@ -28,12 +28,6 @@
 #include "common.hpp"
 #include "launch.hpp"
 
-#ifndef MOE_TILED_INT4_MIX
-#define MOE_TILED_INT4_MIX 1  // INT4: expand the next stage's codes between this stage's MFMAs
-#endif
-#ifndef MOE_TILED_INT4_MIX_VALU
-#define MOE_TILED_INT4_MIX_VALU 6  // VALU operations placed after each MFMA
-#endif
 
 namespace moe {
 
@@ -44,6 +38,13 @@ constexpr int kTBM = 256;   // dispatch rows per tile
 constexpr int kTBK = 32;    // K per stage (64 bytes of every tile row)
 constexpr int kStages = 4;  // LDS ring: stage k+3 streams in while stage k is multiplied
 constexpr int kTileBytes = 256 * kTBK * 2;  // 16 KB per operand per stage
+// INT4 kernel: 4 + 4 stages of 16 KB, the code ring (4 x 4 KB) and the scale ring (2 x 4 KB).
+constexpr int kInt4LdsBytes = 2 * kStages * kTileBytes + kStages * 4096 + 2 * 4096;
+// bf16 kernel: 2 weight + 3 dispatch-row stages of 32 KB, all of a CU's LDS.
+constexpr int kBf16LdsBytes = 5 * 32768;
+// INT4: VALU operations of the next stage's code expansion placed after each MFMA of this stage
+// (other group sizes spill).
+constexpr int kInt4MixValu = 6;
 
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
@@ -161,13 +162,13 @@ __device__ __forceinline__ void dequant_word_to_lds(uint32_t word, uint32_t sbit
 // padded region laid out [dispatch row][weight row], then reads it back in
 // 16-byte chunks, so every store instruction writes whole 128-byte lines of H
 // instead of 16-byte pieces of 32 rows.  Not for SwiGLU (two rows per unit).
-template <int TI, int TJ, int ACT, int NWAVE>
+template <int TI, int TJ, int ACT, int NWAVE, int LDS_BYTES>
 __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[TI][TJ], uint8_t* lds, void* __restrict__ out,
                                                int N, int n0, int p0, int rows, int wn, int wm, int r, int h,
                                                bool math) {
     constexpr int NW = 32 * TI, MW = 32 * TJ;  // this wavefront's weight rows x dispatch rows
     constexpr int STRIDE = NW * 2 + 16;        // padded LDS row in bytes (16-byte aligned)
-    static_assert(NWAVE * MW * STRIDE <= 5 * 32768, "epilogue staging exceeds the kernel's LDS");
+    static_assert(NWAVE * MW * STRIDE <= LDS_BYTES, "epilogue staging exceeds the kernel's LDS");
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     uint8_t* wl = lds + wave * (MW * STRIDE);
     barrier();  // every wavefront has finished reading the last stage
@@ -200,13 +201,13 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[TI][TJ], uint
 // every store instruction writes whole rows of Y.  Each wavefront reuses only
 // its own region and its LDS operations execute in order, so one barrier (the
 // last stage is no longer read) is enough.
-template <int TI, int TJ, int NWAVE>
+template <int TI, int TJ, int NWAVE, int LDS_BYTES>
 __device__ __forceinline__ void store_tile_lds_f32(const f32x16 (&acc)[TI][TJ], uint8_t* lds, float* __restrict__ out,
                                                    int N, int n0, int p0, int rows, int wn, int wm, int r, int h,
                                                    bool math) {
     constexpr int NW = 32 * TI;         // this wavefront's weight rows (columns of Y)
     constexpr int STRIDE = NW * 4 + 16;  // padded LDS row in bytes
-    static_assert(NWAVE * 32 * STRIDE <= 5 * 32768, "epilogue staging exceeds the kernel's LDS");
+    static_assert(NWAVE * 32 * STRIDE <= LDS_BYTES, "epilogue staging exceeds the kernel's LDS");
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     uint8_t* wl = lds + wave * (32 * STRIDE);
     constexpr int CH = NW * 4 / 16, RPI = 64 / CH;  // 16-byte chunks per row, rows per instruction
@@ -538,7 +539,7 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
             barrier();
             if (rem >= 3) issue_xe(s + 3, (J + 3) % kStages);
             if (rem >= 4) issue_c(s + 4);
-            if (MOE_TILED_INT4_MIX && rem >= 1) {
+            if (rem >= 1) {
                 // stage s + 1's codes are expanded between the MFMAs of stage s's
                 // first substep and written to their (free) slot after stage s
                 wait_c(rem);
@@ -555,7 +556,7 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
 #pragma unroll
                     for (int m = 0; m < TI * TJ; ++m) {
                         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x002, MOE_TILED_INT4_MIX_VALU, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, kInt4MixValu, 0);
                     }
                 });
                 const uint32_t wb = lds_addr(Wt[(s + 1) % kStages]) + wdst;
@@ -588,9 +589,9 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
 
     // the last stage waited for every load (vmcnt 0), so nothing lands in the staging area
     if constexpr (WHICH == 1 && ACT != kActSwiglu) {
-        store_tile_lds<TI, TJ, ACT, 4>(acc, &Wt[0][0], out, N, n0, p0, rows, wn, wm, r, h, true);
+        store_tile_lds<TI, TJ, ACT, 4, kInt4LdsBytes>(acc, &Wt[0][0], out, N, n0, p0, rows, wn, wm, r, h, true);
     } else if constexpr (WHICH == 2) {
-        store_tile_lds_f32<TI, TJ, 4>(acc, &Wt[0][0], static_cast<float*>(out), N, n0, p0, rows, wn, wm, r, h, true);
+        store_tile_lds_f32<TI, TJ, 4, kInt4LdsBytes>(acc, &Wt[0][0], static_cast<float*>(out), N, n0, p0, rows, wn, wm, r, h, true);
     } else {
         store_tile<WHICH, TI, TJ, ACT>(acc, out, N, n0, p0, rows, wn, wm, r, h);
     }
@@ -745,9 +746,9 @@ __device__ __forceinline__ void tile_gemm_bf16(uint8_t* lds, const uint16_t* __r
     }
     mma_sub(dw, dx);
     if constexpr (WHICH == 1 && ACT != kActSwiglu) {
-        store_tile_lds<TI, TJ, ACT, NWAVE>(acc, lds, out, N, n0, p0, rows, wn, wm, r, h, math);
+        store_tile_lds<TI, TJ, ACT, NWAVE, kBf16LdsBytes>(acc, lds, out, N, n0, p0, rows, wn, wm, r, h, math);
     } else if constexpr (WHICH == 2) {
-        store_tile_lds_f32<TI, TJ, NWAVE>(acc, lds, static_cast<float*>(out), N, n0, p0, rows, wn, wm, r, h, math);
+        store_tile_lds_f32<TI, TJ, NWAVE, kBf16LdsBytes>(acc, lds, static_cast<float*>(out), N, n0, p0, rows, wn, wm, r, h, math);
     } else {
         if (math) store_tile<WHICH, TI, TJ, ACT>(acc, out, N, n0, p0, rows, wn, wm, r, h);
     }
@@ -762,10 +763,8 @@ __global__ void __launch_bounds__(256, 1)
 gemm_tiled_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
                   const int32_t* __restrict__ offsets, int E, const uint8_t* __restrict__ W, int64_t W_stride,
                   const uint16_t* __restrict__ Wsc, void* __restrict__ out, int N, int K, int ntiles_n, int rows_lo) {
-    // 4 + 4 stages of 16 KB, the code ring (4 x 4 KB) and the scale ring (2 x 4 KB).
     static_assert(WQ == kINT4, "bf16 experts use gemm_tiled_bf16_kernel");
-    constexpr int kLdsBytes = 2 * kStages * kTileBytes + kStages * 4096 + 2 * 4096;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kInt4LdsBytes];
     uint8_t (*Wt)[kTileBytes] = reinterpret_cast<uint8_t (*)[kTileBytes]>(smem);
     uint8_t (*Xt)[kTileBytes] = reinterpret_cast<uint8_t (*)[kTileBytes]>(smem + kStages * kTileBytes);
     uint8_t (*Ct)[4096] = reinterpret_cast<uint8_t (*)[4096]>(smem + 2 * kStages * kTileBytes);     // INT4 code ring
@@ -807,7 +806,7 @@ gemm_tiled_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict
                        const int32_t* __restrict__ offsets, int E, const uint8_t* __restrict__ W, int64_t W_stride,
                        void* __restrict__ out, int N, int K, int ntiles_n, int rows_lo, int ksplit,
                        int64_t split_stride) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[5 * 32768];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kBf16LdsBytes];
     asm volatile("" ::: "a0");  // accumulators in AGPRs (see gemm_tiled_kernel)
     const MtileScan scan = scan_mtiles(offsets, E, kTBM, rows_lo, 0x7fffffff);
     // ksplit = 2 (GEMM2 only): workgroups 2 b and 2 b + 1 take the two K halves

@@ -23,10 +23,7 @@ namespace {
 
 constexpr int kRouterThreads = 256;
 constexpr int kTT = 8;           // tokens per partial-logit workgroup
-#ifndef MOE_ROUTER_ROW_CHUNK
-#define MOE_ROUTER_ROW_CHUNK 128
-#endif
-constexpr int kRowChunk = MOE_ROUTER_ROW_CHUNK;  // input rows staged in LDS per step
+constexpr int kRowChunk = 128;   // input rows staged in LDS per step
 constexpr int kMaxSplits = 64;
 
 // Eight consecutive experts of one Wg row (Wg is d x E row-major), as floats.

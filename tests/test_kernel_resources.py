@@ -1,11 +1,18 @@
-"""Register use of the tiled grouped-GEMM kernels, from the compiler's resource
-report (hipcc for gfx950 on the host, no GPU).
+"""Register and scratch use of the grouped-GEMM kernels, from the compiler's
+resource report (hipcc for gfx950 on the host, no GPU), and the compiler the
+kernels were validated with.
 
-The tiled kernels read their MFMA fragments from LDS with inline-asm loads
-whose completion they await explicitly; the compiler takes such an output
-register as written when the load is issued.  A spill (or copy) of one of
-those registers before its wait would store a stale value, so none of these
-kernels may spill."""
+The tiled kernels read their MFMA fragments (and the INT4 kernel its codes and
+scales) from LDS with inline-asm loads whose completion they await
+explicitly; the compiler takes such an output register as written when the
+load is issued.  A spill or copy of one of those registers before its wait
+would store a stale value, so no tiled or streaming instantiation may spill a
+register or use scratch memory at all (the streaming kernels are held to the
+same rule: their pipelines are tuned on the assumption that nothing lives in
+scratch).  The inline-asm reads were validated on the GPU with the compiler
+named in build.VALIDATED_COMPILER; another compiler builds (with a warning),
+but this test then fails, so that the parity tests are run again before its
+binaries are trusted."""
 import os
 import re
 import shutil
@@ -15,14 +22,18 @@ import pytest
 
 from sparse_mixture_experts_03_amd import build as hip_build
 
-SRC = os.path.join(hip_build.CSRC, "gemm_tiled.hip")
+SOURCES = ["gemm_tiled.hip", "gemm_stream.hip"]
+
+
+def _hipcc():
+    if not os.path.exists(hip_build.HIPCC) and shutil.which("hipcc") is None:
+        pytest.skip("hipcc not available")
+    return hip_build.HIPCC
 
 
 def resource_report(src, tmp_path):
-    if not os.path.exists(hip_build.HIPCC) and shutil.which("hipcc") is None:
-        pytest.skip("hipcc not available")
-    out = os.path.join(str(tmp_path), "k.o")
-    r = subprocess.run([hip_build.HIPCC, *hip_build.FLAGS, "-c", src, "-o", out,
+    out = os.path.join(str(tmp_path), os.path.basename(src) + ".o")
+    r = subprocess.run([_hipcc(), *hip_build.FLAGS, "-c", src, "-o", out,
                         "-Rpass-analysis=kernel-resource-usage"], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-2000:]
     kernels = {}
@@ -39,10 +50,21 @@ def resource_report(src, tmp_path):
     return kernels
 
 
-def test_tiled_kernels_do_not_spill(tmp_path):
-    kernels = resource_report(SRC, tmp_path)
-    tiled = {k: v for k, v in kernels.items() if "gemm_tiled" in k and "kernel" in k}
-    assert len(tiled) >= 8, sorted(kernels)  # bf16 and INT4, GEMM1 (three activations) and GEMM2
-    for name, res in tiled.items():
+@pytest.mark.parametrize("src", SOURCES)
+def test_gemm_kernels_do_not_spill_or_use_scratch(tmp_path, src):
+    kernels = resource_report(os.path.join(hip_build.CSRC, src), tmp_path)
+    gemm = {k: v for k, v in kernels.items() if "gemm_" in k and "kernel" in k}
+    # tiled: GEMM1 with three activations and GEMM2, for INT4 and for bf16 weights; streaming: every
+    # (weight type, GEMM, tile shape) instantiation the launcher can choose
+    assert len(gemm) >= {"gemm_tiled.hip": 8, "gemm_stream.hip": 8}[src], sorted(kernels)
+    for name, res in gemm.items():
+        assert "ScratchSize" in res, (name, res)
         assert res.get("VGPRs Spill", 0) == 0, (name, res)
         assert res.get("SGPRs Spill", 0) == 0, (name, res)
+        assert res["ScratchSize"] == 0, (name, res)
+
+
+def test_compiler_is_the_validated_one():
+    _hipcc()
+    version = hip_build.compiler_version()
+    assert hip_build.VALIDATED_COMPILER in version, version
