@@ -27,49 +27,25 @@
 #include "common.hpp"
 #include "launch.hpp"
 
-#ifndef MOE_STREAM_NB_BF16
-#define MOE_STREAM_NB_BF16 1   // 16-row weight tiles per workgroup, bf16 experts
-#endif
-#ifndef MOE_STREAM_NB_INT4
-#define MOE_STREAM_NB_INT4 4   // 16-row weight tiles per workgroup, INT4 experts
-#endif
-#ifndef MOE_STREAM_STAGE_BF16
-#define MOE_STREAM_STAGE_BF16 256  // bytes of each weight row per pipeline stage, bf16 experts
-#endif
-#ifndef MOE_STREAM_STAGE_INT4
-#define MOE_STREAM_STAGE_INT4 256  // bytes of each weight row per pipeline stage, INT4 experts
-#endif
-#ifndef MOE_STREAM_NT
-#define MOE_STREAM_NT 1        // 1: non-temporal hint on weight loads
-#endif
-#ifndef MOE_STREAM_NB_INT4_16
-#define MOE_STREAM_NB_INT4_16 4  // the same for 16-row dispatch tiles
-#endif
-#ifndef MOE_STREAM_STAGE_INT4_16
-#define MOE_STREAM_STAGE_INT4_16 128  // the same for 16-row dispatch tiles
-#endif
-#ifndef MOE_STREAM_XPRE
-#define MOE_STREAM_XPRE 1      // 1: INT4, 16-row dispatch tiles: a stage's activations loaded before the next weights
-#endif
-
 namespace moe {
 
 namespace {
 
 constexpr int kStreamBM = 16;  // dispatch rows per tile
+// Tile shapes (measured per weight type and dispatch-tile height): 16-row weight tiles per workgroup and bytes
+// of each weight row per pipeline stage.
+constexpr int kNbBf16 = 1, kStageBf16 = 256;          // bf16 experts, 16-row dispatch tiles
+constexpr int kNbInt4x16 = 4, kStageInt4x16 = 128;    // INT4 experts, 16-row dispatch tiles
+constexpr int kNbInt4 = 4, kStageInt4 = 256;          // INT4 experts, 32- and 64-row dispatch tiles
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Weight loads: read once, never reused.
+// Weight loads: read once, never reused (non-temporal).
 __device__ __forceinline__ uint4 ldw16(const void* p) {
-#if MOE_STREAM_NT
     u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
-#else
-    return ld16(p);
-#endif
 }
 
 // Eight signed INT4 codes (one 32-bit word, code i in bits 4i..4i+3) to eight
@@ -92,9 +68,6 @@ __device__ __forceinline__ bf16x8 int4x8_to_bf16_offset136(uint32_t w) {
     return as_bf16x8(r);
 }
 
-#ifndef MOE_STREAM_INT4_KPERM
-#define MOE_STREAM_INT4_KPERM 1
-#endif
 // The same eight codes in a permuted K order that needs no byte permute:
 // output dword j holds codes j (bits 4j..4j+3 of w, low half) and j + 4 (bits
 // 16+4j.., high half), i.e. K slots (0,4,1,5,2,6,3,7); the activation operand
@@ -267,7 +240,7 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
 
     // Two register buffers: stage st + 1 is in flight while stage st is parked
     // in LDS and multiplied.
-    constexpr bool XP = WQ == kINT4 && MOE_STREAM_XPRE && MT == 1;
+    constexpr bool XP = WQ == kINT4 && MT == 1;
     constexpr int XG = XP ? GPS : 1;
     uint4 xs[XG][MT][4];
     auto xload = [&](int st) {
@@ -316,7 +289,7 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
             const int gbase = (int)(s0 / 64);
             // the permuted-K dequantisation where registers allow it (16-row dispatch
             // tiles; with 32 or 64 rows its activation copies would spill)
-            constexpr bool KPERM = MOE_STREAM_INT4_KPERM && MT == 1;
+            constexpr bool KPERM = MT == 1;
             scales_t sv[NB][4];  // this lane's output rows 16 b + 4 g + i
 #pragma unroll
             for (int b = 0; b < NB; ++b)
@@ -486,16 +459,17 @@ hipError_t launch_stream_nb(const GemmArgs& a, hipStream_t stream) {
 // register double buffer stays at 8 loads per lane).  INT4: 64 weight rows.
 hipError_t launch_stream_bf16(const GemmArgs& a, hipStream_t stream) {
     // SwiGLU pairs a gate and an up block of 16 rows inside one workgroup: NB even
-    if (a.stream_mt == 1 && a.which == 1 && a.act == kActSwiglu && MOE_STREAM_NB_BF16 % 2 != 0)
-        return launch_stream_nb<kBF16, 2, 1, 128>(a, stream);
-    if (a.stream_mt == 1) return launch_stream_nb<kBF16, MOE_STREAM_NB_BF16, 1, MOE_STREAM_STAGE_BF16>(a, stream);
+    if constexpr (kNbBf16 % 2 != 0) {
+        if (a.stream_mt == 1 && a.which == 1 && a.act == kActSwiglu) return launch_stream_nb<kBF16, 2, 1, 128>(a, stream);
+    }
+    if (a.stream_mt == 1) return launch_stream_nb<kBF16, kNbBf16, 1, kStageBf16>(a, stream);
     if (a.stream_mt == 2) return launch_stream_nb<kBF16, 2, 2, 128>(a, stream);
     return launch_stream_nb<kBF16, 4, 4, 128>(a, stream);
 }
 hipError_t launch_stream_int4(const GemmArgs& a, hipStream_t stream) {
-    if (a.stream_mt == 1) return launch_stream_nb<kINT4, MOE_STREAM_NB_INT4_16, 1, MOE_STREAM_STAGE_INT4_16>(a, stream);
-    if (a.stream_mt == 2) return launch_stream_nb<kINT4, MOE_STREAM_NB_INT4, 2, MOE_STREAM_STAGE_INT4>(a, stream);
-    return launch_stream_nb<kINT4, MOE_STREAM_NB_INT4, 4, MOE_STREAM_STAGE_INT4>(a, stream);
+    if (a.stream_mt == 1) return launch_stream_nb<kINT4, kNbInt4x16, 1, kStageInt4x16>(a, stream);
+    if (a.stream_mt == 2) return launch_stream_nb<kINT4, kNbInt4, 2, kStageInt4>(a, stream);
+    return launch_stream_nb<kINT4, kNbInt4, 4, kStageInt4>(a, stream);
 }
 
 }  // namespace

@@ -37,6 +37,17 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_no_undefined_library_symbols():
+    """Every symbol of the library's own namespace is defined in it: a kernel
+    whose launch stub the compiler's host pass failed to emit builds and links
+    (as an undefined symbol of the shared library) but cannot be loaded."""
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libmoe_mi355x.so is not built (run __graft_entry__.build())")
+    r = subprocess.run(["nm", "-D", "--undefined-only", binding.LIB_PATH], capture_output=True, text=True, check=True)
+    own = [l.split()[-1] for l in r.stdout.splitlines() if "_ZN3moe" in l or "moe_" in l]
+    assert own == [], own
+
+
 def test_config_struct_layout(tmp_path):
     """The ctypes mirror of moe_config matches the C compiler's layout."""
     fields = [f for f, _ in binding.MoeConfig._fields_]

@@ -132,6 +132,10 @@ FORWARD_CASES = {
     # an odd number of scale groups per row (scales read one by one)
     "int4-T12-d640-dff1152-E8": (case(12, 640, 1152, 8, w=INT4), [moe.GEMM_STREAMING]),
     "int4-T5-d1152-dff640-E4-k1": (case(5, 1152, 640, 4, k=1, w=INT4), [moe.GEMM_STREAMING]),
+    # 16-row dispatch tiles with K a multiple of 256 (the LDS-ring kernel): K = 5120 gives every wavefront
+    # five stages (one full turn of the ring, then one), K = 2304 gives 2, 2, 2 and 3; SwiGLU on the same path
+    "int4-T16-d5120-dff2304-E8": (case(16, 5120, 2304, 8, w=INT4), [moe.GEMM_STREAMING]),
+    "int4-T7-d2304-dff5120-E8-swiglu": (case(7, 2304, 5120, 8, w=INT4, ffn=SWIGLU), [moe.GEMM_STREAMING]),
     "int4-T200-d384-dff768-E8-gumbel": (case(200, 384, 768, 8, w=INT4, tau=0.5, gumbel=True), [moe.GEMM_AUTO]),
     # K = 1024 and 3072: one and three 32-stage scale blocks; skewed rows exercise all three tile heights
     "int4-T200-d1024-dff3072-E8-skewed": (case(200, 1024, 3072, 8, w=INT4, bias=True),
