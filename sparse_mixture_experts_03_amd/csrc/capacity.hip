@@ -24,9 +24,15 @@
 // token's experts as 64-bit keys that order like z (the token's kept experts
 // get the lowest key).  Wavefront 0 holds every expert's count in registers
 // (lane l owns experts l, l + 64, ...), so one step is: mask full experts and
-// those the token took earlier in the walk, a DPP max-reduction of the keys,
-// a DPP min-reduction of the expert index among the lanes holding the
-// maximum (ties go to the lower index), and a register increment.
+// those the token took earlier in the walk, take each lane's best key, one
+// DPP max-reduction of the keys' high halves and a ballot of the lanes that
+// hold it.  When exactly one lane does, its key is the unique maximum and the
+// lane and its slot give the expert; otherwise (equal high halves, or only
+// NaN or no candidates) the low halves are reduced among the tied lanes and
+// then the expert index among the lanes holding the full maximum (ties go to
+// the lower index).  The owning lane increments the expert's count.  The next
+// step's keys and token are read from LDS under the current step's
+// reductions.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -55,6 +61,8 @@ __device__ __forceinline__ uint64_t rank_key(double z) {
     return (b >> 63) ? ~b : (b | (1ull << 63));
 }
 
+// JN = ceil(E / 64): experts per lane of wavefront 0.
+template <int JN>
 __global__ void __launch_bounds__(kThreads)
 capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int32_t* __restrict__ pos,
                 const int32_t* __restrict__ offsets, const int32_t* __restrict__ counts,
@@ -72,9 +80,9 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
     const int w = tid >> 6;
     if (tid < E) offs[tid] = offsets[tid];
     // wavefront 0: the count of expert lane + 64 j after pass 1, then after each reroute
-    int held[4];
+    int held[JN];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < JN; ++j) {
         const int e = lane + 64 * j;
         held[j] = (w == 0 && e < E) ? min(counts[e], cap) : cap;  // absent experts count as full
     }
@@ -148,11 +156,12 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
                 const int nr = min(rows, total - q0);
                 if (w == 0) {
                     const uint64_t* buf = ring[b & 1];
-                    uint64_t key[4];
+                    uint64_t key[JN];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) key[j] = lane + 64 * j < E ? buf[lane + 64 * j] : 0ull;
+                    for (int j = 0; j < JN; ++j) key[j] = lane + 64 * j < E ? buf[lane + 64 * j] : 0ull;
+                    int tnext = ltok[q0];
                     for (int r = 0; r < nr; ++r) {
-                        const int t = ltok[q0 + r];
+                        const int t = tnext;
                         if (t != tok) {
                             tok = t;
                             took = 0;
@@ -160,7 +169,7 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
                         uint64_t bk = 0;
                         int bj = 0;
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
+                        for (int j = 0; j < JN; ++j) {
                             uint64_t kj = key[j];
                             if (held[j] >= cap || ((took >> j) & 1)) kj = 0;
                             if (kj > bk) {  // strict: the lower index keeps a tie
@@ -168,27 +177,34 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
                                 bj = j;
                             }
                         }
-                        if (r + 1 < nr) {  // the next step's keys load under this step's reductions
+                        const int rn = min(r + 1, nr - 1);
 #pragma unroll
-                            for (int j = 0; j < 4; ++j)
-                                key[j] = lane + 64 * j < E ? buf[(r + 1) * E + lane + 64 * j] : 0ull;
-                        }
-                        // max over the wavefront: high halves, then low halves among the lanes that tie
+                        for (int j = 0; j < JN; ++j) key[j] = lane + 64 * j < E ? buf[rn * E + lane + 64 * j] : 0ull;
+                        tnext = ltok[q0 + rn];
                         const uint32_t hi = (uint32_t)(bk >> 32);
                         const uint32_t mhi = __ockl_wfred_max_u32(hi);
-                        const uint32_t mlo = __ockl_wfred_max_u32(hi == mhi ? (uint32_t)bk : 0u);
-                        if (mhi != 0 || mlo != 0) {
-                            const bool top = hi == mhi && (uint32_t)bk == mlo;
-                            const uint32_t be = __ockl_wfred_min_u32(top ? (uint32_t)(lane + 64 * bj) : 0xffffffffu);
-                            if (lane == (int)(be & 63)) {
-#pragma unroll
-                                for (int j = 0; j < 4; ++j)
-                                    if (j == (int)(be >> 6)) {
-                                        held[j] += 1;
-                                        took |= 1 << j;
-                                    }
+                        const uint64_t at_max = __ballot(hi == mhi);
+                        int be = -1;
+                        if (mhi != 0 && __popcll(at_max) == 1) {
+                            const int wl = __ffsll((unsigned long long)at_max) - 1;
+                            be = wl + 64 * __builtin_amdgcn_readlane(bj, wl);
+                        } else {
+                            // low halves among the lanes at the maximum high half, then the lowest index
+                            const uint32_t mlo = __ockl_wfred_max_u32(hi == mhi ? (uint32_t)bk : 0u);
+                            if (mhi != 0 || mlo != 0) {
+                                const bool top = hi == mhi && (uint32_t)bk == mlo;
+                                be = (int)__ockl_wfred_min_u32(top ? (uint32_t)(lane + 64 * bj) : 0xffffffffu);
                             }
-                            if (lane == 0) res[q0 + r] = (int)be;
+                        }
+                        if (be >= 0) {
+                            const bool own = lane == (be & 63);
+#pragma unroll
+                            for (int j = 0; j < JN; ++j)
+                                if (j == (be >> 6)) {
+                                    held[j] += own ? 1 : 0;
+                                    took |= own ? 1 << j : 0;
+                                }
+                            if (lane == 0) res[q0 + r] = be;
                         }
                     }
                 } else if (b + 1 < nb) {
@@ -216,8 +232,15 @@ hipError_t launch_capacity(int32_t* ids, float* gates, const int32_t* pos, const
                            int k, int cap, int policy, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     if (E < 1 || E > kMaxE || k < 1 || k > kMaxK || cap < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(capacity_kernel, dim3(1), dim3(kThreads), 0, stream, ids, gates, pos, offsets, counts, z_rows,
-                       prob_rows, T * k, E, k, cap, policy == 1 ? 1 : 0);
+#define MOE_CAPACITY_LAUNCH(JN_)                                                                               \
+    hipLaunchKernelGGL((capacity_kernel<JN_>), dim3(1), dim3(kThreads), 0, stream, ids, gates, pos, offsets, counts, \
+                       z_rows, prob_rows, T * k, E, k, cap, policy == 1 ? 1 : 0)
+    const int jn = (E + 63) / 64;
+    if (jn == 1) MOE_CAPACITY_LAUNCH(1);
+    else if (jn == 2) MOE_CAPACITY_LAUNCH(2);
+    else if (jn == 3) MOE_CAPACITY_LAUNCH(3);
+    else MOE_CAPACITY_LAUNCH(4);
+#undef MOE_CAPACITY_LAUNCH
     return hipGetLastError();
 }
 
