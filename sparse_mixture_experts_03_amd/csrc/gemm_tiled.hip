@@ -38,7 +38,9 @@ constexpr int kTBM = 256;   // dispatch rows per tile
 constexpr int kTBK = 32;    // K per stage (64 bytes of every tile row)
 constexpr int kStages = 4;  // LDS ring: stage k+3 streams in while stage k is multiplied
 constexpr int kTileBytes = 256 * kTBK * 2;  // 16 KB per operand per stage
-// INT4 kernel: 4 + 4 stages of 16 KB, the code ring (4 x 4 KB) and the scale ring (2 x 4 KB).
+// INT4 kernel: 4 + 4 stages of 16 KB, the code ring (4 x 4 KB) and the scale ring (2 x 4 KB).  Both
+// kernels stage their epilogues through the same LDS, over the rings: safe only once the last stage has
+// waited for every copy (vmcnt 0), which both do before their epilogues.
 constexpr int kInt4LdsBytes = 2 * kStages * kTileBytes + kStages * 4096 + 2 * 4096;
 // bf16 kernel: 2 weight + 3 dispatch-row stages of 32 KB, all of a CU's LDS.
 constexpr int kBf16LdsBytes = 5 * 32768;
