@@ -20,7 +20,10 @@ the next; tokens/s from the median step.  Then K more steps replay the layer
 through the stage entry points (router, permute, W1, W2, combine) with events
 between the stages: each stage's average duration, and the roofline of both
 expert GEMMs (algorithmic bytes or flops per launch / duration), the longer
-one being the dominant kernel.  The CPU oracle is timed beside it on a
+one being the dominant kernel.  For a bf16 workload bound by the matrix
+cores, `library_dense_gemm` adds context: the vendor library's dense bf16
+product (torch.matmul, i.e. hipBLASLt) with the W1 GEMM's flops, timed the
+same way outside the layer steps.  The CPU oracle is timed beside it on a
 bounded sample of the same workload, on one host core and on all of them.
 
 --import-counters turns two rocprofv3 --pmc runs of this benchmark with
@@ -287,11 +290,44 @@ def measure(name, args, dev, torch, np, moe, moe_synth, with_cpu):
         "roofline": roofs[0] if roofs else None,
         "roofline_other": roofs[1] if len(roofs) > 1 else None,
     }
+    del layer, H, Y
+    torch.cuda.empty_cache()
+    if roofs and roofs[0]["bound"] == "mfma" and cfg["w"] == moe.BF16:
+        out["library_dense_gemm"] = library_dense_gemm(torch, Tk, n1, d, flush)
     if with_cpu:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args, np, moe_synth)
-    del inp, layer, flush, H, Y
+    del inp, flush
     torch.cuda.empty_cache()
     return out
+
+
+def library_dense_gemm(torch, M, N, K, flush, reps=10):
+    """Context for the MFMA fraction, outside every timed step: the vendor
+    library's dense bf16 product with the W1 GEMM's flops (M dispatched rows,
+    N weight rows, K inputs; torch.matmul, i.e. hipBLASLt), no gather and no
+    per-expert tiles.  Median of `reps` launches, each after the same MALL
+    flush as the layer steps."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(1)
+    a = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+    b = torch.randn((K, N), generator=g, device=dev).to(torch.bfloat16)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    torch.matmul(a, b, out=c)
+    ms = []
+    for _ in range(reps):
+        if flush is not None:
+            flush.add_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.matmul(a, b, out=c)
+        e1.record()
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    med = statistics.median(ms)
+    tflops = 2.0 * M * N * K / (med * 1e-3) / 1e12
+    del a, b, c
+    return {"op": "torch.matmul bf16 (hipBLASLt), dense", "shape_mnk": [M, N, K], "ms": round(med, 4),
+            "tflops": round(tflops, 1), "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
 
 
 def main():
