@@ -60,6 +60,10 @@ typedef __attribute__((address_space(3))) void lvoid;
 __device__ __forceinline__ void copy_rows_to_lds(const char* base, uint32_t off, uint8_t* lds_block) {
     __builtin_amdgcn_global_load_lds((gvoid*)(base + off), (lvoid*)lds_block, 16, 0, 0);
 }
+// The same with the non-temporal hint (data read once).
+__device__ __forceinline__ void copy_rows_to_lds_nt(const char* base, uint32_t off, uint8_t* lds_block) {
+    __builtin_amdgcn_global_load_lds((gvoid*)(base + off), (lvoid*)lds_block, 16, 0, 2);
+}
 
 // LDS byte offset of logical segment `seg` (0..3) of tile row `row`.
 // Physical slot = seg ^ ((row >> 2) & 3): any 8 consecutive rows read at one
@@ -642,6 +646,10 @@ __device__ __forceinline__ void tile_gemm_bf16(uint8_t* lds, const uint16_t* __r
     static_assert(WN_WAVES * (XROWS / (32 * TJ)) == MWAVE, "wave grid");
     const bool math = (threadIdx.x >> 6) < MWAVE;
     constexpr uint32_t kStage = 256 * 128;
+    // A tile of at most 128 dispatch rows is an expert's only m-tile or its last, so no later tile re-reads its
+    // weights: they are copied with the non-temporal hint (each instruction moves whole 128-byte lines).  On
+    // the balanced 128-expert prefill, where nearly every tile streams its weights, W1 3.18 -> 2.89 ms.
+    constexpr bool kWeightsOnce = XROWS <= 128;
     uint8_t* const Wr = lds;
     uint8_t* const Xr = lds + 2 * kStage;
     const int tid = threadIdx.x;
@@ -667,7 +675,12 @@ __device__ __forceinline__ void tile_gemm_bf16(uint8_t* lds, const uint16_t* __r
         const uint32_t kb = (uint32_t)(kt0 + kt) * 128;
         uint8_t* slot = Wr + (kt & 1) * kStage;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) copy_rows_to_lds(wbase, woff[i] + kb, slot + (32 * wave + 8 * i) * 128);
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (kWeightsOnce)
+                copy_rows_to_lds_nt(wbase, woff[i] + kb, slot + (32 * wave + 8 * i) * 128);
+            else
+                copy_rows_to_lds(wbase, woff[i] + kb, slot + (32 * wave + 8 * i) * 128);
+        }
     };
     auto issue_x = [&](int kt) {
         const uint32_t kb = (uint32_t)(kt0 + kt) * 128;
