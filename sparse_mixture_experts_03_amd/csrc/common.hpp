@@ -115,9 +115,9 @@ __device__ __forceinline__ float act_f(float v, int act) { return act == kActSil
 // whole wavefront (every lane gets the same total); E <= 256, 4 experts per
 // lane.
 struct MtileScan {
-    int tiles[4], begin[4];  // this lane's experts 4 lane .. 4 lane + 3
-    int excl, incl;          // m-tiles of the experts before / up to this lane's
-    int total;               // all m-tiles
+    int tiles[4], begin[4], end[4];  // this lane's experts 4 lane .. 4 lane + 3: tiles, rows [begin, end)
+    int excl, incl;                  // m-tiles of the experts before / up to this lane's
+    int total;                       // all m-tiles
 };
 
 // Only experts whose row count n satisfies rows_lo < n <= rows_hi get tiles.
@@ -129,13 +129,15 @@ __device__ __forceinline__ MtileScan scan_mtiles(const int32_t* __restrict__ off
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = lane * 4 + j;
-        int n = 0, b = 0;
+        int n = 0, b = 0, end = 0;
         if (e < E) {
             b = offsets[e];
-            n = offsets[e + 1] - b;
+            end = offsets[e + 1];
+            n = end - b;
             if (n <= rows_lo || n > rows_hi) n = 0;
         }
         s.begin[j] = b;
+        s.end[j] = end;
         s.tiles[j] = (n + BM - 1) / BM;
         local += s.tiles[j];
     }
@@ -153,9 +155,11 @@ __device__ __forceinline__ MtileScan scan_mtiles(const int32_t* __restrict__ off
 }
 
 // (expert, first dispatch position, rows) of m-tile mt < s.total; called by
-// the whole wavefront that built s.
+// the whole wavefront that built s (no memory access: the scan kept each
+// expert's row range).
 __device__ __forceinline__ void lookup_mtile(const MtileScan& s, const int32_t* __restrict__ offsets, int BM, int mt,
                                              int* expert, int* pos0, int* rows) {
+    (void)offsets;
     const int lane = threadIdx.x & 63;
     const unsigned long long hit = __ballot(mt >= s.excl && mt < s.incl);  // the lane whose range holds mt
     const int src = __ffsll((long long)hit) - 1;
@@ -167,7 +171,7 @@ __device__ __forceinline__ void lookup_mtile(const MtileScan& s, const int32_t* 
             if (e_found < 0 && mt < acc + s.tiles[j]) {
                 e_found = lane * 4 + j;
                 p0 = s.begin[j] + (mt - acc) * BM;
-                r = min(BM, offsets[e_found + 1] - p0);
+                r = min(BM, s.end[j] - p0);
             }
             acc += s.tiles[j];
         }
