@@ -483,7 +483,9 @@ def import_counters(args):
     fetch_csv, write_csv = args.import_counters
     fr = _counter_rows(fetch_csv, "FETCH_SIZE")
     wr = _counter_rows(write_csv, "WRITE_SIZE")
-    copies = lambda rows: [float(r["Counter_Value"]) for r in rows if "copy" in r["Kernel_Name"].lower()]
+    # the runtime's device-to-device copy kernel (torch's elementwise copy kernels of the input generation are
+    # not the calibration copy)
+    copies = lambda rows: [float(r["Counter_Value"]) for r in rows if "copybuffer" in r["Kernel_Name"].lower()]
     cf, cw = copies(fr), copies(wr)
     if not cf or not cw:
         raise SystemExit("no copy kernel in the counter files: run the bench with --calibrate-copy")
