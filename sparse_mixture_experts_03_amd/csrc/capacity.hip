@@ -19,20 +19,25 @@
 // fill (each choice depends on every earlier one through the expert counts),
 // so it runs on one workgroup: the assignments stream through in chunks of
 // whole tokens and the chunk's overflowing assignments are listed in order
-// with a block scan.  Wavefront 0 then walks the list while the other
-// fifteen stage, one batch ahead in a double-buffered LDS ring, each listed
-// token's experts as 64-bit keys that order like z (the token's kept experts
-// get the lowest key).  Wavefront 0 holds every expert's count in registers
-// (lane l owns experts l, l + 64, ...), so one step is: mask full experts and
-// those the token took earlier in the walk, take each lane's best key, one
-// DPP max-reduction of the keys' high halves and a ballot of the lanes that
-// hold it.  When exactly one lane does, its key is the unique maximum and the
-// lane and its slot give the expert; otherwise (equal high halves, or only
-// NaN or no candidates) the low halves are reduced among the tied lanes and
-// then the expert index among the lanes holding the full maximum (ties go to
-// the lower index).  The owning lane increments the expert's count.  The next
-// step's keys and token are read from LDS under the current step's
-// reductions.
+// with a block scan.  The list is cut into batches; wavefront 0 walks a batch
+// while the other fifteen stage the next one into a double-buffered LDS ring:
+// each listed row's experts as 64-bit keys that order like z (the token's kept
+// experts get key 0), and the row's kCand best keys among the experts that are
+// not at capacity in a snapshot wavefront 0 published two batches earlier
+// (experts only fill up, so a stale snapshot merely leaves in experts that the
+// walk then finds full).
+//
+// The walk takes up to 64 rows at a time, one per lane.  A lane proposes the
+// first of its ranked candidates that is below capacity and not taken by its
+// token, skipping as many further live candidates as its token has earlier
+// rows in the group (those rows take them).  A bit-sliced ballot match counts
+// the lower lanes proposing the same expert, and the rows before the first
+// proposal that would push its expert past capacity are committed at once:
+// each of them is exactly the sequential greedy choice at its row.  The walk
+// resumes at the conflicting row, or, when a row has used up all kCand ranked
+// candidates, takes that row alone with an exact wavefront reduction over its
+// keys (masked by the current counts and the token's picks; ties go to the
+// lower expert index).  Expert counts live in LDS.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -49,16 +54,35 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kPerThread = 4;
 constexpr int kChunk = kThreads * kPerThread;  // assignments per chunk (rounded down to whole tokens)
 constexpr int kMaxE = 256;
-constexpr int kRingKeys = 4096;                // keys per ring buffer (32 KB)
 constexpr int kMaxK = 8;
+constexpr int kCand = 4;                       // ranked candidates staged per listed assignment (16 bits each)
+constexpr int kStagers = kWaves - 1;           // wavefronts that stage while wavefront 0 walks
 
 // A 64-bit key that orders like the router's ranking: larger z larger key,
 // any NaN below every number, and 0 reserved for "not a candidate".  -0 is
 // folded into +0 (they compare equal, so the lower index must decide).
 __device__ __forceinline__ uint64_t rank_key(double z) {
-    if (isnan(z)) return 1;
-    const uint64_t b = (uint64_t)__double_as_longlong(z + 0.0);
-    return (b >> 63) ? ~b : (b | (1ull << 63));
+    const int64_t b = __double_as_longlong(z + 0.0);
+    const uint64_t key = (uint64_t)b ^ ((uint64_t)(b >> 63) | (1ull << 63));  // negative: all bits flipped
+    return isnan(z) ? 1ull : key;
+}
+
+// The maxima of a and of b over the wavefront, left in lane 63: a prefix max
+// within each row of 16 lanes (row_shr 1, 2, 4, 8), then row 0's and row 2's
+// maxima into rows 1 and 3 (row_bcast 15) and row 1's into rows 2 and 3
+// (row_bcast 31).  The two chains are interleaved so that each one's DPP
+// operand waits are the other's issue slots.
+__device__ __forceinline__ void wave_max_lane63_x2(uint32_t& a, uint32_t& b) {
+#define MOE_DPP_MAX_STEP(CTRL, ROWS)                                                                    \
+    a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, CTRL, ROWS, 0xf, false));               \
+    b = max(b, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b, CTRL, ROWS, 0xf, false));
+    MOE_DPP_MAX_STEP(0x111, 0xf)
+    MOE_DPP_MAX_STEP(0x112, 0xf)
+    MOE_DPP_MAX_STEP(0x114, 0xf)
+    MOE_DPP_MAX_STEP(0x118, 0xf)
+    MOE_DPP_MAX_STEP(0x142, 0xa)
+    MOE_DPP_MAX_STEP(0x143, 0xc)
+#undef MOE_DPP_MAX_STEP
 }
 
 // JN = ceil(E / 64): experts per lane of wavefront 0.
@@ -74,21 +98,22 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
     __shared__ int res[kChunk];       // their final experts (-1: dropped)
     __shared__ int ltok[kChunk];      // their tokens (chunk-local)
     __shared__ int wsum[kWaves];
-    __shared__ uint64_t ring[2][kRingKeys];
+    __shared__ uint64_t cand[2][64];        // per listed assignment of a batch: its kCand best candidates, 0xffff past the last
+    __shared__ uint64_t snap[2][4];         // experts at capacity (bit e % 64 of word e / 64), published per batch
+    __shared__ int hcnt[kMaxE];             // each expert's count after pass 1, then after each reroute
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
-    if (tid < E) offs[tid] = offsets[tid];
-    // wavefront 0: the count of expert lane + 64 j after pass 1, then after each reroute
-    int held[JN];
-#pragma unroll
-    for (int j = 0; j < JN; ++j) {
-        const int e = lane + 64 * j;
-        held[j] = (w == 0 && e < E) ? min(counts[e], cap) : cap;  // absent experts count as full
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform, so wavefront 0's walk is scalar code
+    if (tid < E) {
+        offs[tid] = offsets[tid];
+        hcnt[tid] = min(counts[tid], cap);
     }
     __syncthreads();
     const int chunk = (kChunk / k) * k;
-    const int rows = min(256, kRingKeys / E);  // listed assignments per ring buffer
+    // listed assignments per batch: kG per staging wavefront, whose z is requested a batch ahead
+    constexpr int kG = JN <= 2 ? 4 : 2;
+    constexpr int rows = kStagers * kG;
+    static_assert(rows <= 64, "a batch is walked by one wavefront");
 
     for (int64_t base = 0; base < Tk; base += chunk) {
         const int n_here = (int)min((int64_t)chunk, Tk - base);
@@ -135,80 +160,304 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
         // pass 2 (reroute)
         if (reroute && total > 0) {
             const int nb = (total + rows - 1) / rows;
-            // keys of listed assignments [q0, q0 + nr) into ring[buf], by threads t0, t0 + stride, ...
-            auto stage = [&](int q0, int nr, uint64_t* buf, int t0, int stride) {
-                for (int idx = t0; idx < nr * E; idx += stride) {
-                    const int r = idx / E;
-                    const int e = idx - r * E;
-                    const int i = list[q0 + r];
-                    const int first = i - i % k;  // the token's slot 0 (chunks hold whole tokens)
-                    bool kept = false;
-                    for (int jj = 0; jj < k; ++jj) kept |= cur[first + jj] == e;
-                    buf[idx] = kept ? 0ull : rank_key(z_rows[((base + i) / k) * E + e]);
+            const int64_t tok0 = base / k;  // the chunk's first token (chunks hold whole tokens)
+            // wavefront 0: the experts at capacity as bit words (bit l of word j is expert 64 j + l)
+            auto publish = [&](int sn) {
+#pragma unroll
+                for (int j = 0; j < JN; ++j) {
+                    const int e = lane + 64 * j;
+                    const uint64_t f = __ballot(e >= E || hcnt[e] >= cap);
+                    if (lane == 0) snap[sn][j] = f;
                 }
             };
-            stage(0, min(rows, total), ring[0], tid, kThreads);
-            __syncthreads();
-            int tok = -1;  // wavefront 0: the token being rerouted, and the experts it took so far
-            int took = 0;
-            for (int b = 0; b < nb; ++b) {
+            // best key of a wavefront's JN keys per lane (expert lane + 64 j): one DPP max over the high halves and a
+            // ballot; equal high halves (or only NaN keys) fall back to the low halves and then the lowest index.
+            // -1 when every key is 0.  The result is wavefront-uniform.
+            auto wave_argmax = [&](const uint64_t (&kv)[JN]) -> int {
+                uint64_t bk = 0;
+                int bj = 0;
+#pragma unroll
+                for (int j = 0; j < JN; ++j)
+                    if (kv[j] > bk) {  // strict: the lower index keeps a tie
+                        bk = kv[j];
+                        bj = j;
+                    }
+                const uint32_t hi = (uint32_t)(bk >> 32);
+                const uint32_t mhi = __ockl_wfred_max_u32(hi);
+                const uint64_t at_max = __ballot(hi == mhi);
+                if (mhi != 0 && __popcll(at_max) == 1) {
+                    const int wl = __ffsll((unsigned long long)at_max) - 1;
+                    return wl + 64 * __builtin_amdgcn_readlane(bj, wl);
+                }
+                const uint32_t mlo = __ockl_wfred_max_u32(hi == mhi ? (uint32_t)bk : 0u);
+                if (mhi == 0 && mlo == 0) return -1;
+                const bool top = hi == mhi && (uint32_t)bk == mlo;
+                return __builtin_amdgcn_readfirstlane(
+                    (int)__ockl_wfred_min_u32(top ? (uint32_t)(lane + 64 * bj) : 0xffffffffu));
+            };
+            // a listed row's keys: z order, 0 for the token's kept experts and where out[j] is set
+            auto row_keys = [&](int q, const double (&zv)[JN], uint64_t (&kv)[JN], const bool (&out)[JN]) {
+                const int first = ltok[q] * k;  // the token's slot 0
+                bool kept[JN];
+#pragma unroll
+                for (int j = 0; j < JN; ++j) kept[j] = out[j];
+                for (int jj = 0; jj < k; ++jj) {
+                    const int ce = cur[first + jj];
+#pragma unroll
+                    for (int j = 0; j < JN; ++j) kept[j] |= ce == lane + 64 * j;
+                }
+#pragma unroll
+                for (int j = 0; j < JN; ++j) kv[j] = kept[j] ? 0ull : rank_key(zv[j]);
+            };
+            auto zload = [&](int q, double (&dst)[JN]) {
+                const double* zr = z_rows + (tok0 + ltok[min(q, total - 1)]) * E;
+#pragma unroll
+                for (int j = 0; j < JN; ++j) dst[j] = lane + 64 * j < E ? zr[lane + 64 * j] : 0.0;
+            };
+
+            // ---- staging (wavefronts 1 .. kStagers): row sw + kStagers g of each batch (g < kG) belongs to
+            // staging wavefront sw.  A row's candidates are its kCand best keys among the experts that are not at
+            // capacity in the snapshot published two batches earlier (experts only fill up, so the snapshot leaves
+            // out only experts that are still full when the row is walked).  Two rows are ranked side by side: each
+            // lane sorts its JN keys (stable odd-even transposition, so equal keys keep the lower expert first),
+            // and every round reduces the lanes' leading keys (one DPP max of the high halves and a ballot; the low
+            // halves and the expert index only on a tie or NaN) and shifts the winning lane's list up by one.
+            const int sw = w - 1;
+            auto prefetch = [&](int b, double (&dst)[kG][JN]) {
+#pragma unroll
+                for (int g = 0; g < kG; ++g) zload(b * rows + sw + kStagers * g, dst[g]);
+            };
+            auto rank_pair = [&](int q0, int nr, int slot, int g, const double (&zc)[kG][JN], const bool (&fx)[JN]) {
+                uint64_t kv[2][JN];
+                int ix[2][JN];
+                bool fin[2];
+                int rr[2];
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    rr[p] = sw + kStagers * (g + p);
+                    fin[p] = rr[p] >= nr;
+                    row_keys(q0 + min(rr[p], nr - 1), zc[g + p], kv[p], fx);
+#pragma unroll
+                    for (int j = 0; j < JN; ++j) {
+                        ix[p][j] = lane + 64 * j;
+                        if (fin[p]) kv[p][j] = 0;
+                    }
+#pragma unroll
+                    for (int pass = 0; pass < JN; ++pass)
+#pragma unroll
+                        for (int j = pass & 1; j + 1 < JN; j += 2)
+                            if (kv[p][j + 1] > kv[p][j]) {
+                                const uint64_t tk = kv[p][j];
+                                kv[p][j] = kv[p][j + 1];
+                                kv[p][j + 1] = tk;
+                                const int ti = ix[p][j];
+                                ix[p][j] = ix[p][j + 1];
+                                ix[p][j + 1] = ti;
+                            }
+                }
+                uint64_t cw[2] = {~0ull, ~0ull};
+                for (int c = 0; c < kCand && !(fin[0] && fin[1]); ++c) {
+                    uint32_t hi[2], mx[2];
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) mx[p] = hi[p] = (uint32_t)(kv[p][0] >> 32);
+                    wave_max_lane63_x2(mx[0], mx[1]);
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) {
+                        const uint32_t mhi = __builtin_amdgcn_readlane(mx[p], 63);
+                        const uint64_t am = __ballot(hi[p] == mhi);
+                        int be;
+                        if (mhi != 0 && __popcll(am) == 1) {
+                            be = __builtin_amdgcn_readlane(ix[p][0], __builtin_ctzll(am));
+                        } else {  // equal high halves, only NaN keys, or none left
+                            const uint64_t hk = kv[p][0];
+                            const uint32_t mlo = __ockl_wfred_max_u32(hi[p] == mhi ? (uint32_t)hk : 0u);
+                            const bool top = hi[p] == mhi && (uint32_t)hk == mlo;
+                            be = (mhi == 0 && mlo == 0)
+                                     ? -1
+                                     : __builtin_amdgcn_readfirstlane(
+                                           (int)__ockl_wfred_min_u32(top ? (uint32_t)ix[p][0] : 0xffffffffu));
+                        }
+                        if (fin[p] || be < 0) {
+                            fin[p] = true;
+                            continue;
+                        }
+                        cw[p] ^= (uint64_t)(be ^ 0xffff) << (16 * c);
+                        const bool win = ix[p][0] == be;
+#pragma unroll
+                        for (int j = 0; j + 1 < JN; ++j) {
+                            kv[p][j] = win ? kv[p][j + 1] : kv[p][j];
+                            ix[p][j] = win ? ix[p][j + 1] : ix[p][j];
+                        }
+                        kv[p][JN - 1] = win ? 0ull : kv[p][JN - 1];
+                    }
+                }
+                if (lane == 0) {
+#pragma unroll
+                    for (int p = 0; p < 2; ++p)
+                        if (rr[p] < nr) cand[slot][rr[p]] = cw[p];
+                }
+            };
+            // batch b's rows are ranked from z requested during the previous batch; batch b + 1's z is requested
+            // afterwards (the compiler waits for every outstanding load before the first use of batch b's z, so
+            // requests made before the ranking would be waited for there)
+            auto stage = [&](int b, const double (&zc)[kG][JN], double (&zn)[kG][JN]) {
                 const int q0 = b * rows;
                 const int nr = min(rows, total - q0);
-                if (w == 0) {
-                    const uint64_t* buf = ring[b & 1];
-                    uint64_t key[JN];
+                const int slot = b & 1;
+                bool fx[JN];  // expert lane + 64 j is past E or at capacity in the snapshot
 #pragma unroll
-                    for (int j = 0; j < JN; ++j) key[j] = lane + 64 * j < E ? buf[lane + 64 * j] : 0ull;
-                    int tnext = ltok[q0];
-                    for (int r = 0; r < nr; ++r) {
-                        const int t = tnext;
-                        if (t != tok) {
-                            tok = t;
-                            took = 0;
+                for (int j = 0; j < JN; ++j) fx[j] = lane + 64 * j >= E || ((snap[slot][j] >> lane) & 1);
+#pragma unroll
+                for (int g = 0; g < kG; g += 2) rank_pair(q0, nr, slot, g, zc, fx);
+                if (b + 1 < nb) prefetch(b + 1, zn);
+            };
+
+            // ---- walk (wavefront 0): a batch in one pass, lane l taking row g0 + l.  A lane proposes the m-th of
+            // its ranked candidates that is below capacity now and not taken by its token before row g0, m being
+            // the number of rows of its token among rows g0 .. g0 + l - 1 (those rows take the candidates ranked
+            // before it).  A bit-sliced ballot match counts the lower lanes proposing the same expert; the rows
+            // before the first proposal that would exceed capacity (or that needs the exact pick: all kCand
+            // candidates gone) are committed, and the walk resumes at that row.  Experts only fill up, so each
+            // committed proposal is the best expert left at its row in the sequential order.
+            constexpr int kBits = JN == 1 ? 6 : JN == 2 ? 7 : 8;
+            auto walk = [&](int b) {
+                const int q0 = b * rows;
+                const int nr = min(rows, total - q0);
+                const int slot = b & 1;
+                const uint64_t lt = (1ull << lane) - 1;
+                int g0 = 0;
+                for (int pass = 0; g0 < nr && pass < nr; ++pass) {  // every pass commits at least row g0
+                    const int r = g0 + lane;
+                    const bool in = r < nr;
+                    const int qr = q0 + r;
+                    // one round of LDS reads: the row's candidates and token, the token of the row before it, and
+                    // (lane d - 1) the token and pick of row g0 - d for d < k
+                    const uint64_t cw = in ? cand[slot][r] : ~0ull;
+                    const int tk = in ? ltok[qr] : -1;
+                    const int tpv = in && qr >= 1 ? ltok[qr - 1] : -2;
+                    const int qd = q0 + g0 - 1 - lane;
+                    const bool dl = lane < k - 1 && qd >= 0;
+                    const int td = dl ? ltok[qd] : -3;
+                    const int pd = dl ? res[qd] : -1;
+                    // the experts row g0's token took before row g0
+                    const int t0 = __builtin_amdgcn_readfirstlane(tk);
+                    uint64_t pm[JN];
+#pragma unroll
+                    for (int j = 0; j < JN; ++j) pm[j] = 0;
+                    for (uint64_t mb = __ballot(dl && td == t0 && pd >= 0); mb; mb &= mb - 1) {
+                        const int pe = __builtin_amdgcn_readlane(pd, __builtin_ctzll(mb));
+#pragma unroll
+                        for (int j = 0; j < JN; ++j)
+                            if ((pe >> 6) == j) pm[j] |= 1ull << (pe & 63);
+                    }
+                    // rank among the pass's rows of the same token; lanes of the first run continue row g0 - 1's token
+                    const uint64_t starts = __ballot(tk != tpv);
+                    const uint64_t le = starts & (lt | (1ull << lane));
+                    const int run0 = le ? 63 - __clzll((long long)le) : 0;
+                    const bool cont = (starts & 1) == 0 && le == 0;
+                    const int m = lane - run0;
+                    // the proposal: m-th live candidate; -1 drop (the ranking ran out), -3 exact pick needed
+                    int hc[kCand];
+#pragma unroll
+                    for (int c = 0; c < kCand; ++c) hc[c] = hcnt[min((int)((cw >> (16 * c)) & 0xffff), E - 1)];
+                    int pe = -3, ph = 0, v = 0;
+                    bool done = !in;
+#pragma unroll
+                    for (int c = 0; c < kCand; ++c) {
+                        const int ce = (int)((cw >> (16 * c)) & 0xffff);
+                        if (!done && ce == 0xffff) {
+                            pe = -1;
+                            done = true;
                         }
-                        uint64_t bk = 0;
-                        int bj = 0;
+                        if (!done) {
+                            uint64_t pw = pm[0];
 #pragma unroll
-                        for (int j = 0; j < JN; ++j) {
-                            uint64_t kj = key[j];
-                            if (held[j] >= cap || ((took >> j) & 1)) kj = 0;
-                            if (kj > bk) {  // strict: the lower index keeps a tie
-                                bk = kj;
-                                bj = j;
+                            for (int j = 1; j < JN; ++j)
+                                if ((ce >> 6) == j) pw = pm[j];
+                            const bool live = hc[c] < cap && !(cont && ((pw >> (ce & 63)) & 1));
+                            if (live && v == m) {
+                                pe = ce;
+                                ph = hc[c];
+                                done = true;
                             }
-                        }
-                        const int rn = min(r + 1, nr - 1);
-#pragma unroll
-                        for (int j = 0; j < JN; ++j) key[j] = lane + 64 * j < E ? buf[rn * E + lane + 64 * j] : 0ull;
-                        tnext = ltok[q0 + rn];
-                        const uint32_t hi = (uint32_t)(bk >> 32);
-                        const uint32_t mhi = __ockl_wfred_max_u32(hi);
-                        const uint64_t at_max = __ballot(hi == mhi);
-                        int be = -1;
-                        if (mhi != 0 && __popcll(at_max) == 1) {
-                            const int wl = __ffsll((unsigned long long)at_max) - 1;
-                            be = wl + 64 * __builtin_amdgcn_readlane(bj, wl);
-                        } else {
-                            // low halves among the lanes at the maximum high half, then the lowest index
-                            const uint32_t mlo = __ockl_wfred_max_u32(hi == mhi ? (uint32_t)bk : 0u);
-                            if (mhi != 0 || mlo != 0) {
-                                const bool top = hi == mhi && (uint32_t)bk == mlo;
-                                be = (int)__ockl_wfred_min_u32(top ? (uint32_t)(lane + 64 * bj) : 0xffffffffu);
-                            }
-                        }
-                        if (be >= 0) {
-                            const bool own = lane == (be & 63);
-#pragma unroll
-                            for (int j = 0; j < JN; ++j)
-                                if (j == (be >> 6)) {
-                                    held[j] += own ? 1 : 0;
-                                    took |= own ? 1 << j : 0;
-                                }
-                            if (lane == 0) res[q0 + r] = be;
+                            v += live ? 1 : 0;
                         }
                     }
+                    // lower lanes proposing the same expert
+                    const bool has = in && pe >= 0;
+                    uint64_t eq = __ballot(has);
+#pragma unroll
+                    for (int bit = 0; bit < kBits; ++bit) {
+                        const bool set = (pe >> bit) & 1;
+                        const uint64_t bm = __ballot(has && set);
+                        eq &= set ? bm : ~bm;
+                    }
+                    const bool ok = !in || pe == -1 || (pe >= 0 && ph + __popcll(eq & lt) < cap);
+                    const uint64_t bad = __ballot(!ok);
+                    const int n_in = nr - g0;
+                    const int f = bad ? (int)__builtin_ctzll(bad) : n_in;
+                    const uint64_t cm = f >= 64 ? ~0ull : (1ull << f) - 1;
+                    if (lane < f) res[qr] = pe;
+                    if (has && lane < f && (eq & cm & ~(lt | (1ull << lane))) == 0) hcnt[pe] = ph + __popcll(eq & cm);
+                    if (f == n_in) break;
+                    if (__builtin_amdgcn_readlane(pe, f) != -3) {  // over capacity: propose again from row g0 + f
+                        g0 += f;
+                        continue;
+                    }
+                    // the exact pick for row g0 + f: its keys from z, without the experts at capacity and those its
+                    // token took at earlier rows
+                    const int q = q0 + g0 + f;
+                    const int tq = __builtin_amdgcn_readfirstlane(ltok[q]);
+                    uint64_t tm[JN];
+#pragma unroll
+                    for (int j = 0; j < JN; ++j) tm[j] = 0;
+                    for (int d = 1; d < k && q - d >= 0; ++d) {
+                        if (__builtin_amdgcn_readfirstlane(ltok[q - d]) != tq) break;
+                        const int te = __builtin_amdgcn_readfirstlane(res[q - d]);
+                        if (te >= 0) {
+#pragma unroll
+                            for (int j = 0; j < JN; ++j)
+                                if ((te >> 6) == j) tm[j] |= 1ull << (te & 63);
+                        }
+                    }
+                    double zv[JN];
+                    zload(q, zv);
+                    bool out[JN];
+#pragma unroll
+                    for (int j = 0; j < JN; ++j) {
+                        const int e = lane + 64 * j;
+                        out[j] = e >= E || hcnt[min(e, E - 1)] >= cap || ((tm[j] >> lane) & 1);
+                    }
+                    uint64_t kv[JN];
+                    row_keys(q, zv, kv, out);
+                    const int be = wave_argmax(kv);
+                    if (lane == 0) {
+                        res[q] = be;
+                        if (be >= 0) hcnt[be] += 1;
+                    }
+                    g0 += f + 1;
+                }
+            };
+
+            double za[kG][JN], zb[kG][JN];
+            if (w == 0) {
+                publish(0);
+                publish(1);
+            } else {
+                prefetch(0, za);
+            }
+            __syncthreads();
+            if (w != 0) stage(0, za, zb);
+            __syncthreads();
+            for (int b = 0; b < nb; ++b) {
+                if (w == 0) {
+                    walk(b);
+                    publish(b & 1);  // read when batch b + 2 is staged
                 } else if (b + 1 < nb) {
-                    stage(q0 + rows, min(rows, total - q0 - rows), ring[(b + 1) & 1], tid - 64, kThreads - 64);
+                    if ((b + 1) & 1)
+                        stage(b + 1, zb, za);
+                    else
+                        stage(b + 1, za, zb);
                 }
                 __syncthreads();
             }
@@ -219,7 +468,7 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
             const int64_t a = base + list[q];
             const int e = res[q];
             ids[a] = e;
-            gates[a] = e >= 0 ? (float)prob_rows[(a / k) * E + e] : 0.0f;
+            gates[a] = e >= 0 ? (float)prob_rows[(base / k + ltok[q]) * E + e] : 0.0f;
         }
         __syncthreads();  // cur, list, res and wsum are reused by the next chunk
     }

@@ -39,6 +39,11 @@ CASES = {
     "int4-T200-d384-dff768-E8-gumbel-cf0.9": (case(200, 384, 768, 8, w=INT4, tau=0.5, gumbel=True), 0.9),
     # decode: capacity ceil(8 * 2 / 128) = 1, streaming GEMMs
     "bf16-T8-d512-dff1024-E128-cf1": (case(8, 512, 1024, 128), 1.0),
+    # the routing of the skewed T2048 E128 prefill layer at capacity factor 2 (about 3,700 overflowing slots walked in
+    # batches of 32, each batch ranked while the one before it fills experts)
+    "bf16-T2048-d128-dff256-E128-skewed-cf2": (case(2048, 128, 256, 128, bias=True), 2.0),
+    # k = 8 of 256 skewed experts over two chunks, batches of 16
+    "bf16-T1024-d128-dff128-E256-k8-skewed-cf1": (case(1024, 128, 128, 256, k=8, bias=True), 1.0),
 }
 PARAMS = [(n, pol) for n in CASES for pol in (DROP, REROUTE)]
 
