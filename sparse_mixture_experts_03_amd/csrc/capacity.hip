@@ -67,15 +67,29 @@ __device__ __forceinline__ uint64_t rank_key(double z) {
     return isnan(z) ? 1ull : key;
 }
 
-// The maxima of a and of b over the wavefront, left in lane 63: a prefix max
+// The maxima of a and of b (of a, b, c and d) over the wavefront, left in lane 63: a prefix max
 // within each row of 16 lanes (row_shr 1, 2, 4, 8), then row 0's and row 2's
 // maxima into rows 1 and 3 (row_bcast 15) and row 1's into rows 2 and 3
-// (row_bcast 31).  The two chains are interleaved so that each one's DPP
-// operand waits are the other's issue slots.
+// (row_bcast 31).  The chains are interleaved so that each one's DPP
+// operand waits are the others' issue slots.
 __device__ __forceinline__ void wave_max_lane63_x2(uint32_t& a, uint32_t& b) {
 #define MOE_DPP_MAX_STEP(CTRL, ROWS)                                                                    \
     a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, CTRL, ROWS, 0xf, false));               \
     b = max(b, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b, CTRL, ROWS, 0xf, false));
+    MOE_DPP_MAX_STEP(0x111, 0xf)
+    MOE_DPP_MAX_STEP(0x112, 0xf)
+    MOE_DPP_MAX_STEP(0x114, 0xf)
+    MOE_DPP_MAX_STEP(0x118, 0xf)
+    MOE_DPP_MAX_STEP(0x142, 0xa)
+    MOE_DPP_MAX_STEP(0x143, 0xc)
+#undef MOE_DPP_MAX_STEP
+}
+__device__ __forceinline__ void wave_max_lane63_x4(uint32_t& a, uint32_t& b, uint32_t& c, uint32_t& d) {
+#define MOE_DPP_MAX_STEP(CTRL, ROWS)                                                                    \
+    a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, CTRL, ROWS, 0xf, false));               \
+    b = max(b, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b, CTRL, ROWS, 0xf, false));               \
+    c = max(c, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)c, CTRL, ROWS, 0xf, false));               \
+    d = max(d, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d, CTRL, ROWS, 0xf, false));
     MOE_DPP_MAX_STEP(0x111, 0xf)
     MOE_DPP_MAX_STEP(0x112, 0xf)
     MOE_DPP_MAX_STEP(0x114, 0xf)
@@ -218,7 +232,7 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
             // ---- staging (wavefronts 1 .. kStagers): row sw + kStagers g of each batch (g < kG) belongs to
             // staging wavefront sw.  A row's candidates are its kCand best keys among the experts that are not at
             // capacity in the snapshot published two batches earlier (experts only fill up, so the snapshot leaves
-            // out only experts that are still full when the row is walked).  Two rows are ranked side by side: each
+            // out only experts that are still full when the row is walked).  A wavefront's rows of a batch are ranked side by side: each
             // lane sorts its JN keys (stable odd-even transposition, so equal keys keep the lower expert first),
             // and every round reduces the lanes' leading keys (one DPP max of the high halves and a ballot; the low
             // halves and the expert index only on a tie or NaN) and shifts the winning lane's list up by one.
@@ -227,16 +241,17 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
 #pragma unroll
                 for (int g = 0; g < kG; ++g) zload(b * rows + sw + kStagers * g, dst[g]);
             };
-            auto rank_pair = [&](int q0, int nr, int slot, int g, const double (&zc)[kG][JN], const bool (&fx)[JN]) {
-                uint64_t kv[2][JN];
-                int ix[2][JN];
-                bool fin[2];
-                int rr[2];
+            auto rank_rows = [&](int q0, int nr, int slot, const double (&zc)[kG][JN], const bool (&fx)[JN]) {
+                constexpr int P = kG;  // this wavefront's rows of the batch, ranked side by side
+                uint64_t kv[P][JN];
+                int ix[P][JN];
+                bool fin[P];
+                int rr[P];
 #pragma unroll
-                for (int p = 0; p < 2; ++p) {
-                    rr[p] = sw + kStagers * (g + p);
+                for (int p = 0; p < P; ++p) {
+                    rr[p] = sw + kStagers * p;
                     fin[p] = rr[p] >= nr;
-                    row_keys(q0 + min(rr[p], nr - 1), zc[g + p], kv[p], fx);
+                    row_keys(q0 + min(rr[p], nr - 1), zc[p], kv[p], fx);
 #pragma unroll
                     for (int j = 0; j < JN; ++j) {
                         ix[p][j] = lane + 64 * j;
@@ -255,14 +270,21 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
                                 ix[p][j + 1] = ti;
                             }
                 }
-                uint64_t cw[2] = {~0ull, ~0ull};
-                for (int c = 0; c < kCand && !(fin[0] && fin[1]); ++c) {
-                    uint32_t hi[2], mx[2];
+                uint64_t cw[P];
 #pragma unroll
-                    for (int p = 0; p < 2; ++p) mx[p] = hi[p] = (uint32_t)(kv[p][0] >> 32);
-                    wave_max_lane63_x2(mx[0], mx[1]);
+                for (int p = 0; p < P; ++p) cw[p] = ~0ull;
 #pragma unroll
-                    for (int p = 0; p < 2; ++p) {
+                for (int c = 0; c < kCand; ++c) {
+                    uint32_t hi[P], mx[P];
+#pragma unroll
+                    for (int p = 0; p < P; ++p) mx[p] = hi[p] = (uint32_t)(kv[p][0] >> 32);
+                    if constexpr (P == 4)
+                        wave_max_lane63_x4(mx[0], mx[1], mx[2 % P], mx[3 % P]);
+                    else
+                        wave_max_lane63_x2(mx[0], mx[1 % P]);
+#pragma unroll
+                    for (int p = 0; p < P; ++p) {
+                        if (fin[p]) continue;
                         const uint32_t mhi = __builtin_amdgcn_readlane(mx[p], 63);
                         const uint64_t am = __ballot(hi[p] == mhi);
                         int be;
@@ -277,7 +299,7 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
                                      : __builtin_amdgcn_readfirstlane(
                                            (int)__ockl_wfred_min_u32(top ? (uint32_t)ix[p][0] : 0xffffffffu));
                         }
-                        if (fin[p] || be < 0) {
+                        if (be < 0) {
                             fin[p] = true;
                             continue;
                         }
@@ -293,7 +315,7 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
                 }
                 if (lane == 0) {
 #pragma unroll
-                    for (int p = 0; p < 2; ++p)
+                    for (int p = 0; p < P; ++p)
                         if (rr[p] < nr) cand[slot][rr[p]] = cw[p];
                 }
             };
@@ -307,8 +329,7 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
                 bool fx[JN];  // expert lane + 64 j is past E or at capacity in the snapshot
 #pragma unroll
                 for (int j = 0; j < JN; ++j) fx[j] = lane + 64 * j >= E || ((snap[slot][j] >> lane) & 1);
-#pragma unroll
-                for (int g = 0; g < kG; g += 2) rank_pair(q0, nr, slot, g, zc, fx);
+                rank_rows(q0, nr, slot, zc, fx);
                 if (b + 1 < nb) prefetch(b + 1, zn);
             };
 
