@@ -42,8 +42,12 @@ CASES = {
     # the routing of the skewed T2048 E128 prefill layer at capacity factor 2 (about 3,700 overflowing slots walked in
     # batches of 32, each batch ranked while the one before it fills experts)
     "bf16-T2048-d128-dff256-E128-skewed-cf2": (case(2048, 128, 256, 128, bias=True), 2.0),
-    # k = 8 of 256 skewed experts over two chunks, batches of 16
+    # k = 8 of 256 skewed experts over two chunks
     "bf16-T1024-d128-dff128-E256-k8-skewed-cf1": (case(1024, 128, 128, 256, k=8, bias=True), 1.0),
+    # 160 experts (three 64-expert words per lane of the walk, 30-row batches), k = 4
+    "bf16-T700-d128-dff128-E160-k4-skewed-cf1": (case(700, 128, 128, 160, k=4, bias=True), 1.0),
+    # exactly one 64-expert word
+    "bf16-T1000-d128-dff128-E64-skewed-cf1.5": (case(1000, 128, 128, 64, bias=True), 1.5),
 }
 PARAMS = [(n, pol) for n in CASES for pol in (DROP, REROUTE)]
 
