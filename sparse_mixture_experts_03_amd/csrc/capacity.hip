@@ -229,34 +229,49 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
                 for (int j = 0; j < JN; ++j) dst[j] = lane + 64 * j < E ? zr[lane + 64 * j] : 0.0;
             };
 
-            // ---- staging (wavefronts 1 .. kStagers): row sw + kStagers g of each batch (g < kG) belongs to
-            // staging wavefront sw.  A row's candidates are its kCand best keys among the experts that are not at
-            // capacity in the snapshot published two batches earlier (experts only fill up, so the snapshot leaves
-            // out only experts that are still full when the row is walked).  A wavefront's rows of a batch are ranked side by side: each
-            // lane sorts its JN keys (stable odd-even transposition, so equal keys keep the lower expert first),
-            // and every round reduces the lanes' leading keys (one DPP max of the high halves and a ballot; the low
-            // halves and the expert index only on a tie or NaN) and shifts the winning lane's list up by one.
+            // ---- staging (wavefronts 1 .. kStagers).  Rows of one token in a batch share their candidates (the same
+            // kept experts and the same snapshot), so only the first row of each token's run in the batch is ranked
+            // and its candidates are written for the whole run.  Those run starts are dealt out in order: the kG
+            // starts sw, sw + kStagers, ... belong to staging wavefront sw.  A row's candidates are its kCand best
+            // keys among the experts that are not at capacity in the snapshot published two batches earlier
+            // (experts only fill up, so the snapshot leaves out only experts that are still full when the row is
+            // walked).  A wavefront's rows are ranked side by side: each lane sorts its JN keys (stable odd-even
+            // transposition, so equal keys keep the lower expert first), and every round reduces the lanes'
+            // leading keys (one DPP max of the high halves and a ballot; the low halves and the expert index only on
+            // a tie or NaN) and shifts the winning lane's list up by one.
             const int sw = w - 1;
-            auto prefetch = [&](int b, double (&dst)[kG][JN]) {
+            // this wavefront's rows of batch b (-1: none)
+            auto assign = [&](int b, int (&rr)[kG]) {
+                const int q0 = b * rows;
+                const int nr = min(rows, total - q0);
+                const bool start = lane < nr && (lane == 0 || ltok[q0 + lane] != ltok[q0 + lane - 1]);
+                const int idx = __popcll(__ballot(start) & ((1ull << lane) - 1));
 #pragma unroll
-                for (int g = 0; g < kG; ++g) zload(b * rows + sw + kStagers * g, dst[g]);
+                for (int g = 0; g < kG; ++g) {
+                    const uint64_t m = __ballot(start && idx == sw + kStagers * g);
+                    rr[g] = m ? (int)__builtin_ctzll(m) : -1;
+                }
             };
-            auto rank_rows = [&](int q0, int nr, int slot, const double (&zc)[kG][JN], const bool (&fx)[JN]) {
-                constexpr int P = kG;  // this wavefront's rows of the batch, ranked side by side
+            auto prefetch = [&](int b, const int (&rr)[kG], double (&dst)[kG][JN]) {
+#pragma unroll
+                for (int g = 0; g < kG; ++g) zload(b * rows + max(rr[g], 0), dst[g]);
+            };
+            auto rank_rows = [&](int q0, int nr, int slot, const int (&rr)[kG], const double (&zc)[kG][JN],
+                                 const bool (&fx)[JN]) {
+                constexpr int P = kG;
                 uint64_t kv[P][JN];
                 int ix[P][JN];
                 bool fin[P];
-                int rr[P];
 #pragma unroll
                 for (int p = 0; p < P; ++p) {
-                    rr[p] = sw + kStagers * p;
-                    fin[p] = rr[p] >= nr;
-                    row_keys(q0 + min(rr[p], nr - 1), zc[p], kv[p], fx);
+                    fin[p] = rr[p] < 0;
 #pragma unroll
                     for (int j = 0; j < JN; ++j) {
                         ix[p][j] = lane + 64 * j;
-                        if (fin[p]) kv[p][j] = 0;
+                        kv[p][j] = 0;
                     }
+                    if (fin[p]) continue;
+                    row_keys(q0 + rr[p], zc[p], kv[p], fx);
 #pragma unroll
                     for (int pass = 0; pass < JN; ++pass)
 #pragma unroll
@@ -270,6 +285,9 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
                                 ix[p][j + 1] = ti;
                             }
                 }
+                // starts are dealt in order (a third row only if there is a second), so with two rows or fewer only
+                // the first two chains are reduced
+                const bool two = P == 2 || fin[2 % P];
                 uint64_t cw[P];
 #pragma unroll
                 for (int p = 0; p < P; ++p) cw[p] = ~0ull;
@@ -278,7 +296,7 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
                     uint32_t hi[P], mx[P];
 #pragma unroll
                     for (int p = 0; p < P; ++p) mx[p] = hi[p] = (uint32_t)(kv[p][0] >> 32);
-                    if constexpr (P == 4)
+                    if (P == 4 && !two)
                         wave_max_lane63_x4(mx[0], mx[1], mx[2 % P], mx[3 % P]);
                     else
                         wave_max_lane63_x2(mx[0], mx[1 % P]);
@@ -315,22 +333,29 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
                 }
                 if (lane == 0) {
 #pragma unroll
-                    for (int p = 0; p < P; ++p)
-                        if (rr[p] < nr) cand[slot][rr[p]] = cw[p];
+                    for (int p = 0; p < P; ++p) {
+                        if (rr[p] < 0) continue;
+                        const int tk = ltok[q0 + rr[p]];
+                        for (int r2 = rr[p]; r2 < nr && ltok[q0 + r2] == tk; ++r2) cand[slot][r2] = cw[p];
+                    }
                 }
             };
             // batch b's rows are ranked from z requested during the previous batch; batch b + 1's z is requested
             // afterwards (the compiler waits for every outstanding load before the first use of batch b's z, so
             // requests made before the ranking would be waited for there)
-            auto stage = [&](int b, const double (&zc)[kG][JN], double (&zn)[kG][JN]) {
+            auto stage = [&](int b, const int (&rc)[kG], const double (&zc)[kG][JN], int (&rn)[kG],
+                             double (&zn)[kG][JN]) {
                 const int q0 = b * rows;
                 const int nr = min(rows, total - q0);
                 const int slot = b & 1;
                 bool fx[JN];  // expert lane + 64 j is past E or at capacity in the snapshot
 #pragma unroll
                 for (int j = 0; j < JN; ++j) fx[j] = lane + 64 * j >= E || ((snap[slot][j] >> lane) & 1);
-                rank_rows(q0, nr, slot, zc, fx);
-                if (b + 1 < nb) prefetch(b + 1, zn);
+                rank_rows(q0, nr, slot, rc, zc, fx);
+                if (b + 1 < nb) {
+                    assign(b + 1, rn);
+                    prefetch(b + 1, rn, zn);
+                }
             };
 
             // ---- walk (wavefront 0): a batch in one pass, lane l taking row g0 + l.  A lane proposes the m-th of
@@ -461,14 +486,16 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
             };
 
             double za[kG][JN], zb[kG][JN];
+            int ra[kG], rb[kG];
             if (w == 0) {
                 publish(0);
                 publish(1);
             } else {
-                prefetch(0, za);
+                assign(0, ra);
+                prefetch(0, ra, za);
             }
             __syncthreads();
-            if (w != 0) stage(0, za, zb);
+            if (w != 0) stage(0, ra, za, rb, zb);
             __syncthreads();
             for (int b = 0; b < nb; ++b) {
                 if (w == 0) {
@@ -476,9 +503,9 @@ capacity_kernel(int32_t* __restrict__ ids, float* __restrict__ gates, const int3
                     publish(b & 1);  // read when batch b + 2 is staged
                 } else if (b + 1 < nb) {
                     if ((b + 1) & 1)
-                        stage(b + 1, zb, za);
+                        stage(b + 1, rb, zb, ra, za);
                     else
-                        stage(b + 1, za, zb);
+                        stage(b + 1, ra, za, rb, zb);
                 }
                 __syncthreads();
             }
