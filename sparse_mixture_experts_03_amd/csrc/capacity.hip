@@ -19,13 +19,14 @@
 // fill (each choice depends on every earlier one through the expert counts),
 // so it runs on one workgroup: the assignments stream through in chunks of
 // whole tokens and the chunk's overflowing assignments are listed in order
-// with a block scan.  The list is cut into batches; wavefront 0 walks a batch
-// while the other fifteen stage the next one into a double-buffered LDS ring:
-// each listed row's experts as 64-bit keys that order like z (the token's kept
-// experts get key 0), and the row's kCand best keys among the experts that are
-// not at capacity in a snapshot wavefront 0 published two batches earlier
-// (experts only fill up, so a stale snapshot merely leaves in experts that the
-// walk then finds full).
+// with a block scan.  The list is cut into batches of at most 60 rows;
+// wavefront 0 walks a batch while the other fifteen rank the next one into a
+// double-buffered LDS array: a row's candidates are its kCand best experts in
+// z order (the token's kept experts excluded) among those not at capacity in
+// a snapshot wavefront 0 published two batches earlier (experts only fill up,
+// so a stale snapshot merely leaves in experts that the walk then finds full).
+// A token's rows in one batch share their candidates, so each token's run is
+// ranked once.
 //
 // The walk takes up to 64 rows at a time, one per lane.  A lane proposes the
 // first of its ranked candidates that is below capacity and not taken by its
@@ -36,8 +37,8 @@
 // each of them is exactly the sequential greedy choice at its row.  The walk
 // resumes at the conflicting row, or, when a row has used up all kCand ranked
 // candidates, takes that row alone with an exact wavefront reduction over its
-// keys (masked by the current counts and the token's picks; ties go to the
-// lower expert index).  Expert counts live in LDS.
+// keys rebuilt from z (masked by the current counts and the token's picks;
+// ties go to the lower expert index).  Expert counts live in LDS.
 #include "common.hpp"
 #include "launch.hpp"
 
