@@ -48,6 +48,8 @@ CASES = {
     "bf16-T700-d128-dff128-E160-k4-skewed-cf1": (case(700, 128, 128, 160, k=4, bias=True), 1.0),
     # exactly one 64-expert word
     "bf16-T1000-d128-dff128-E64-skewed-cf1.5": (case(1000, 128, 128, 64, bias=True), 1.5),
+    # k = 1: every overflowing assignment is its token's only one
+    "bf16-T1500-d128-dff128-E32-k1-skewed-cf1": (case(1500, 128, 128, 32, k=1, bias=True), 1.0),
 }
 PARAMS = [(n, pol) for n in CASES for pol in (DROP, REROUTE)]
 
