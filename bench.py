@@ -14,9 +14,11 @@ The metric has two halves, measured in one run:
   * prefill (default: 4096 tokens, d = 4096, d_ff = 16384, 16 experts, skewed
     routing), bound by the bf16 matrix cores: the nested "prefill" object.
 For each: K timed steps after W warm-ups, each step bracketed by HIP events on
-the stream it runs on, with a 512 MB buffer touched between steps (outside the
-events) so the 256 MB Infinity Cache cannot carry weights from one step to
-the next; tokens/s from the median step.  Then K more steps replay the layer
+the stream it runs on, with a 512 MB buffer read between steps (outside the
+events, a matrix-vector product that writes 256 KB) so the 256 MB Infinity
+Cache cannot carry weights from one step to the next; tokens/s from the
+median step.  (Reading evicts the cache as writing does; a write touch would
+also leave dirty lines whose write-back slows the next step's kernels.)  Then K more steps replay the layer
 through the stage entry points (router, permute, W1, W2, combine) with events
 between the stages: each stage's average duration, and the roofline of both
 expert GEMMs (algorithmic bytes or flops per launch / duration), the longer
@@ -50,6 +52,17 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector
 FLUSH_BYTES = 512 << 20
+
+
+def make_touch(torch, dev):
+    """A read of FLUSH_BYTES between steps: a matrix-vector product over the
+    buffer viewed as fp32 rows of 2048 (rocBLAS gemv, bandwidth-bound), whose
+    only write is its 256 KB result vector."""
+    buf = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    mat = buf.view(torch.float32).view(-1, 2048)
+    vec = torch.zeros(2048, dtype=torch.float32, device=dev)
+    res = torch.empty(mat.shape[0], dtype=torch.float32, device=dev)
+    return lambda: torch.mv(mat, vec, out=res)
 COPY_BYTES = 1 << 30           # the calibration copy
 
 
@@ -63,7 +76,7 @@ def parse(argv=None):
                     help="second workload measured in the same run ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="oracle seconds per timed leg (about)")
-    ap.add_argument("--no-flush", action="store_true", help="do not touch a 512 MB buffer between steps")
+    ap.add_argument("--no-flush", action="store_true", help="do not read a 512 MB buffer between steps")
     ap.add_argument("--capacity-factor", type=float, default=0.0, help="0: dropless dispatch")
     ap.add_argument("--capacity-policy", choices=["drop", "reroute"], default="drop")
     ap.add_argument("--gate-norm", action="store_true", help="gates renormalised over the k chosen experts")
@@ -159,7 +172,7 @@ def measure(name, args, dev, torch, np, moe, moe_synth, with_cpu):
     layer = moe.MoELayerForward(c, device=dev)
     stream = torch.cuda.current_stream()
     tm = StreamTimer(torch, stream)
-    flush = None if args.no_flush else torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush = None if args.no_flush else make_touch(torch, dev)
     run = lambda: layer(inp["x"], inp["Wg"], inp["bias"], inp["W1"], inp["W2"], inp["S1"], inp["S2"],
                         W_in=inp["W_in"], b_in=inp["b_in"])
 
@@ -171,7 +184,7 @@ def measure(name, args, dev, torch, np, moe, moe_synth, with_cpu):
     t0 = time.perf_counter()
     for _ in range(args.steps):
         if flush is not None:
-            flush.add_(1)  # reads and writes 512 MB: evicts the previous step's lines from the MALL
+            flush()  # reads 512 MB: evicts the previous step's lines from the MALL
         a = tm.mark()
         run()
         marks.append((a, tm.mark()))
@@ -220,7 +233,7 @@ def measure(name, args, dev, torch, np, moe, moe_synth, with_cpu):
         per = {s: [] for s, _ in stages}
         for _ in range(args.steps):
             if flush is not None:
-                flush.add_(1)
+                flush()
             prev = tm.mark()
             for s, fn in stages:
                 fn()
@@ -280,7 +293,7 @@ def measure(name, args, dev, torch, np, moe, moe_synth, with_cpu):
                    "capacity_factor": args.capacity_factor,
                    "capacity_policy": args.capacity_policy if args.capacity_factor > 0 else None,
                    "gate_norm": int(args.gate_norm), "noise_std": args.noise_std, "expert_act": args.expert_act,
-                   "router_hidden": args.router_hidden, "mall_flush_between_steps": flush is not None},
+                   "router_hidden": args.router_hidden, "mall_flush_between_steps": "read 512 MB" if flush is not None else None},
         "layer_hbm_frac": round(step_bytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "layer_mfma_frac": round(step_flops / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "active_experts": active,
@@ -316,7 +329,7 @@ def library_dense_gemm(torch, M, N, K, flush, reps=10):
     ms = []
     for _ in range(reps):
         if flush is not None:
-            flush.add_(1)
+            flush()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         torch.matmul(a, b, out=c)
