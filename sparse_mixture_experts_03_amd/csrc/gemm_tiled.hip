@@ -182,14 +182,20 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[TI][TJ], uint
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int i = 0; i < TI; ++i)
+        for (int i = 0; i < TI; ++i) {
+            // one 32 x 32 block at a time: the empty statement pins the block to the accumulator registers
+            // until here, so the compiler does not copy every block out of them at once (more registers
+            // than are left beside the accumulators)
+            f32x16 blk = acc[i][j];
+            asm volatile("" : "+a"(blk));
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 uint2 packed;
-                packed.x = pack_bf16x2(act_f(acc[i][j][4 * q], ACT), act_f(acc[i][j][4 * q + 1], ACT));
-                packed.y = pack_bf16x2(act_f(acc[i][j][4 * q + 2], ACT), act_f(acc[i][j][4 * q + 3], ACT));
+                packed.x = pack_bf16x2(act_f(blk[4 * q], ACT), act_f(blk[4 * q + 1], ACT));
+                packed.y = pack_bf16x2(act_f(blk[4 * q + 2], ACT), act_f(blk[4 * q + 3], ACT));
                 *reinterpret_cast<uint2*>(wl + (32 * j + r) * STRIDE + (32 * i + 8 * q + 4 * h) * 2) = packed;
             }
+        }
     constexpr int CH = NW * 2 / 16, RPI = 64 / CH;  // chunks per row, rows per instruction
     const int cr = lane / CH, cc = lane % CH;
     const int n = n0 + wn + cc * 8;  // N is a multiple of 8
@@ -254,11 +260,13 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TI][TJ], void* __
             for (int i = 0; i < TI; ++i) {
                 const int nb = n0 + wn + 32 * i;
                 if (nb >= N) continue;
+                f32x16 blk = acc[i][j];
+                asm volatile("" : "+a"(blk));  // one block out of the accumulator registers at a time
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
                     float hv[4];
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) hv[c] = silu_f(acc[i][j][4 * q + c]) * acc[i][j][4 * q + 8 + c];
+                    for (int c = 0; c < 4; ++c) hv[c] = silu_f(blk[4 * q + c]) * blk[4 * q + 8 + c];
                     uint2 packed;
                     packed.x = pack_bf16x2(hv[0], hv[1]);
                     packed.y = pack_bf16x2(hv[2], hv[3]);
@@ -770,6 +778,232 @@ __device__ __forceinline__ void tile_gemm_bf16(uint8_t* lds, const uint16_t* __r
 }
 
 
+// ---- bf16 GEMM2, 256 dispatch rows: two wavefront groups in ping-pong ----
+// The K-stages of 64 and the LDS layout of tile_gemm_bf16 (whole 128-byte
+// lines per tile row, 32 KB per operand and stage): kPpW weight slots and
+// kPpX dispatch-row slots, 160 KB in all.  Whole-line copies matter here:
+// with K-stages of 32 (half lines) the copies alone took longer than the
+// MFMAs (dense 4096 x 16384 x 4096: 0.37 ms of copies against 0.33 ms of
+// MFMAs and fragment reads), twice as long again with 32 KB rows.
+//
+// Group 0 (wavefronts 0-3, one per SIMD) and group 1 (wavefronts 4-7, the
+// other wavefront of each SIMD) take turns: time is cut into phases ended
+// by a workgroup barrier, and in every phase one group multiplies one half
+// of a stage (16 MFMAs per wavefront, K = 32, from fragments already in
+// registers) while the other reads its fragments of the next half from LDS
+// and issues copies.  Each SIMD's matrix pipe is then fed by one wavefront
+// while the other's LDS reads and copies run beside it, and no wavefront
+// waits on its own reads.  Half-stage h (stage h / 2) is multiplied by
+// group 0 in phase 2h and by group 1 in phase 2h + 1; group 0 reads its
+// fragments in phase 2h - 1, group 1 in phase 2h.
+//
+// Copies: group 0 copies the weight tile, group 1 the dispatch rows, each
+// wavefront 64 tile rows (8 loads of 8 rows x 128 bytes) per stage, issued
+// as two halves of 4 loads in two phases (all 8 at once stalled the
+// issuing wavefronts: GEMM2 5% slower).  Stage s is last read in phase
+// 4s + 2 (group 1, half-stage 2s + 1), and stage s + 1 must be published
+// by the barrier ending phase 4s + 2.  Group 1 issues the first half of
+// dispatch-row stage s + kPpX right after its own reads of phase 4s + 2
+// have returned (group 0 read that half-stage a phase earlier) and the
+// second half in phase 4s + 4; it waits for its loads of stage s + 1 in
+// phase 4s + 2.  Group 0 issues the halves of weight stage s + kPpW in
+// phases 4s + 3 and 4s + 5 and waits for its loads of stage s + 1 after its
+// MFMAs of phase 4s + 2.  Fragment reads are waited for before the barrier
+// that ends their phase, so no slot is refilled under a read.
+//
+// Measured against tile_gemm_bf16 on 256-row tiles (same box, round-robin):
+// GEMM2 3-5% faster on the skewed 16- and 128-expert prefills, GEMM1 2-4%
+// slower on the 16-expert one, so GEMM1 keeps tile_gemm_bf16.
+constexpr int kPpW = 3, kPpX = 2;
+
+template <int OFF>
+__device__ __forceinline__ bf16x8 ds_read16_at(uint32_t addr) {
+    bf16x8 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+    return v;
+}
+
+// stages kt0 .. kt0 + ns - 1 of 64 along K
+template <int WHICH, int ACT>
+__device__ __forceinline__ void tile_gemm_bf16_pp(uint8_t* lds, const uint16_t* __restrict__ A,
+                                                  const int32_t* __restrict__ a_rows, const void* Wexp,
+                                                  void* __restrict__ out, int N, int K, int n0, int p0, int rows,
+                                                  int kt0, int ns) {
+    constexpr int TI = 4, TJ = 2;
+    constexpr uint32_t kSlot = 256 * 128;
+    static_assert((kPpW + kPpX) * kSlot <= kBf16LdsBytes, "rings exceed the kernel's LDS");
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;
+    const int v = wave & 3;
+    const int R = grp == 0 ? kPpW : kPpX;  // this group's ring
+    const uint32_t wring = lds_addr(lds), xring = lds_addr(lds + kPpW * kSlot);
+
+    // this wavefront's copies: tile rows [64 v, 64 v + 64) of its group's operand, 8 rows x 128 bytes per
+    // load; lane L moves logical segment (L & 7) ^ ((row >> 1) & 7) of row L >> 3 of its block, which lands
+    // at LDS byte 16 L of the block.  Rows past N (weights) or past the tile's rows (tokens) are clamped:
+    // they only feed outputs that are never stored.
+    const uint32_t rowbytes = (uint32_t)K * 2;
+    const char* src = grp == 0 ? reinterpret_cast<const char*>(Wexp) : reinterpret_cast<const char*>(A);
+    uint32_t goff[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int trow = 64 * v + 8 * q + (lane >> 3);
+        const uint32_t seg = (uint32_t)((lane & 7) ^ ((trow >> 1) & 7));
+        if (grp == 0) {
+            goff[q] = (uint32_t)min(n0 + trow, N - 1) * rowbytes + 16 * seg;
+        } else {
+            const int drow = min(trow, rows - 1);
+            const uint32_t arow = (WHICH == 1) ? (uint32_t)a_rows[p0 + drow] : (uint32_t)(p0 + drow);
+            goff[q] = arow * rowbytes + 16 * seg;
+        }
+    }
+    uint8_t* const ring = lds + grp * (kPpW * kSlot) + 8192 * v;
+    // half hf of this wavefront's loads of stage st: tile rows 64 v + 32 hf .. + 32
+    auto issue_half = [&](int st, int hf) {
+        if (st >= ns) return;
+        const uint32_t kb = (uint32_t)(kt0 + st) * 128;
+        uint8_t* slot = ring + (st % R) * kSlot;
+        if (hf == 0) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) copy_rows_to_lds(src, goff[q] + kb, slot + 1024 * q);
+        } else {
+#pragma unroll
+            for (int q = 4; q < 8; ++q) copy_rows_to_lds(src, goff[q] + kb, slot + 1024 * q);
+        }
+    };
+    // wait until at most n of this wavefront's loads are in flight (n a multiple of 4, at most 16)
+    auto wait_loads = [&](int n) {
+        if (n >= 16) wait_vmcnt<16>();
+        else if (n >= 12) wait_vmcnt<12>();
+        else if (n >= 8) wait_vmcnt<8>();
+        else if (n >= 4) wait_vmcnt<4>();
+        else wait_vmcnt<0>();
+    };
+
+    // fragments of half-stage hs: weight rows wn + 32 i + r and dispatch rows wm + 32 j + r, k-substep
+    // 2 (hs & 1) + ks; lane half h reads logical segment 2 (2 (hs & 1) + ks) + h; tiles i and j sit 4 KB apart
+    // with the same permutation
+    const int wn = (wave & 1) * 128;
+    const int wm = (wave >> 1) * 64;
+    const int r = lane & 31;
+    const int h = lane >> 5;
+    const uint32_t swz = (uint32_t)((r >> 1) & 7);
+    uint32_t lw[4], lx[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+        const uint32_t so = 16 * ((uint32_t)(2 * s4 + h) ^ swz);
+        lw[s4] = (uint32_t)(wn + r) * 128 + so;
+        lx[s4] = (uint32_t)(wm + r) * 128 + so;
+    }
+    bf16x8 wf[2][TI], xf[2][TJ];
+    auto read_frags = [&](int hs, auto hi) {  // hi = hs & 1, a compile-time constant
+        const int st = hs >> 1;
+        const uint32_t wb = wring + (st % kPpW) * kSlot, xb = xring + (st % kPpX) * kSlot;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const uint32_t aw = wb + lw[2 * decltype(hi)::value + ks], ax = xb + lx[2 * decltype(hi)::value + ks];
+            wf[ks][0] = ds_read16_at<0>(aw);
+            wf[ks][1] = ds_read16_at<4096>(aw);
+            wf[ks][2] = ds_read16_at<8192>(aw);
+            wf[ks][3] = ds_read16_at<12288>(aw);
+            xf[ks][0] = ds_read16_at<0>(ax);
+            xf[ks][1] = ds_read16_at<4096>(ax);
+        }
+    };
+    auto wait_frags = [&] {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int i = 0; i < TI; ++i) asm volatile("" : "+v"(wf[ks][i]));
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) asm volatile("" : "+v"(xf[ks][j]));
+        }
+    };
+    f32x16 acc[TI][TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    auto mma = [&] {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32x32x16(wf[ks][i], xf[ks][j], acc[i][j]);
+    };
+    const int nh = 2 * ns;
+    // a wavefront's step outside its multiply phases: the fragments of half-stage m, and the copies and
+    // waits that fall in that phase
+    using Even = std::integral_constant<int, 0>;
+    using Odd = std::integral_constant<int, 1>;
+    auto fetch = [&](int m, auto odd) {  // odd = m & 1
+        if (m >= nh) return;
+        read_frags(m, odd);
+        if (grp == 0) {
+            // weight stage m / 2 - 1 + kPpW into the slot of stage m / 2 - 1, no longer read
+            if (m >= 2) issue_half(m / 2 - 1 + kPpW, decltype(odd)::value);
+            wait_frags();
+        } else {
+            wait_frags();
+            if (decltype(odd)::value) {  // that was the last read of stage st: its slot takes stage st + kPpX
+                const int st = m / 2;
+                issue_half(st + kPpX, 0);
+                if (st + 1 < ns) wait_loads(st + 2 < ns ? 4 : 0);  // stage st + 1 in, half of st + 2 in flight
+            } else if (m >= 2) {
+                issue_half(m / 2 - 1 + kPpX, 1);
+            }
+        }
+    };
+    // Both groups run the same loop, multiply | barrier | fetch | barrier; group 1 enters it one phase
+    // later (one more barrier before it, one fewer after the epilogue), so its multiply phases are group 0's
+    // fetch phases.  The multiplies stay in straight-line code, which keeps the accumulators in AGPRs.  The
+    // scheduling fences keep each phase's instructions on its side of the barrier (MFMAs are not memory
+    // operations, so the barrier alone would not hold them).
+    auto phase_end = [] {
+        __builtin_amdgcn_sched_barrier(0);
+        barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int st = 0; st < R; ++st) {
+        issue_half(st, 0);
+        issue_half(st, 1);
+    }
+    wait_loads(8 * (min(R, ns) - 1));  // stage 0 in
+    barrier();
+    fetch(0, Even{});
+    if (grp == 1) phase_end();
+    for (int st = 0; st < ns; ++st) {  // half-stages 2 st and 2 st + 1
+        mma();
+        phase_end();
+        fetch(2 * st + 1, Odd{});
+        phase_end();
+        mma();
+        if (grp == 0 && st + 1 < ns) wait_loads(st + 2 < ns ? 8 : 0);  // weights: st + 1 in, st + 2 in flight
+        phase_end();
+        fetch(2 * st + 2, Even{});
+        phase_end();
+    }
+    // every load has landed and every fragment read has returned: the epilogue may stage through the rings
+    if constexpr (WHICH == 1 && ACT != kActSwiglu) {
+        store_tile_lds<TI, TJ, ACT, 8, kBf16LdsBytes>(acc, lds, out, N, n0, p0, rows, wn, wm, r, h, true);
+    } else if constexpr (WHICH == 2) {
+        store_tile_lds_f32<TI, TJ, 8, kBf16LdsBytes>(acc, lds, static_cast<float*>(out), N, n0, p0, rows, wn, wm,
+                                                    r, h, true);
+    } else {
+        store_tile<WHICH, TI, TJ, ACT>(acc, out, N, n0, p0, rows, wn, wm, r, h);
+    }
+    // group 0 has passed one barrier fewer; it takes it here, where the accumulators are no longer live (a
+    // conditional barrier while they are makes the compiler copy them all out of the AGPRs)
+    if (grp == 0) barrier();
+}
+
+
 // W: the experts' weights, W_stride bytes apart (bf16 [N][K] or INT4 codes
 // [N][K/2]); Wsc: INT4 scales bf16 [E][N][K/128] (unused for bf16).  Only
 // experts holding more than rows_lo rows are multiplied here.
@@ -840,12 +1074,16 @@ gemm_tiled_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict
     rows = __builtin_amdgcn_readfirstlane(rows);
     const int n0 = nt * kTBN;
     const void* Wexp = W + (int64_t)e * W_stride;
-    if (rows > 128)
-        tile_gemm_bf16<WHICH, 4, 2, 256, ACT>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows, kt0, nk);
-    else if (rows > 64)
+    if (rows > 128) {
+        if constexpr (WHICH == 2)
+            tile_gemm_bf16_pp<WHICH, ACT>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows, kt0, nk);
+        else
+            tile_gemm_bf16<WHICH, 4, 2, 256, ACT>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows, kt0, nk);
+    } else if (rows > 64) {
         tile_gemm_bf16<WHICH, 2, 2, 128, ACT>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows, kt0, nk);
-    else
+    } else {
         tile_gemm_bf16<WHICH, 2, 2, 64, ACT, 4>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows, kt0, nk);
+    }
 }
 
 }  // namespace
