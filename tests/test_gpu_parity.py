@@ -121,6 +121,13 @@ FORWARD_CASES = {
     # N tails (576 = 2 x 256 + 64 for W1, 320 for W2) on every tiled tile height: 256-, 128- and 64-row tiles
     "bf16-T300-d320-dff576-E8-skewed-ntail": (case(300, 320, 576, 8, bias=True), [moe.GEMM_TILED]),
     "bf16-T40-d256-dff256-E256-k8": (case(40, 256, 256, 256, k=8), [moe.GEMM_STREAMING, moe.GEMM_TILED]),
+    # short GEMM2 K ranges on 256-row tiles (the two-group schedule's prologue and last waits): K = 64 (one
+    # stage), 128 (two K halves of one stage in the layer), 192 (three stages), 384 (halves of three stages,
+    # with N = 320 leaving a 64-row weight tile)
+    "bf16-T600-d256-dff64-E3": (case(600, 256, 64, 3), [moe.GEMM_TILED]),
+    "bf16-T600-d256-dff128-E3-skewed": (case(600, 256, 128, 3, bias=True), [moe.GEMM_TILED]),
+    "bf16-T600-d192-dff192-E3": (case(600, 192, 192, 3), [moe.GEMM_TILED]),
+    "bf16-T640-d320-dff384-E2-skewed": (case(640, 320, 384, 2, bias=True), [moe.GEMM_TILED]),
     "bf16-T9-d256-dff512-E1-k1": (case(9, 256, 512, 1, k=1), [moe.GEMM_STREAMING, moe.GEMM_TILED]),
     # streaming with 32-row (T <= 32) and 64-row dispatch tiles
     "bf16-T24-d512-dff1024-E4": (case(24, 512, 1024, 4), [moe.GEMM_STREAMING]),
