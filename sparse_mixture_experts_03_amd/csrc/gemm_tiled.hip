@@ -308,8 +308,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TI][TJ], void* __
 // wavefronts of 128 x 128; XROWS = 128: 4 x 1 of 64 x 128; XROWS = 64: 4 x 1
 // of 64 x 64.  The smaller shapes serve the last, partial tile of an expert
 // so that a remainder of 40 rows costs a quarter tile, not a full one.
-// WQ = kBF16: Wexp is the expert's bf16 [N][K] matrix; WQ = kINT4: its packed
-// codes [N][K/2] with bf16 scales Wsc [N][K/128].
+// Wexp is the expert's packed INT4 codes [N][K/2], Wsc its bf16 scales
+// [N][K/128] (bf16 experts use tile_gemm_bf16 and tile_gemm2_bf16_pp).
 template <int WQ, int WHICH, int TI, int TJ, int XROWS, int ACT>
 __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*Xt)[kTileBytes], uint8_t (*Ct)[4096],
                                           uint8_t (*St)[4096],
@@ -389,217 +389,161 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
     auto no_mid = [] {};
 
     const int nk = K / kTBK;
-    if constexpr (WQ == kBF16) {
-        // This wavefront copies tile rows [64 * wave, 64 * wave + 64) of the
-        // weight tile, and of the dispatch tile if they lie inside XROWS, 16
-        // rows per instruction (4 instructions per operand per stage).  Rows
-        // past N (weights) or past the tile's dispatch rows (tokens) are
-        // clamped to a valid row: they only feed outputs that are never stored.
-        const bool xload = 64 * wave < XROWS;
-        const char* wbase = reinterpret_cast<const char*>(Wexp);
-        uint32_t woff[4], xoff[4];
+    static_assert(WQ == kINT4, "bf16 experts use tile_gemm_bf16 and tile_gemm2_bf16_pp");
+    // The 16 code bytes per weight-tile row for stage j, C(j), are
+    // copied at step j-4 into code slot j % 4 (one direct-to-LDS load per
+    // wavefront: lane L's bytes land at 16 L of the wavefront's 1 KB, and
+    // each wavefront dequantises only the rows it copied itself, so its own
+    // vmcnt guards them),
+    // and the dispatch rows X(j) at step j-3, spread evenly over the four
+    // wavefronts (XROWS / 64 loads each).  A wavefront's loads thus go out
+    // in the order
+    //   C(0) X(0) C(1) X(1) C(2) X(2) C(3) | X(3) C(4) | X(4) C(5) | ...
+    // (prologue | step 0 | step 1 ...), and a wait for one of them counts
+    // the loads issued after it.  The scales of the row's next 8 groups
+    // (16 bytes, 32 stages) follow the same route every 32 stages, issued
+    // before the codes of the first stage that needs them; being extra
+    // loads that the counts leave out, they can only lengthen a wait.
+    // Step s:
+    //   wait for X(s) and for this thread's LDS stores (W(s), written at
+    //   step s-1); barrier (publishes stage s, frees the slot of s-1);
+    //   issue X(s+3) into that slot and C(s+4); wait for C(s+1) and read
+    //   its codes; multiply stage s, expanding those codes to bf16 in
+    //   registers between the MFMAs of its first substep (one wavefront
+    //   per SIMD: VALU work placed between MFMAs runs while they execute,
+    //   6 operations after each MFMA measured best); then store them to
+    //   LDS slot (s+1) % 4 (last read at step s-3, before the barrier of
+    //   step s-2).
+    // K is a multiple of 1024: the stages come in whole blocks of 32.
+    constexpr int XL = XROWS / 64;  // dispatch-row loads per wavefront per stage
+    const char* cbase = reinterpret_cast<const char*>(Wexp);
+    const char* sbase = reinterpret_cast<const char*>(Wsc);
+    // lane L of wavefront w copies the codes (and scales) of weight-tile
+    // row 64 (L / 16) + 16 w + L % 16: the rows this wavefront dequantises
+    const uint32_t wrow = (uint32_t)min(n0 + 64 * (lane >> 4) + 16 * wave + (lane & 15), N - 1);
+    const uint32_t coff = wrow * ((uint32_t)K / 2);
+    const uint32_t soff = wrow * ((uint32_t)K / 128) * 2;
+    // rows past the tile's dispatch rows are clamped (as above)
+    uint32_t xoff_e[XL];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int trow = 64 * wave + 16 * i + (lane >> 2);
-            woff[i] = (uint32_t)min(n0 + trow, N - 1) * xrowbytes + 16 * lseg;
-            const int drow = min(trow, rows - 1);
-            const uint32_t arow = (WHICH == 1) ? (uint32_t)a_rows[p0 + drow] : (uint32_t)(p0 + drow);
-            xoff[i] = arow * xrowbytes + 16 * lseg;
-        }
-        // 4 (weights) + 4 (dispatch rows, when this wavefront copies any) loads per stage
-        auto issue = [&](int kt, int buf) {
-            const uint32_t kb = (uint32_t)kt * (kTBK * 2);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) copy_rows_to_lds(wbase, woff[i] + kb, &Wt[buf][(64 * wave + 16 * i) * 64]);
-            if (xload) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) copy_rows_to_lds(xbase, xoff[i] + kb, &Xt[buf][(64 * wave + 16 * i) * 64]);
-            }
-        };
-        // wait until at most `stages` later stages of this wavefront's loads are in flight
-        auto wait_stages = [&](int stages) {
-            if (xload) {
-                if (stages >= 2) wait_vmcnt<16>(); else if (stages == 1) wait_vmcnt<8>(); else wait_vmcnt<0>();
-            } else {
-                if (stages >= 2) wait_vmcnt<8>(); else if (stages == 1) wait_vmcnt<4>(); else wait_vmcnt<0>();
-            }
-        };
-
-        // Ring of kStages buffers.  Step k waits until its own loads have landed
-        // (the loads of the two later stages stay in flight), then one barrier
-        // both publishes stage k and frees the buffer of stage k-1, into which
-        // stage k+3 is issued.  The steady state runs in a loop without exits;
-        // the last steps drain the ring.
-        const int pre = min(nk, kStages - 1);
-        for (int s = 0; s < pre; ++s) issue(s, s);
-        int kt = 0;
-        for (; kt + kStages - 1 < nk; ++kt) {
-            wait_stages(2);
-            barrier();
-            issue(kt + kStages - 1, (kt + kStages - 1) % kStages);
-            compute(kt % kStages, no_mid);
-        }
-        for (; kt < nk; ++kt) {  // drain: every remaining stage is already issued
-            wait_stages(nk - kt - 1);
-            barrier();
-            compute(kt % kStages, no_mid);
-        }
-    } else {
-        // INT4: the 16 code bytes per weight-tile row for stage j, C(j), are
-        // copied at step j-4 into code slot j % 4 (one direct-to-LDS load per
-        // wavefront: lane L's bytes land at 16 L of the wavefront's 1 KB, and
-        // each wavefront dequantises only the rows it copied itself, so its own
-        // vmcnt guards them),
-        // and the dispatch rows X(j) at step j-3, spread evenly over the four
-        // wavefronts (XROWS / 64 loads each).  A wavefront's loads thus go out
-        // in the order
-        //   C(0) X(0) C(1) X(1) C(2) X(2) C(3) | X(3) C(4) | X(4) C(5) | ...
-        // (prologue | step 0 | step 1 ...), and a wait for one of them counts
-        // the loads issued after it.  The scales of the row's next 8 groups
-        // (16 bytes, 32 stages) follow the same route every 32 stages, issued
-        // before the codes of the first stage that needs them; being extra
-        // loads that the counts leave out, they can only lengthen a wait.
-        // Step s:
-        //   wait for X(s) and for this thread's LDS stores (W(s), written at
-        //   step s-1); barrier (publishes stage s, frees the slot of s-1);
-        //   issue X(s+3) into that slot and C(s+4); wait for C(s+1) and read
-        //   its codes; multiply stage s, expanding those codes to bf16 in
-        //   registers between the MFMAs of its first substep (one wavefront
-        //   per SIMD: VALU work placed between MFMAs runs while they execute,
-        //   6 operations after each MFMA measured best); then store them to
-        //   LDS slot (s+1) % 4 (last read at step s-3, before the barrier of
-        //   step s-2).
-        // K is a multiple of 1024: the stages come in whole blocks of 32.
-        constexpr int XL = XROWS / 64;  // dispatch-row loads per wavefront per stage
-        const char* cbase = reinterpret_cast<const char*>(Wexp);
-        const char* sbase = reinterpret_cast<const char*>(Wsc);
-        // lane L of wavefront w copies the codes (and scales) of weight-tile
-        // row 64 (L / 16) + 16 w + L % 16: the rows this wavefront dequantises
-        const uint32_t wrow = (uint32_t)min(n0 + 64 * (lane >> 4) + 16 * wave + (lane & 15), N - 1);
-        const uint32_t coff = wrow * ((uint32_t)K / 2);
-        const uint32_t soff = wrow * ((uint32_t)K / 128) * 2;
-        // rows past the tile's dispatch rows are clamped (as above)
-        uint32_t xoff_e[XL];
-#pragma unroll
-        for (int i = 0; i < XL; ++i) {
-            const int trow = wave * (XROWS / 4) + 16 * i + (lane >> 2);
-            const int drow = min(trow, rows - 1);
-            const uint32_t arow = (WHICH == 1) ? (uint32_t)a_rows[p0 + drow] : (uint32_t)(p0 + drow);
-            xoff_e[i] = arow * xrowbytes + 16 * lseg;
-        }
-        auto issue_xe = [&](int kt, int buf) {
-            const uint32_t kb = (uint32_t)kt * (kTBK * 2);
-#pragma unroll
-            for (int i = 0; i < XL; ++i)
-                copy_rows_to_lds(xbase, xoff_e[i] + kb, &Xt[buf][(wave * (XROWS / 4) + 16 * i) * 64]);
-        };
-        auto issue_c = [&](int kt) { copy_rows_to_lds(cbase, coff + (uint32_t)kt * 16, &Ct[kt % kStages][wave * 1024]); };
-        auto issue_scales = [&](int blk) {  // groups 8 blk .. 8 blk + 7 (stages 32 blk .. 32 blk + 31)
-            copy_rows_to_lds(sbase, soff + (uint32_t)blk * 16, &St[blk & 1][wave * 1024]);
-        };
-        // Dequantisation: thread (wavefront w, lane l) writes 16-byte physical
-        // slot l & 3 of weight-tile rows 64 j + 16 w + l / 4, j = 0..3, so each
-        // of its LDS stores covers 1 KB contiguously (free of bank conflicts);
-        // that slot holds logical segment lseg of every one of those rows.  Row
-        // 64 j + 16 w + r was copied by lane 16 j + r of this wavefront: its
-        // codes sit at 1024 w + 256 j + 16 r of the code slot.
-        const uint32_t cread = lds_addr(Ct[0]) + 1024 * wave + 16 * (lane >> 2) + 4 * lseg;
-        const uint32_t sread = lds_addr(St[0]) + 1024 * wave + 16 * (lane >> 2);
-        const uint32_t wdst = 1024 * wave + 16 * lane;
-        uint32_t sc0, sc1, sc2, sc3;  // group scales of this thread's four rows
-        auto read_scales = [&](int g) {
-            ds_read_scales(sread + (uint32_t)((g >> 3) & 1) * 4096 + (uint32_t)(g & 7) * 2, sc0, sc1, sc2, sc3);
-        };
-        // rem = stages after s (>= 0); the counts follow the issue order above
-        auto wait_x = [&](int rem) {
-            if (rem >= 3) wait_vmcnt<3 + 2 * XL>();
-            else if (rem == 2) wait_vmcnt<2 + 2 * XL>();
-            else if (rem == 1) wait_vmcnt<1 + XL>();
-            else wait_vmcnt<0>();
-        };
-        // C(s+1) landed; rem = stages after s (>= 1)
-        auto wait_c = [&](int rem) {
-            if (rem >= 4) wait_vmcnt<3 + 3 * XL>();
-            else if (rem == 3) wait_vmcnt<2 + 3 * XL>();
-            else if (rem == 2) wait_vmcnt<1 + 2 * XL>();
-            else wait_vmcnt<XL>();
-        };
-        auto dequant = [&](int j) {  // stage j's codes -> LDS slot j % 4 (scales of group j / 4 loaded)
-            uint32_t w0, w1, w2, w3;
-            ds_read_codes(cread + (uint32_t)(j % kStages) * 4096, w0, w1, w2, w3);
-            const uint32_t wb = lds_addr(Wt[j % kStages]) + wdst;
-            dequant_word_to_lds(w0, sc0, wb);
-            dequant_word_to_lds(w1, sc1, wb + 4096);
-            dequant_word_to_lds(w2, sc2, wb + 8192);
-            dequant_word_to_lds(w3, sc3, wb + 12288);
-        };
-        // prologue
-        issue_scales(0);
-        issue_c(0);
-        issue_xe(0, 0);
-        issue_c(1);
-        issue_xe(1, 1);
-        issue_c(2);
-        issue_xe(2, 2);
-        issue_c(3);
-        wait_c(4);
-        read_scales(0);
-        dequant(0);
-
-        // one step; J = s % 4 (static), rem = nk - 1 - s (static in each call below)
-        auto step = [&](int s, const int J, const int rem) {
-            wait_x(rem);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            barrier();
-            if (rem >= 3) issue_xe(s + 3, (J + 3) % kStages);
-            if (rem >= 4) issue_c(s + 4);
-            if (rem >= 1) {
-                // stage s + 1's codes are expanded between the MFMAs of stage s's
-                // first substep and written to their (free) slot after stage s
-                wait_c(rem);
-                if (J == 3) read_scales((s + 1) >> 2);
-                uint32_t w0, w1, w2, w3;
-                ds_read_codes(cread + (uint32_t)((s + 1) % kStages) * 4096, w0, w1, w2, w3);
-                uint4 d0, d1, d2, d3;
-                compute(J, [&] {
-                    d0 = dequant_word(w0, sc0);
-                    d1 = dequant_word(w1, sc1);
-                    d2 = dequant_word(w2, sc2);
-                    d3 = dequant_word(w3, sc3);
-                    // one MFMA, then a share of the expansion's VALU operations, in turn
-#pragma unroll
-                    for (int m = 0; m < TI * TJ; ++m) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x002, kInt4MixValu, 0);
-                    }
-                });
-                const uint32_t wb = lds_addr(Wt[(s + 1) % kStages]) + wdst;
-                ds_write16(wb, d0.x, d0.y, d0.z, d0.w);
-                ds_write16(wb + 4096, d1.x, d1.y, d1.z, d1.w);
-                ds_write16(wb + 8192, d2.x, d2.y, d2.z, d2.w);
-                ds_write16(wb + 12288, d3.x, d3.y, d3.z, d3.w);
-                return;
-            }
-            if (rem >= 1) {
-                wait_c(rem);
-                if (J == 3) read_scales((s + 1) >> 2);  // stage s + 1 opens a new group
-                dequant(s + 1);
-            }
-            compute(J, no_mid);
-        };
-        int s0 = 0;
-        for (; s0 + 8 <= nk; s0 += 4) {  // steady state: every step has 4 or more stages after it
-            if ((s0 & 31) == 0 && s0 + 32 < nk) issue_scales((s0 >> 5) + 1);
-            step(s0, 0, 4);
-            step(s0 + 1, 1, 4);
-            step(s0 + 2, 2, 4);
-            step(s0 + 3, 3, 4);
-        }
-        step(s0, 0, 3);  // the last four stages
-        step(s0 + 1, 1, 2);
-        step(s0 + 2, 2, 1);
-        step(s0 + 3, 3, 0);
+    for (int i = 0; i < XL; ++i) {
+        const int trow = wave * (XROWS / 4) + 16 * i + (lane >> 2);
+        const int drow = min(trow, rows - 1);
+        const uint32_t arow = (WHICH == 1) ? (uint32_t)a_rows[p0 + drow] : (uint32_t)(p0 + drow);
+        xoff_e[i] = arow * xrowbytes + 16 * lseg;
     }
+    auto issue_xe = [&](int kt, int buf) {
+        const uint32_t kb = (uint32_t)kt * (kTBK * 2);
+#pragma unroll
+        for (int i = 0; i < XL; ++i)
+            copy_rows_to_lds(xbase, xoff_e[i] + kb, &Xt[buf][(wave * (XROWS / 4) + 16 * i) * 64]);
+    };
+    auto issue_c = [&](int kt) { copy_rows_to_lds(cbase, coff + (uint32_t)kt * 16, &Ct[kt % kStages][wave * 1024]); };
+    auto issue_scales = [&](int blk) {  // groups 8 blk .. 8 blk + 7 (stages 32 blk .. 32 blk + 31)
+        copy_rows_to_lds(sbase, soff + (uint32_t)blk * 16, &St[blk & 1][wave * 1024]);
+    };
+    // Dequantisation: thread (wavefront w, lane l) writes 16-byte physical
+    // slot l & 3 of weight-tile rows 64 j + 16 w + l / 4, j = 0..3, so each
+    // of its LDS stores covers 1 KB contiguously (free of bank conflicts);
+    // that slot holds logical segment lseg of every one of those rows.  Row
+    // 64 j + 16 w + r was copied by lane 16 j + r of this wavefront: its
+    // codes sit at 1024 w + 256 j + 16 r of the code slot.
+    const uint32_t cread = lds_addr(Ct[0]) + 1024 * wave + 16 * (lane >> 2) + 4 * lseg;
+    const uint32_t sread = lds_addr(St[0]) + 1024 * wave + 16 * (lane >> 2);
+    const uint32_t wdst = 1024 * wave + 16 * lane;
+    uint32_t sc0, sc1, sc2, sc3;  // group scales of this thread's four rows
+    auto read_scales = [&](int g) {
+        ds_read_scales(sread + (uint32_t)((g >> 3) & 1) * 4096 + (uint32_t)(g & 7) * 2, sc0, sc1, sc2, sc3);
+    };
+    // rem = stages after s (>= 0); the counts follow the issue order above
+    auto wait_x = [&](int rem) {
+        if (rem >= 3) wait_vmcnt<3 + 2 * XL>();
+        else if (rem == 2) wait_vmcnt<2 + 2 * XL>();
+        else if (rem == 1) wait_vmcnt<1 + XL>();
+        else wait_vmcnt<0>();
+    };
+    // C(s+1) landed; rem = stages after s (>= 1)
+    auto wait_c = [&](int rem) {
+        if (rem >= 4) wait_vmcnt<3 + 3 * XL>();
+        else if (rem == 3) wait_vmcnt<2 + 3 * XL>();
+        else if (rem == 2) wait_vmcnt<1 + 2 * XL>();
+        else wait_vmcnt<XL>();
+    };
+    auto dequant = [&](int j) {  // stage j's codes -> LDS slot j % 4 (scales of group j / 4 loaded)
+        uint32_t w0, w1, w2, w3;
+        ds_read_codes(cread + (uint32_t)(j % kStages) * 4096, w0, w1, w2, w3);
+        const uint32_t wb = lds_addr(Wt[j % kStages]) + wdst;
+        dequant_word_to_lds(w0, sc0, wb);
+        dequant_word_to_lds(w1, sc1, wb + 4096);
+        dequant_word_to_lds(w2, sc2, wb + 8192);
+        dequant_word_to_lds(w3, sc3, wb + 12288);
+    };
+    // prologue
+    issue_scales(0);
+    issue_c(0);
+    issue_xe(0, 0);
+    issue_c(1);
+    issue_xe(1, 1);
+    issue_c(2);
+    issue_xe(2, 2);
+    issue_c(3);
+    wait_c(4);
+    read_scales(0);
+    dequant(0);
+
+    // one step; J = s % 4 (static), rem = nk - 1 - s (static in each call below)
+    auto step = [&](int s, const int J, const int rem) {
+        wait_x(rem);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        barrier();
+        if (rem >= 3) issue_xe(s + 3, (J + 3) % kStages);
+        if (rem >= 4) issue_c(s + 4);
+        if (rem >= 1) {
+            // stage s + 1's codes are expanded between the MFMAs of stage s's
+            // first substep and written to their (free) slot after stage s
+            wait_c(rem);
+            if (J == 3) read_scales((s + 1) >> 2);
+            uint32_t w0, w1, w2, w3;
+            ds_read_codes(cread + (uint32_t)((s + 1) % kStages) * 4096, w0, w1, w2, w3);
+            uint4 d0, d1, d2, d3;
+            compute(J, [&] {
+                d0 = dequant_word(w0, sc0);
+                d1 = dequant_word(w1, sc1);
+                d2 = dequant_word(w2, sc2);
+                d3 = dequant_word(w3, sc3);
+                // one MFMA, then a share of the expansion's VALU operations, in turn
+#pragma unroll
+                for (int m = 0; m < TI * TJ; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, kInt4MixValu, 0);
+                }
+            });
+            const uint32_t wb = lds_addr(Wt[(s + 1) % kStages]) + wdst;
+            ds_write16(wb, d0.x, d0.y, d0.z, d0.w);
+            ds_write16(wb + 4096, d1.x, d1.y, d1.z, d1.w);
+            ds_write16(wb + 8192, d2.x, d2.y, d2.z, d2.w);
+            ds_write16(wb + 12288, d3.x, d3.y, d3.z, d3.w);
+            return;
+        }
+        if (rem >= 1) {
+            wait_c(rem);
+            if (J == 3) read_scales((s + 1) >> 2);  // stage s + 1 opens a new group
+            dequant(s + 1);
+        }
+        compute(J, no_mid);
+    };
+    int s0 = 0;
+    for (; s0 + 8 <= nk; s0 += 4) {  // steady state: every step has 4 or more stages after it
+        if ((s0 & 31) == 0 && s0 + 32 < nk) issue_scales((s0 >> 5) + 1);
+        step(s0, 0, 4);
+        step(s0 + 1, 1, 4);
+        step(s0 + 2, 2, 4);
+        step(s0 + 3, 3, 4);
+    }
+    step(s0, 0, 3);  // the last four stages
+    step(s0 + 1, 1, 2);
+    step(s0 + 2, 2, 1);
+    step(s0 + 3, 3, 0);
 
     // the last stage waited for every load (vmcnt 0), so nothing lands in the staging area
     if constexpr (WHICH == 1 && ACT != kActSwiglu) {
@@ -823,12 +767,10 @@ __device__ __forceinline__ bf16x8 ds_read16_at(uint32_t addr) {
     return v;
 }
 
-// stages kt0 .. kt0 + ns - 1 of 64 along K
-template <int WHICH, int ACT>
-__device__ __forceinline__ void tile_gemm_bf16_pp(uint8_t* lds, const uint16_t* __restrict__ A,
-                                                  const int32_t* __restrict__ a_rows, const void* Wexp,
-                                                  void* __restrict__ out, int N, int K, int n0, int p0, int rows,
-                                                  int kt0, int ns) {
+// GEMM2 (A = H, rows p0 .. p0 + rows - 1; fp32 Y), stages kt0 .. kt0 + ns - 1 of 64 along K
+__device__ __forceinline__ void tile_gemm2_bf16_pp(uint8_t* lds, const uint16_t* __restrict__ A, const void* Wexp,
+                                                   float* __restrict__ out, int N, int K, int n0, int p0, int rows,
+                                                   int kt0, int ns) {
     constexpr int TI = 4, TJ = 2;
     constexpr uint32_t kSlot = 256 * 128;
     static_assert((kPpW + kPpX) * kSlot <= kBf16LdsBytes, "rings exceed the kernel's LDS");
@@ -842,8 +784,8 @@ __device__ __forceinline__ void tile_gemm_bf16_pp(uint8_t* lds, const uint16_t* 
 
     // this wavefront's copies: tile rows [64 v, 64 v + 64) of its group's operand, 8 rows x 128 bytes per
     // load; lane L moves logical segment (L & 7) ^ ((row >> 1) & 7) of row L >> 3 of its block, which lands
-    // at LDS byte 16 L of the block.  Rows past N (weights) or past the tile's rows (tokens) are clamped:
-    // they only feed outputs that are never stored.
+    // at LDS byte 16 L of the block.  Rows past N (weights) or past the tile's rows (dispatch rows) are
+    // clamped: they only feed outputs that are never stored.
     const uint32_t rowbytes = (uint32_t)K * 2;
     const char* src = grp == 0 ? reinterpret_cast<const char*>(Wexp) : reinterpret_cast<const char*>(A);
     uint32_t goff[8];
@@ -851,13 +793,8 @@ __device__ __forceinline__ void tile_gemm_bf16_pp(uint8_t* lds, const uint16_t* 
     for (int q = 0; q < 8; ++q) {
         const int trow = 64 * v + 8 * q + (lane >> 3);
         const uint32_t seg = (uint32_t)((lane & 7) ^ ((trow >> 1) & 7));
-        if (grp == 0) {
-            goff[q] = (uint32_t)min(n0 + trow, N - 1) * rowbytes + 16 * seg;
-        } else {
-            const int drow = min(trow, rows - 1);
-            const uint32_t arow = (WHICH == 1) ? (uint32_t)a_rows[p0 + drow] : (uint32_t)(p0 + drow);
-            goff[q] = arow * rowbytes + 16 * seg;
-        }
+        const uint32_t grow = grp == 0 ? (uint32_t)min(n0 + trow, N - 1) : (uint32_t)(p0 + min(trow, rows - 1));
+        goff[q] = grow * rowbytes + 16 * seg;
     }
     uint8_t* const ring = lds + grp * (kPpW * kSlot) + 8192 * v;
     // half hf of this wavefront's loads of stage st: tile rows 64 v + 32 hf .. + 32
@@ -990,14 +927,7 @@ __device__ __forceinline__ void tile_gemm_bf16_pp(uint8_t* lds, const uint16_t* 
         phase_end();
     }
     // every load has landed and every fragment read has returned: the epilogue may stage through the rings
-    if constexpr (WHICH == 1 && ACT != kActSwiglu) {
-        store_tile_lds<TI, TJ, ACT, 8, kBf16LdsBytes>(acc, lds, out, N, n0, p0, rows, wn, wm, r, h, true);
-    } else if constexpr (WHICH == 2) {
-        store_tile_lds_f32<TI, TJ, 8, kBf16LdsBytes>(acc, lds, static_cast<float*>(out), N, n0, p0, rows, wn, wm,
-                                                    r, h, true);
-    } else {
-        store_tile<WHICH, TI, TJ, ACT>(acc, out, N, n0, p0, rows, wn, wm, r, h);
-    }
+    store_tile_lds_f32<TI, TJ, 8, kBf16LdsBytes>(acc, lds, out, N, n0, p0, rows, wn, wm, r, h, true);
     // group 0 has passed one barrier fewer; it takes it here, where the accumulators are no longer live (a
     // conditional barrier while they are makes the compiler copy them all out of the AGPRs)
     if (grp == 0) barrier();
@@ -1076,7 +1006,7 @@ gemm_tiled_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict
     const void* Wexp = W + (int64_t)e * W_stride;
     if (rows > 128) {
         if constexpr (WHICH == 2)
-            tile_gemm_bf16_pp<WHICH, ACT>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows, kt0, nk);
+            tile_gemm2_bf16_pp(smem, A, Wexp, static_cast<float*>(out), N, K, n0, p0, rows, kt0, nk);
         else
             tile_gemm_bf16<WHICH, 4, 2, 256, ACT>(smem, A, a_rows, Wexp, out, N, K, n0, p0, rows, kt0, nk);
     } else if (rows > 64) {
