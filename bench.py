@@ -39,6 +39,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -106,15 +107,27 @@ def gemm_path_name(cfg):
     return "tiled"
 
 
-def kernel_source_hash(kernel):
-    """Hash of the sources that define a grouped-GEMM kernel: its own file, the
-    shared headers and the launch parameters chosen in moe_api.hip."""
-    csrc = os.path.join(ROOT, "sparse_mixture_experts_03_amd", "csrc")
+# string and character literals (kept) and comments (dropped) of a C/C++/HIP source
+_SOURCE_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def source_code_only(text):
+    """A source's code without its comments, whitespace collapsed: what a
+    counter measurement depends on."""
+    text = _SOURCE_TOKENS.sub(lambda m: " " if m.group(0).startswith("/") else m.group(0), text)
+    return " ".join(text.split())
+
+
+def kernel_source_hash(kernel, csrc=None):
+    """Hash of the code that defines a grouped-GEMM kernel: its own file, the
+    shared headers and the launch parameters chosen in moe_api.hip (comments
+    and layout left out, so editing a comment keeps the counters valid)."""
+    csrc = csrc or os.path.join(ROOT, "sparse_mixture_experts_03_amd", "csrc")
     path = kernel.rsplit("_", 1)[-1]
     h = hashlib.sha256()
     for f in ("common.hpp", "launch.hpp", "moe_api.hip", KERNEL_SOURCES[path]):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + source_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -4,22 +4,28 @@
 // W2, so one kernel serves all experts; P3 §4.2 notes the per-expert work is
 // really a grouped GEMM over the tokens scattered to each expert, and P2 §3.3
 // credits fusing the activation into the expert GEMM.  Here:
-//   workgroup tile = 256 weight rows x 256 dispatch rows (one expert);
-//   tiles go straight from HBM/L2 into LDS with gfx950's global_load_lds
-//   (16 bytes per lane, no register staging).  bf16 weights: K-stages of 64,
-//   so every tile row of a stage is one whole 128-byte line, double-buffered
-//   (2 x 64 KB).  INT4 weights (P1 §5.4, P2 §2.3): K-stages of 32 in a ring
-//   of four, the dispatch rows three stages ahead and the codes four; the
-//   workgroup turns each stage's codes into bf16(q * s) in LDS, in the layout
-//   the bf16 tiles use, so the MFMA step is the same.  One barrier per stage.
-//   Tile rows keep their 16-byte segments in XOR-permuted slots, so the
-//   loads, the dequantised stores and the 32-row MFMA fragment reads are free
-//   of LDS bank conflicts;
-//   4 wavefronts in a 2 x 2 arrangement, each 128 x 128 outputs as 16 MFMA
-//   32x32x16 bf16 tiles with fp32 accumulation (256 accumulators in AGPRs:
-//   64 flops per byte read from LDS); an expert's last, partial tile uses a
-//   128- or 64-row variant (4 x 1 wavefronts) so padding stays small;
-//   GEMM1's epilogue applies GeLU and stores bf16 H; GEMM2's stores fp32 Y.
+//   workgroup tile = 256 weight rows x 256 dispatch rows (one expert), one
+//   workgroup per CU; an expert's last, partial tile uses a 128- or 64-row
+//   variant so padding stays small.  Tiles go straight from HBM/L2 into LDS
+//   with gfx950's global_load_lds (16 bytes per lane, no register staging),
+//   and tile rows keep their 16-byte segments in XOR-permuted slots, so the
+//   copies, the dequantised stores and the 32-row MFMA fragment reads are
+//   free of LDS bank conflicts.  MFMA 32x32x16 bf16 with fp32 accumulators in
+//   AGPRs throughout.
+//   bf16 weights: K-stages of 64 (every tile row of a stage is one whole
+//   128-byte line), two weight and three dispatch-row slots of 32 KB (all
+//   160 KB of LDS), eight wavefronts (two per SIMD) of 128 x 64 outputs.
+//   GEMM1 runs them in lockstep, one barrier per stage; GEMM2's 256-row
+//   tiles run two groups of four in ping-pong (one multiplies while the other
+//   reads fragments and copies).
+//   INT4 weights (P1 §5.4, P2 §2.3): K-stages of 32 in a ring of four, the
+//   dispatch rows three stages ahead and the codes four; the workgroup turns
+//   each stage's codes into bf16(q * s) in LDS, in the layout the bf16 tiles
+//   use, so the MFMA step is the same; four wavefronts of 128 x 128 outputs
+//   (256 accumulators each), one barrier per stage.
+//   GEMM1's epilogue applies the activation and stores bf16 H, GEMM2's
+//   stores fp32 Y; both are staged through LDS so every store writes whole
+//   lines (SwiGLU, which pairs gate and up rows, stores from registers).
 // The m-tiles of all experts are numbered expert-major and located from the
 // offsets on the device, so skewed loads (0 .. thousands of rows per expert)
 // need no host round trip; tiles past the last real one exit at once.

@@ -62,3 +62,19 @@ def test_import_needs_the_calibration_copy(tmp_path, monkeypatch):
     args = bench.parse(["--import-counters", str(fetch), str(write), "--workload", "int4-decode-T16-d12288-E16"])
     with pytest.raises(SystemExit):
         bench.import_counters(args)
+
+
+def test_source_hash_follows_code_not_comments(tmp_path):
+    # counters stay valid across comment edits and are invalidated by code edits
+    import shutil
+    csrc = os.path.join(ROOT, "sparse_mixture_experts_03_amd", "csrc")
+    for f in ("common.hpp", "launch.hpp", "moe_api.hip", "gemm_tiled.hip"):
+        shutil.copy(os.path.join(csrc, f), tmp_path / f)
+    base = bench.kernel_source_hash("moe_grouped_gemm_w1_tiled", csrc=str(tmp_path))
+    assert base == bench.kernel_source_hash("moe_grouped_gemm_w1_tiled")
+    src = (tmp_path / "gemm_tiled.hip").read_text()
+    (tmp_path / "gemm_tiled.hip").write_text("// a new comment line\n" + src.replace("\n", "\n\n", 3) + "/* trailing */\n")
+    assert bench.kernel_source_hash("moe_grouped_gemm_w1_tiled", csrc=str(tmp_path)) == base
+    (tmp_path / "gemm_tiled.hip").write_text(src.replace("constexpr int kPpW = 3", "constexpr int kPpW = 2", 1))
+    assert bench.kernel_source_hash("moe_grouped_gemm_w1_tiled", csrc=str(tmp_path)) != base
+    assert bench.source_code_only('a = "// kept"; // dropped\n/* dropped */ b;') == 'a = "// kept"; b;'
