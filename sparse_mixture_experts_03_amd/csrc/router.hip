@@ -278,10 +278,13 @@ __device__ __forceinline__ double router_noise(double l, int use_gumbel, double 
     return v;
 }
 
-// One workgroup per token.  Thread e sums the split partials of expert e (all
+// One token per workgroup (E > 64) or per wavefront (E <= 64, four tokens per
+// workgroup).  Thread e of the token sums the split partials of expert e (all
 // loads issued before the adds, summed in split order), adds bias and noise
-// and applies the temperature; wavefront 0 then picks the top-k and forms the
-// softmax gates from the E values in LDS.
+// and applies the temperature; the token's first wavefront then picks the
+// top-k and forms the softmax gates from the E values in LDS.  The values and
+// the order of every operation are the same in both arrangements.
+template <bool kWavePerToken>
 __global__ void __launch_bounds__(256)
 router_finalize_kernel(const double* __restrict__ partial, int nsplit, int T, int E, int k,
                        const float* __restrict__ bias, double tau, int use_gumbel, double noise_std,
@@ -289,12 +292,17 @@ router_finalize_kernel(const double* __restrict__ partial, int nsplit, int T, in
                        float* __restrict__ gates,
                        double* __restrict__ prob_rows, double* __restrict__ entropy_rows,
                        double* __restrict__ z_rows) {
-    __shared__ double zs[256];
-    __shared__ int sel[8];  // the chosen experts, best first
-    const int t = blockIdx.x;
+    __shared__ double zs_all[256];
+    __shared__ int sel_all[4][8];  // the chosen experts, best first
     const int tid = threadIdx.x;
-    if (tid < E) {
-        const double* src = partial + (int64_t)t * E + tid;
+    const int wave = tid >> 6;
+    const int t = kWavePerToken ? blockIdx.x * 4 + wave : blockIdx.x;
+    const int e_own = kWavePerToken ? (tid & 63) : tid;  // the expert this thread sums
+    double* const zs = kWavePerToken ? zs_all + 64 * wave : zs_all;
+    int* const sel = sel_all[kWavePerToken ? wave : 0];
+    if (kWavePerToken && t >= T) return;  // whole wavefronts
+    if (e_own < E) {
+        const double* src = partial + (int64_t)t * E + e_own;
         const int64_t step = (int64_t)T * E;
         double v[kMaxSplits];
 #pragma unroll
@@ -304,14 +312,17 @@ router_finalize_kernel(const double* __restrict__ partial, int nsplit, int T, in
 #pragma unroll
         for (int s = 0; s < kMaxSplits; ++s)
             if (s < nsplit) l += v[s];
-        if (bias) l += (double)bias[tid];
+        if (bias) l += (double)bias[e_own];
         if (use_gumbel || noise_std > 0.0)
-            l = router_noise(l, use_gumbel, noise_std, seed, token_offset + (uint64_t)t, (uint64_t)tid);
-        zs[tid] = l / tau;
+            l = router_noise(l, use_gumbel, noise_std, seed, token_offset + (uint64_t)t, (uint64_t)e_own);
+        zs[e_own] = l / tau;
     }
-    __syncthreads();
-    if (tid >= 64) return;
-    const int lane = tid;
+    // one wavefront per token reads back only its own LDS writes, which complete in order
+    if constexpr (!kWavePerToken) {
+        __syncthreads();
+        if (tid >= 64) return;
+    }
+    const int lane = tid & 63;
     double z[4];
     bool live[4];
 #pragma unroll
@@ -454,10 +465,16 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t stream) {
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(router_finalize_kernel, dim3((unsigned)a.T), dim3(256), 0, stream, a.partial, nsplit,
-                       (int)a.T, a.E, a.k, a.bias, (double)a.tau, a.use_gumbel, (double)a.noise_std, a.gate_norm,
-                       a.seed, a.token_offset, a.ids,
-                       a.gates, a.prob_rows, a.entropy_rows, a.z_rows);
+    if (a.E <= 64)
+        hipLaunchKernelGGL(router_finalize_kernel<true>, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, stream,
+                           a.partial, nsplit, (int)a.T, a.E, a.k, a.bias, (double)a.tau, a.use_gumbel,
+                           (double)a.noise_std, a.gate_norm, a.seed, a.token_offset, a.ids, a.gates, a.prob_rows,
+                           a.entropy_rows, a.z_rows);
+    else
+        hipLaunchKernelGGL(router_finalize_kernel<false>, dim3((unsigned)a.T), dim3(256), 0, stream, a.partial,
+                           nsplit, (int)a.T, a.E, a.k, a.bias, (double)a.tau, a.use_gumbel, (double)a.noise_std,
+                           a.gate_norm, a.seed, a.token_offset, a.ids, a.gates, a.prob_rows, a.entropy_rows,
+                           a.z_rows);
     return hipGetLastError();
 }
 
