@@ -429,7 +429,8 @@ __device__ __forceinline__ void tile_gemm(uint8_t (*Wt)[kTileBytes], uint8_t (*X
     const uint32_t wrow = (uint32_t)min(n0 + 64 * (lane >> 4) + 16 * wave + (lane & 15), N - 1);
     const uint32_t coff = wrow * ((uint32_t)K / 2);
     const uint32_t soff = wrow * ((uint32_t)K / 128) * 2;
-    // rows past the tile's dispatch rows are clamped (as above)
+    // rows past the tile's dispatch rows (and weight rows past N) are clamped to a valid row: they
+    // only feed outputs that are never stored
     uint32_t xoff_e[XL];
 #pragma unroll
     for (int i = 0; i < XL; ++i) {
