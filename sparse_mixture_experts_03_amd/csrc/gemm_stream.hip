@@ -130,7 +130,7 @@ __global__ void __launch_bounds__(256)
 gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows,
                    const int32_t* __restrict__ offsets, int E, const uint8_t* __restrict__ W,
                    const uint16_t* __restrict__ Wsc, int64_t W_stride, void* __restrict__ out, int N, int K,
-                   int ntiles_n, int rows_lo, int rows_hi, int act) {
+                   int ntiles_n, int rows_lo, int rows_hi, int act, int ksplit, int64_t split_stride) {
     constexpr int ROWS = 16 * NB;              // weight rows per workgroup
     constexpr int SEGS = kStageBytes / 16;     // 16-byte segments per row per stage
     constexpr int LROW = kStageBytes + 16;     // padded LDS row (conflict-free 16-row column reads)
@@ -146,8 +146,13 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
     f32x4 (*red)[NB * MT][64] = reinterpret_cast<f32x4 (*)[NB * MT][64]>(smem);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int mt = blockIdx.x / ntiles_n;
-    const int nt = blockIdx.x - mt * ntiles_n;
+    // ksplit = 2 (GEMM2 only): workgroups 2 b and 2 b + 1 take the two halves of tile b's K stages and write
+    // them to out and out + split_stride (fp32 partials, added in a fixed order by the combine)
+    const int ks = blockIdx.x % ksplit;
+    const int b_tile = blockIdx.x / ksplit;
+    const int mt = b_tile / ntiles_n;
+    const int nt = b_tile - mt * ntiles_n;
+    if (WHICH == 2) out = static_cast<float*>(out) + ks * split_stride;
     int e, p0, rows;
     if (!find_mtile(offsets, E, kStreamBM * MT, mt, &e, &p0, &rows, rows_lo, rows_hi)) return;
 
@@ -175,9 +180,10 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
     uint8_t* lds = stage_lds[wave];
     const uint4 zero4 = make_uint4(0, 0, 0, 0);
 
-    // This wavefront's stages (kStageBytes of every row each) of the K range.
+    // This wavefront's stages (kStageBytes of every row each) of the workgroup's K range.
     const int nstages = (int)((row_bytes + kStageBytes - 1) / kStageBytes);
-    const int st0 = wave * nstages / 4, st1 = (wave + 1) * nstages / 4;
+    const int lo = ks * nstages / ksplit, span = (ks + 1) * nstages / ksplit - lo;
+    const int st0 = lo + wave * span / 4, st1 = lo + (wave + 1) * span / 4;
 
     // coalesced loads: instruction i, lane L -> row (64i + L) / SEGS, segment (64i + L) % SEGS
     auto gload = [&](int st, uint4 (&buf)[LOADS]) {
@@ -432,14 +438,17 @@ hipError_t launch_stream_nb(const GemmArgs& a, hipStream_t stream) {
     const uint16_t* A = static_cast<const uint16_t*>(a.A);
     const uint8_t* W = static_cast<const uint8_t*>(a.W);
     const uint16_t* S = static_cast<const uint16_t*>(a.W_scales);
-    dim3 grid((unsigned)blocks), block(256);
+    const int ksplit = (a.which == 2 && a.ksplit == 2) ? 2 : 1;
+    if (blocks * ksplit > 0x7fffffff) return hipErrorInvalidValue;
+    const int64_t split_stride = a.T * a.k * a.N;
+    dim3 grid((unsigned)(blocks * ksplit)), block(256);
     // INT4: each stage's group scales are one vector load when every row's
     // scales start on a stage boundary of an aligned array
     const bool scv = WQ == kINT4 && (a.K / 128) % (SB / 64) == 0 && ((uintptr_t)S % 16) == 0;
 #define MOE_STREAM_LAUNCH(WHICH_, SCV_)                                                                            \
     hipLaunchKernelGGL((gemm_stream_kernel<WQ, WHICH_, NB, MT, SB, SCV_>), grid, block, 0, stream, A, a.a_rows,     \
                        a.offsets, a.E, W, S, a.W_stride, a.out, (int)a.N, (int)a.K, ntiles_n, a.rows_lo, a.rows_hi, \
-                       a.act)
+                       a.act, ksplit, split_stride)
     if constexpr (WQ == kINT4) {
         if (a.which == 1) {
             if (scv) MOE_STREAM_LAUNCH(1, true); else MOE_STREAM_LAUNCH(1, false);

@@ -84,7 +84,7 @@ struct GemmArgs {
     int rows_lo, rows_hi;   // only experts holding n rows, rows_lo < n <= rows_hi
     int stream_mt;          // streaming kernel: 16-row dispatch tiles per workgroup (1, 2 or 4)
     int act = 0;            // which 1: kActGelu, kActSilu or kActSwiglu (N = 2 d_ff weight rows)
-    int ksplit = 1;         // tiled bf16, which 2: K halves written to out and out + T*k*N (fp32 partials)
+    int ksplit = 1;         // which 2 (tiled bf16, streaming): K halves written to out and out + T*k*N (fp32 partials)
 };
 hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream);  // BF16 / INT4 weights
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);   // BF16 weights
