@@ -119,6 +119,9 @@ FORWARD_CASES = {
     # the automatic choice on both sides of its threshold (streaming up to 16 tokens, tiled above), and one token
     "bf16-T17-d512-dff1024-E8": (case(17, 512, 1024, 8), [moe.GEMM_AUTO]),
     "bf16-T1-d512-dff1024-E8": (case(1, 512, 1024, 8), [moe.GEMM_AUTO]),
+    # GEMM2's K range shorter than one streaming stage, so one of the layer's two K halves is empty
+    "bf16-T8-d256-dff64-E4": (case(8, 256, 64, 4), [moe.GEMM_STREAMING]),
+    "int4-T6-d256-dff128-E4": (case(6, 256, 128, 4, w=INT4), [moe.GEMM_STREAMING]),
     "bf16-T300-d512-dff1024-E8-skewed": (case(300, 512, 1024, 8, bias=True), [moe.GEMM_STREAMING, moe.GEMM_TILED]),
     "bf16-T150-d320-dff576-E6-ntail": (case(150, 320, 576, 6), [moe.GEMM_STREAMING, moe.GEMM_TILED]),
     # N tails (576 = 2 x 256 + 64 for W1, 320 for W2) on every tiled tile height: 256-, 128- and 64-row tiles
