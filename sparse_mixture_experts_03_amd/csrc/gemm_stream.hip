@@ -146,13 +146,14 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
     f32x4 (*red)[NB * MT][64] = reinterpret_cast<f32x4 (*)[NB * MT][64]>(smem);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    // ksplit = 2 (GEMM2 only): workgroups 2 b and 2 b + 1 take the two halves of tile b's K stages and write
-    // them to out and out + split_stride (fp32 partials, added in a fixed order by the combine)
+    // ksplit = 2: workgroups 2 b and 2 b + 1 take the two halves of tile b's K stages and write them to out and
+    // out + split_stride as fp32 partials without the activation (GEMM2: added in a fixed order by the combine;
+    // GEMM1: by act_halves_kernel, which applies the activation)
     const int ks = blockIdx.x % ksplit;
     const int b_tile = blockIdx.x / ksplit;
     const int mt = b_tile / ntiles_n;
     const int nt = b_tile - mt * ntiles_n;
-    if (WHICH == 2) out = static_cast<float*>(out) + ks * split_stride;
+    if (WHICH == 2 || ksplit == 2) out = static_cast<float*>(out) + ks * split_stride;
     int e, p0, rows;
     if (!find_mtile(offsets, E, kStreamBM * MT, mt, &e, &p0, &rows, rows_lo, rows_hi)) return;
 
@@ -398,6 +399,18 @@ gemm_stream_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ a
     }
     __syncthreads();
     if (wave == 0) {
+        if (WHICH == 1 && ksplit == 2) {  // fp32 partial of every weight row, the activation comes later
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int c = 0; c < MT; ++c) {
+                    f32x4 v = acc[b][c];
+#pragma unroll
+                    for (int w = 0; w < 3; ++w) v += red[w][b * MT + c][lane];
+                    store_tile<2>(out, N, p0 + 16 * c, rows - 16 * c, n0 + 16 * b, v, lane, act);
+                }
+            return;
+        }
         if constexpr (WHICH == 1 && NB % 2 == 0) {
             if (act == kActSwiglu) {  // blocks 2 b' (gate) and 2 b' + 1 (up) of 32 aligned rows
 #pragma unroll
@@ -438,7 +451,7 @@ hipError_t launch_stream_nb(const GemmArgs& a, hipStream_t stream) {
     const uint16_t* A = static_cast<const uint16_t*>(a.A);
     const uint8_t* W = static_cast<const uint8_t*>(a.W);
     const uint16_t* S = static_cast<const uint16_t*>(a.W_scales);
-    const int ksplit = (a.which == 2 && a.ksplit == 2) ? 2 : 1;
+    const int ksplit = a.ksplit == 2 ? 2 : 1;
     if (blocks * ksplit > 0x7fffffff) return hipErrorInvalidValue;
     const int64_t split_stride = a.T * a.k * a.N;
     dim3 grid((unsigned)(blocks * ksplit)), block(256);
@@ -481,7 +494,52 @@ hipError_t launch_stream_int4(const GemmArgs& a, hipStream_t stream) {
     return launch_stream_nb<kINT4, kNbInt4, 4, kStageInt4>(a, stream);
 }
 
+// GEMM1 in two K halves: H = bf16(act(P0 + P1)) from the fp32 partials P0 = P, P1 = P + stride ([rows][N]
+// each, the halves added in that order).  SwiGLU: N = 2 dff weight rows, 32-row blocks of 16 gate rows then
+// their 16 up rows; hidden unit 16 b + j is silu(gate row 32 b + j) * (up row 32 b + 16 + j).  Four units per
+// thread.
+__global__ void __launch_bounds__(256)
+act_halves_kernel(const float* __restrict__ P, int64_t stride, uint16_t* __restrict__ H, int64_t rows, int N, int dff,
+                  int act) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;  // first of this thread's four units
+    if (i >= rows * dff) return;
+    const int64_t r = i / dff;
+    const int u = (int)(i - r * dff);
+    const float* p0 = P + r * N;
+    const float* p1 = p0 + stride;
+    float h[4];
+    if (act == kActSwiglu) {
+        const int g = 32 * (u >> 4) + (u & 15);  // four units inside one block of 16 (dff is a multiple of 64)
+        const float4 ga = *reinterpret_cast<const float4*>(p0 + g), gb = *reinterpret_cast<const float4*>(p1 + g);
+        const float4 ua = *reinterpret_cast<const float4*>(p0 + g + 16);
+        const float4 ub = *reinterpret_cast<const float4*>(p1 + g + 16);
+        h[0] = silu_f(ga.x + gb.x) * (ua.x + ub.x);
+        h[1] = silu_f(ga.y + gb.y) * (ua.y + ub.y);
+        h[2] = silu_f(ga.z + gb.z) * (ua.z + ub.z);
+        h[3] = silu_f(ga.w + gb.w) * (ua.w + ub.w);
+    } else {
+        const float4 a = *reinterpret_cast<const float4*>(p0 + u), b = *reinterpret_cast<const float4*>(p1 + u);
+        h[0] = act_f(a.x + b.x, act);
+        h[1] = act_f(a.y + b.y, act);
+        h[2] = act_f(a.z + b.z, act);
+        h[3] = act_f(a.w + b.w, act);
+    }
+    uint2 packed;
+    packed.x = pack_bf16x2(h[0], h[1]);
+    packed.y = pack_bf16x2(h[2], h[3]);
+    *reinterpret_cast<uint2*>(H + i) = packed;
+}
+
 }  // namespace
+
+hipError_t launch_act_halves(const float* P, int64_t stride, void* H, int64_t rows, int N, int dff, int act,
+                             hipStream_t stream) {
+    const int64_t quads = rows * dff / 4;
+    if (quads == 0) return hipSuccess;
+    hipLaunchKernelGGL(act_halves_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream, P, stride,
+                       static_cast<uint16_t*>(H), rows, N, dff, act);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream) {
     // N is a multiple of 64, so any NB in {1, 2, 4} tiles it exactly.

@@ -84,9 +84,14 @@ struct GemmArgs {
     int rows_lo, rows_hi;   // only experts holding n rows, rows_lo < n <= rows_hi
     int stream_mt;          // streaming kernel: 16-row dispatch tiles per workgroup (1, 2 or 4)
     int act = 0;            // which 1: kActGelu, kActSilu or kActSwiglu (N = 2 d_ff weight rows)
-    int ksplit = 1;         // which 2 (tiled bf16, streaming): K halves written to out and out + T*k*N (fp32 partials)
+    int ksplit = 1;         // K halves written to out and out + T*k*N as fp32 partials (which 2: tiled bf16 and
+                            // streaming; which 1: streaming, no activation)
 };
 hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream);  // BF16 / INT4 weights
+// H = bf16(act(P + P[stride])) for the two fp32 K-half partials of GEMM1 ([rows][N] each; N = dff, or 2 dff
+// interleaved gate/up rows for SwiGLU); dff a multiple of 4
+hipError_t launch_act_halves(const float* P, int64_t stride, void* H, int64_t rows, int N, int dff, int act,
+                             hipStream_t stream);
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);   // BF16 weights
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t stream);     // F32 weights
 

@@ -168,6 +168,7 @@ FORWARD_CASES = {
     "bf16-T300-d512-dff1024-E8-skewed-swiglu": (case(300, 512, 1024, 8, bias=True, ffn=SWIGLU),
                                                 [moe.GEMM_STREAMING, moe.GEMM_TILED]),
     "bf16-T12-d512-dff1024-E8-swiglu": (case(12, 512, 1024, 8, ffn=SWIGLU), [moe.GEMM_STREAMING]),
+    "bf16-T10-d512-dff1024-E8-silu": (case(10, 512, 1024, 8, ffn=SILU), [moe.GEMM_STREAMING]),
     "bf16-T24-d512-dff1024-E4-swiglu": (case(24, 512, 1024, 4, ffn=SWIGLU), [moe.GEMM_STREAMING]),
     "bf16-T150-d320-dff576-E6-ntail-swiglu": (case(150, 320, 576, 6, ffn=SWIGLU), [moe.GEMM_STREAMING, moe.GEMM_TILED]),
     "int4-T200-d1024-dff1024-E8-skewed-swiglu": (case(200, 1024, 1024, 8, w=INT4, bias=True, ffn=SWIGLU),
