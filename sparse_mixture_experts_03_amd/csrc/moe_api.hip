@@ -136,13 +136,6 @@ struct Layout {
 
 int gemm_path_of(const moe_config& c);
 
-// K halves of the layer's GEMM2, written as two fp32 partials that the
-// combine adds in a fixed order: 2 for the streaming kernel at decode sizes
-// (twice the workgroups streaming the same weights: bf16 decode layer step
-// 0.687 -> 0.672 ms, INT4 decode unchanged), and for the bf16 tiled kernel
-// when its grid holds fewer than four rounds of 256-row tiles for 256 CUs,
-// so that the last, partly filled round of long tiles (K = d_ff) is split in
-// two.  1 otherwise.
 // K halves of the layer's GEMM1 (streaming bf16 kernel at decode sizes), as
 // fp32 partials that act_halves_kernel adds in a fixed order before the
 // activation: GEMM1 0.320 -> 0.312 ms on the 8-token, 128-expert decode.
@@ -150,6 +143,13 @@ int w1_ksplit_of(const moe_config& c) {
     return c.w_dtype == MOE_DTYPE_BF16 && gemm_path_of(c) == MOE_GEMM_STREAMING && c.T <= 16 ? 2 : 1;
 }
 
+// K halves of the layer's GEMM2, written as two fp32 partials that the
+// combine adds in a fixed order: 2 for the streaming kernel at decode sizes
+// (twice the workgroups streaming the same weights: bf16 decode layer step
+// 0.687 -> 0.672 ms, INT4 decode unchanged), and for the bf16 tiled kernel
+// when its grid holds fewer than four rounds of 256-row tiles for 256 CUs,
+// so that the last, partly filled round of long tiles (K = d_ff) is split in
+// two.  1 otherwise.
 int w2_ksplit_of(const moe_config& c) {
     if (c.w_dtype != MOE_DTYPE_F32 && gemm_path_of(c) == MOE_GEMM_STREAMING && c.T <= 16) return 2;
     if (c.w_dtype != MOE_DTYPE_BF16 || gemm_path_of(c) != MOE_GEMM_TILED || c.d_ff % 128 != 0) return 1;
